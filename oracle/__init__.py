@@ -1,0 +1,284 @@
+"""ctypes binding of the CPU oracle (``locks_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the oracle is the plain, slow, double-precision
+reference the GPU library is checked against.  Only the tests, the smoke
+check and the benchmark's CPU-baseline leg import this package.  It shares
+no code with the GPU library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "locks_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblocks_oracle.so")
+_lib = None
+
+_f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+
+
+def build() -> str:
+    """Compile the oracle with gcc (plain IEEE double, no fast-math)."""
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                           "-Wextra", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        c_int, c_double = ctypes.c_int, ctypes.c_double
+        lay = ctypes.POINTER(_Layout)
+        L.orc_lse.argtypes = [c_int, _f64p]
+        L.orc_lse.restype = c_double
+        L.orc_page_summary.argtypes = [c_int, c_int, c_int, _f64p, _f64p, _f64p, _f64p, _f64p]
+        L.orc_page_summary.restype = c_int
+        L.orc_page_estimate.argtypes = [c_int, c_int, c_int, _f64p, _f64p, _f64p, _f64p]
+        L.orc_page_estimate.restype = c_double
+        L.orc_page_exact_lse.argtypes = [c_int, c_int, _f64p, _f64p]
+        L.orc_page_exact_lse.restype = c_double
+        L.orc_select_topk.argtypes = [c_int, _f32p, c_int, c_int, _i32p, _f32p]
+        L.orc_select_topk.restype = c_int
+        L.orc_attend_tokens.argtypes = [c_int, c_int, _f64p, _f64p, _f64p, _f64p,
+                                        ctypes.POINTER(c_double)]
+        L.orc_attend_tokens.restype = None
+        L.orc_build_pool.argtypes = [lay, c_int, _f32p, _f32p, _f32p, _f32p, c_int]
+        L.orc_build_units.argtypes = [lay, c_int, _f32p, c_int, _i32p, _i32p, _i32p, _f64p,
+                                      _f64p, _f64p, _f64p, c_int]
+        L.orc_scan_pool.argtypes = [lay, c_int, _f32p, _f32p, _f32p, _f32p, ctypes.c_void_p,
+                                    ctypes.c_void_p, c_int]
+        L.orc_scan_units.argtypes = [lay, c_int, _f32p, _f32p, _f32p, _f32p, c_int, _i32p,
+                                     _i32p, _i32p, _f64p, _f64p]
+        L.orc_exact_pool.argtypes = [lay, _f32p, _f32p, ctypes.c_void_p, ctypes.c_void_p, c_int]
+        L.orc_select_pool.argtypes = [lay, c_int, _f32p, c_int, _i32p, ctypes.c_void_p]
+        L.orc_attend_pool.argtypes = [lay, _f32p, _f32p, _f32p, ctypes.c_void_p, c_int, _f64p,
+                                      ctypes.c_void_p, c_int]
+        for fn in ("orc_build_pool", "orc_build_units", "orc_scan_pool", "orc_scan_units",
+                   "orc_exact_pool", "orc_select_pool", "orc_attend_pool"):
+            getattr(L, fn).restype = c_int
+        _lib = L
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+# ------------------------------------------------------------------ single page
+
+def lse(x) -> float:
+    x = _f64(x).ravel()
+    return lib().orc_lse(x.size, x)
+
+
+def page_summary(keys, r: int):
+    """Summary of one page: (mu[d], basis[r][d], coef[P][r], sigma[min(P,d)], sweeps)."""
+    keys = _f64(keys)
+    P, d = keys.shape
+    mu = np.zeros(d)
+    basis = np.zeros((max(r, 0), d))
+    coef = np.zeros((P, max(r, 0)))
+    sigma = np.zeros(min(P, d))
+    sweeps = lib().orc_page_summary(P, d, r, keys, mu, basis.reshape(-1) if r else np.zeros(1),
+                                    coef.reshape(-1) if r else np.zeros(1), sigma)
+    if sweeps < 0:
+        raise ValueError("invalid rank")
+    return mu, basis, coef, sigma, sweeps
+
+
+def page_estimate(q, mu, basis, coef) -> float:
+    q, mu = _f64(q), _f64(mu)
+    basis, coef = _f64(basis), _f64(coef)
+    P = coef.shape[0]
+    r = basis.shape[0]
+    return lib().orc_page_estimate(P, q.size, r, q, mu, basis.reshape(-1) if r else np.zeros(1),
+                                   coef.reshape(-1) if r else np.zeros(1))
+
+
+def page_exact_lse(q, keys) -> float:
+    q, keys = _f64(q), _f64(keys)
+    return lib().orc_page_exact_lse(keys.shape[0], q.size, q, keys.reshape(-1) if keys.size
+                                    else np.zeros(1))
+
+
+def select_topk(mass, k: int, width: int | None = None):
+    mass = _f32(mass).ravel()
+    width = k if width is None else width
+    sel = np.zeros(max(width, 1), np.int32)
+    sm = np.zeros(max(width, 1), np.float32)
+    kk = lib().orc_select_topk(mass.size, mass, k, width, sel, sm)
+    return sel[:width], sm[:width], kk
+
+
+def attend_tokens(q, keys, vals):
+    q, keys, vals = _f64(q), _f64(keys), _f64(vals)
+    d = q.size
+    out = np.zeros(d)
+    l = ctypes.c_double()
+    n = keys.shape[0]
+    lib().orc_attend_tokens(n, d, q, keys.reshape(-1) if n else np.zeros(1),
+                            vals.reshape(-1) if n else np.zeros(1), out, ctypes.byref(l))
+    return out, l.value
+
+
+# ------------------------------------------------------------------ paged cache
+
+@dataclass
+class Layout:
+    """Paged layout: block_table [B][max_pages] int32, seq_lens [B] int32."""
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+
+    def __post_init__(self):
+        self.block_table = _i32(self.block_table)
+        self.seq_lens = _i32(self.seq_lens)
+
+    @property
+    def batch(self):
+        return self.block_table.shape[0]
+
+    @property
+    def max_pages(self):
+        return self.block_table.shape[1]
+
+    @property
+    def group(self):
+        return self.num_q_heads // self.num_kv_heads
+
+    def c(self):
+        s = _Layout(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
+                    self.page_size, self.max_pages, self.block_table.ctypes.data,
+                    self.seq_lens.ctypes.data)
+        return ctypes.byref(s), s
+
+
+def build_pool(L: Layout, r: int, k_pool, num_blocks: int, threads: int = 0):
+    k_pool = _f32(k_pool)
+    H, P, d = L.num_kv_heads, L.page_size, L.head_dim
+    mu = np.zeros((num_blocks, H, d), np.float32)
+    basis = np.zeros((num_blocks, H, max(r, 1), d), np.float32)[:, :, :r]
+    basis = np.ascontiguousarray(basis)
+    coef = np.zeros((num_blocks, H, P, r), np.float32)
+    ref, _keep = L.c()
+    _check(lib().orc_build_pool(ref, r, k_pool.reshape(-1), mu.reshape(-1),
+                                basis.reshape(-1) if basis.size else np.zeros(1, np.float32),
+                                coef.reshape(-1) if coef.size else np.zeros(1, np.float32),
+                                threads), "build_pool")
+    return mu, basis, coef
+
+
+def build_units(L: Layout, r: int, k_pool, units, threads: int = 0):
+    """units: int array [n][3] of (b, g, j). Returns double mu, basis, coef, sigma."""
+    units = _i32(units).reshape(-1, 3)
+    n = units.shape[0]
+    P, d = L.page_size, L.head_dim
+    mu = np.zeros((n, d))
+    basis = np.zeros((n, r, d))
+    coef = np.zeros((n, P, r))
+    sigma = np.zeros((n, min(P, d)))
+    ref, _keep = L.c()
+    _check(lib().orc_build_units(ref, r, _f32(k_pool).reshape(-1), n,
+                                 _i32(units[:, 0]), _i32(units[:, 1]), _i32(units[:, 2]),
+                                 mu.reshape(-1), basis.reshape(-1) if basis.size else np.zeros(1),
+                                 coef.reshape(-1) if coef.size else np.zeros(1),
+                                 sigma.reshape(-1), threads), "build_units")
+    return mu, basis, coef, sigma
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def scan_pool(L: Layout, r: int, q, mu, basis, coef, threads: int = 0, heads: bool = True):
+    q, mu, basis, coef = _f32(q), _f32(mu), _f32(basis), _f32(coef)
+    head = np.zeros((L.batch, L.num_q_heads, L.max_pages)) if heads else None
+    page = np.zeros((L.batch, L.num_kv_heads, L.max_pages))
+    ref, _keep = L.c()
+    _check(lib().orc_scan_pool(ref, r, q.reshape(-1), mu.reshape(-1),
+                               basis.reshape(-1) if basis.size else np.zeros(1, np.float32),
+                               coef.reshape(-1) if coef.size else np.zeros(1, np.float32),
+                               _ptr(head), _ptr(page), threads), "scan_pool")
+    return head, page
+
+
+def scan_units(L: Layout, r: int, q, mu, basis, coef, units):
+    units = _i32(units).reshape(-1, 3)
+    n = units.shape[0]
+    head = np.zeros((n, L.group))
+    page = np.zeros(n)
+    ref, _keep = L.c()
+    _check(lib().orc_scan_units(ref, r, _f32(q).reshape(-1), _f32(mu).reshape(-1),
+                                _f32(basis).reshape(-1), _f32(coef).reshape(-1), n,
+                                _i32(units[:, 0]), _i32(units[:, 1]), _i32(units[:, 2]),
+                                head.reshape(-1), page), "scan_units")
+    return head, page
+
+
+def exact_pool(L: Layout, q, k_pool, threads: int = 0):
+    head = np.zeros((L.batch, L.num_q_heads, L.max_pages))
+    page = np.zeros((L.batch, L.num_kv_heads, L.max_pages))
+    ref, _keep = L.c()
+    _check(lib().orc_exact_pool(ref, _f32(q).reshape(-1), _f32(k_pool).reshape(-1),
+                                _ptr(head), _ptr(page), threads), "exact_pool")
+    return head, page
+
+
+def select_pool(L: Layout, budget_tokens: int, page_mass_f32, width: int):
+    pm = _f32(page_mass_f32)
+    sel = np.zeros((L.batch, L.num_kv_heads, max(width, 1)), np.int32)
+    sm = np.zeros((L.batch, L.num_kv_heads, max(width, 1)), np.float32)
+    ref, _keep = L.c()
+    _check(lib().orc_select_pool(ref, budget_tokens, pm.reshape(-1), width, sel.reshape(-1),
+                                 sm.ctypes.data), "select_pool")
+    return sel[:, :, :width], sm[:, :, :width]
+
+
+def attend_pool(L: Layout, q, k_pool, v_pool, sel_pages=None, threads: int = 0):
+    out = np.zeros((L.batch, L.num_q_heads, L.head_dim))
+    lse_ = np.zeros((L.batch, L.num_q_heads))
+    width = 0
+    sel = None
+    if sel_pages is not None:
+        sel = _i32(sel_pages)
+        width = sel.shape[-1]
+    ref, _keep = L.c()
+    _check(lib().orc_attend_pool(ref, _f32(q).reshape(-1), _f32(k_pool).reshape(-1),
+                                 _f32(v_pool).reshape(-1), _ptr(sel), width, out.reshape(-1),
+                                 lse_.ctypes.data, threads), "attend_pool")
+    return out, lse_

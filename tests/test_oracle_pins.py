@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Every check compares the oracle with something other than itself: a closed
+form, a special case that reduces to a textbook identity, a library routine
+(LAPACK SVD, scipy logsumexp, torch SDPA), or brute force on tiny inputs.
+Each is chosen so that a plausible slip (a dropped term, a wrong sign or
+scale, a transposed operand, a wrong index) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+def _page(P, d, rank=None, offset=0.0, seed=0):
+    g = np.random.default_rng(seed)
+    if rank is None:
+        K = g.standard_normal((P, d))
+    else:
+        K = g.standard_normal((P, rank)) @ g.standard_normal((rank, d))
+    return K + offset * g.standard_normal(d)
+
+
+# ---------------------------------------------------------------- log-sum-exp
+
+def test_lse_closed_forms(orc):
+    n = 37
+    x = np.log(np.arange(1, n + 1, dtype=np.float64))
+    assert orc.lse(x) == pytest.approx(math.log(n * (n + 1) / 2), rel=0, abs=1e-13)
+    # overflow safety: exp(1000) overflows a double, the LSE does not
+    assert orc.lse([1000.0, 1000.0]) == pytest.approx(1000.0 + math.log(2.0), abs=1e-12)
+    assert orc.lse([-np.inf, -np.inf]) == -np.inf
+    assert orc.lse([]) == -np.inf
+    assert orc.lse([-np.inf, 0.0]) == 0.0
+
+
+def test_exact_page_lse_worked_example(orc):
+    """Closed form: with q = (sqrt(d), 0, ...) the logit of token i is its first
+    coordinate; first coordinates log(1..P) give LSE = log(P(P+1)/2).  Pins the
+    1/sqrt(d) scale of the logits."""
+    with open(os.path.join(GOLDEN, "exact_lse_worked_example.json")) as f:
+        g = json.load(f)
+    q, keys = np.array(g["q"]), np.array(g["keys"])
+    assert orc.page_exact_lse(q, keys) == pytest.approx(g["expected"], abs=1e-13)
+    P = keys.shape[0]
+    assert g["expected"] == pytest.approx(math.log(P * (P + 1) / 2), abs=1e-15)
+
+
+# ---------------------------------------------------------------- summaries
+
+@pytest.mark.parametrize("P,d,r", [(16, 64, 4), (16, 64, 16), (64, 128, 8), (64, 32, 8),
+                                   (64, 128, 2), (8, 8, 8)])
+def test_summary_singular_values_match_lapack(orc, P, d, r):
+    K = _page(P, d, seed=P * 1000 + d + r)
+    mu, basis, coef, sigma, sweeps = orc.page_summary(K, r)
+    np.testing.assert_allclose(mu, K.mean(axis=0), rtol=0, atol=1e-14)
+    Kc = K - K.mean(axis=0)
+    s_ref = np.linalg.svd(Kc, compute_uv=False)
+    n = min(P, d)
+    # the centred block has rank <= P - 1: its last value is ~0 when P <= d
+    np.testing.assert_allclose(sigma[:n], s_ref[:n], rtol=1e-12, atol=1e-12 * s_ref[0])
+    assert 0 < sweeps < 100
+
+
+@pytest.mark.parametrize("P,d,r", [(16, 64, 4), (64, 128, 8), (64, 32, 8), (32, 64, 1)])
+def test_summary_eckart_young(orc, P, d, r):
+    """Residual-optimality of the page basis (section 3, Retentiegaranties):
+    ||Kc - C V||_F^2 equals the tail energy sum_{k>=r} sigma_k^2; V has
+    orthonormal rows; C = Kc V^T."""
+    K = _page(P, d, offset=3.0, seed=7 * P + d)
+    mu, basis, coef, sigma, _ = orc.page_summary(K, r)
+    Kc = K - mu
+    resid = np.linalg.norm(Kc - coef @ basis) ** 2
+    tail = np.sum(np.linalg.svd(Kc, compute_uv=False)[r:] ** 2)
+    assert resid == pytest.approx(tail, rel=1e-10, abs=1e-10)
+    np.testing.assert_allclose(basis @ basis.T, np.eye(r), atol=1e-12)
+    np.testing.assert_allclose(coef, Kc @ basis.T, atol=1e-12)
+
+
+def test_summary_subspace_matches_lapack_projector(orc):
+    """With a clear spectral gap the top-r subspace is unique: the projector
+    V^T V must equal LAPACK's (sign and rotation free)."""
+    P, d, r = 64, 128, 8
+    g = np.random.default_rng(3)
+    Q = np.linalg.qr(g.standard_normal((d, 12)))[0]
+    Z = g.standard_normal((P, 12)) * (2.0 ** -np.arange(12))
+    K = Z @ Q.T + 1e-3 * g.standard_normal((P, d))
+    mu, basis, coef, sigma, _ = orc.page_summary(K, r)
+    _, s, vt = np.linalg.svd(K - K.mean(0))
+    np.testing.assert_allclose(basis.T @ basis, vt[:r].T @ vt[:r], atol=1e-9)
+
+
+def test_summary_null_direction_is_zero(orc):
+    """After centring, a P-token block has rank <= P - 1: at r = P <= d the
+    last direction is null and is emitted as zero."""
+    K = _page(8, 32, seed=11)
+    mu, basis, coef, sigma, _ = orc.page_summary(K, 8)
+    assert sigma[-1] < 1e-12 * sigma[0]
+    assert not basis[-1].any() and not coef[:, -1].any()
+
+
+def test_summary_rank_bounds(orc):
+    K = _page(16, 64)
+    with pytest.raises(ValueError):
+        orc.page_summary(K, 17)
+    with pytest.raises(ValueError):
+        orc.page_summary(K, -1)
+
+
+# ---------------------------------------------------------------- the estimator
+
+@pytest.mark.parametrize("P,d", [(16, 64), (64, 128), (64, 32)])
+def test_estimate_full_rank_equals_exact_lse(orc, P, d):
+    """At r = min(P, d) the reconstruction is exact, so the estimate of the
+    displayed equation (section 2) equals the exact page LSE: the exact-LSE
+    selection that reads every key."""
+    K = _page(P, d, offset=1.0, seed=P + d)
+    q = np.random.default_rng(d).standard_normal(d) / math.sqrt(d) * 4
+    mu, basis, coef, _, _ = orc.page_summary(K, min(P, d))
+    assert orc.page_estimate(q, mu, basis, coef) == pytest.approx(orc.page_exact_lse(q, K),
+                                                                  abs=1e-12)
+
+
+def test_estimate_exact_on_low_rank_page(orc):
+    """Keys inside mu + span(r directions): rank r already reconstructs them."""
+    P, d, r = 64, 128, 5
+    K = _page(P, d, rank=r, offset=2.0, seed=5)
+    q = np.random.default_rng(9).standard_normal(d)
+    mu, basis, coef, _, _ = orc.page_summary(K, r)
+    assert orc.page_estimate(q, mu, basis, coef) == pytest.approx(orc.page_exact_lse(q, K),
+                                                                  abs=1e-11)
+    # rank r - 1 is not exact on such a page
+    mu, basis, coef, _, _ = orc.page_summary(K, r - 1)
+    assert abs(orc.page_estimate(q, mu, basis, coef) - orc.page_exact_lse(q, K)) > 1e-6
+
+
+def test_estimate_rank_zero_closed_form(orc):
+    """r = 0: every reconstructed logit is q.mu/sqrt(d), so the estimate is
+    q.mu/sqrt(d) + log P (pins the centroid term and the log P count)."""
+    P, d = 16, 64
+    K = _page(P, d, offset=2.0, seed=2)
+    q = np.random.default_rng(4).standard_normal(d)
+    mu, basis, coef, _, _ = orc.page_summary(K, 0)
+    expect = float(q @ K.mean(0)) / math.sqrt(d) + math.log(P)
+    assert orc.page_estimate(q, mu, basis, coef) == pytest.approx(expect, abs=1e-12)
+
+
+def test_estimate_sign_invariance(orc):
+    """Flipping the sign of (v_k, c_k) leaves the estimate unchanged."""
+    P, d, r = 64, 128, 8
+    K = _page(P, d, seed=21)
+    q = np.random.default_rng(5).standard_normal(d)
+    mu, basis, coef, _, _ = orc.page_summary(K, r)
+    a = orc.page_estimate(q, mu, basis, coef)
+    flip = np.where(np.arange(r) % 3 == 0, -1.0, 1.0)
+    b = orc.page_estimate(q, mu, basis * flip[:, None], coef * flip[None, :])
+    assert a == pytest.approx(b, abs=1e-13)
+
+
+def test_estimate_sees_centroid_shift(orc):
+    """Shifting every key by s shifts every logit by q.s/sqrt(d)."""
+    P, d, r = 16, 64, 4
+    K = _page(P, d, seed=8)
+    s = np.random.default_rng(1).standard_normal(d)
+    q = np.random.default_rng(2).standard_normal(d)
+    e1 = orc.page_estimate(q, *orc.page_summary(K, r)[:3])
+    e2 = orc.page_estimate(q, *orc.page_summary(K + s, r)[:3])
+    assert e2 - e1 == pytest.approx(float(q @ s) / math.sqrt(d), abs=1e-12)
+
+
+# ---------------------------------------------------------------- paged drivers
+
+def _small_layout(wl, orc, **kw):
+    spec = wl.config(0).with_(**kw)
+    layer = wl.make(spec)
+    lay = orc.Layout(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                     layer.block_table, layer.seq_lens)
+    return spec, layer, lay
+
+
+def _tokens(layer, spec, b, g, pool):
+    """All valid tokens of (b, g) in logical order (test-side gather)."""
+    P = spec.page_size
+    n = int(layer.seq_lens[b])
+    rows = []
+    for j in range(-(-n // P)):
+        blk = layer.block_table[b, j]
+        valid = min(P, n - j * P)
+        rows.append(pool[blk, g, :valid])
+    return np.concatenate(rows).astype(np.float64)
+
+
+def test_exact_pages_compose_to_row_lse(wl, orc):
+    """LSE over pages of the exact page LSEs = LSE over all tokens (scipy)."""
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=[1000, 333], batch=2, num_q_heads=4,
+                                     num_kv_heads=2, carriers=2)
+    head, page = orc.exact_pool(lay, layer.q, layer.k_f32())
+    K = layer.k_f32()
+    G = spec.group
+    for b in range(2):
+        for h in range(4):
+            toks = _tokens(layer, spec, b, h // G, K)
+            row = logsumexp(toks @ layer.q[b, h].astype(np.float64) / math.sqrt(spec.head_dim))
+            np.testing.assert_allclose(logsumexp(head[b, h][np.isfinite(head[b, h])]), row,
+                                       atol=1e-12)
+        for g in range(2):
+            np.testing.assert_allclose(page[b, g], logsumexp(head[b, g * G:(g + 1) * G], axis=0),
+                                       atol=1e-12)
+
+
+def test_scan_group_aggregation(wl, orc):
+    """Group mass = LSE over the group's heads (heads h with h // G == g);
+    identical heads give estimate + log G; G = 1 is the identity."""
+    spec, layer, lay = _small_layout(wl, orc, num_q_heads=6, num_kv_heads=2, rank=3)
+    mu, basis, coef = orc.build_pool(lay, spec.rank, layer.k_f32(), spec.num_blocks)
+    head, page = orc.scan_pool(lay, spec.rank, layer.q, mu, basis, coef)
+    f = spec.seq_lens[0] // spec.page_size
+    np.testing.assert_allclose(page[0, :, :f], logsumexp(head[0].reshape(2, 3, -1), axis=1)[:, :f],
+                               atol=1e-12)
+    assert np.all(page[0, :, f:] == -np.inf)
+    q_same = np.repeat(layer.q[:, :1], 6, axis=1)
+    head2, page2 = orc.scan_pool(lay, spec.rank, q_same, mu, basis, coef)
+    np.testing.assert_allclose(page2[0, :, :f], head2[0, ::3, :f] + math.log(3), atol=1e-12)
+    spec1, layer1, lay1 = _small_layout(wl, orc)
+    mu, basis, coef = orc.build_pool(lay1, spec1.rank, layer1.k_f32(), spec1.num_blocks)
+    h1, p1 = orc.scan_pool(lay1, spec1.rank, layer1.q, mu, basis, coef)
+    np.testing.assert_array_equal(h1, p1)
+
+
+def test_scan_full_rank_equals_exact(wl, orc):
+    """Pool-level P1 on the tiny workload at r = min(P, d) = 16, with the
+    summaries kept in double (build_units) so only rounding remains."""
+    spec, layer, lay = _small_layout(wl, orc)
+    f = spec.seq_lens[0] // spec.page_size
+    units = np.array([[0, 0, j] for j in range(f)], np.int32)
+    mu, basis, coef, sigma = orc.build_units(lay, 16, layer.k_f32(), units)
+    _, exact = orc.exact_pool(lay, layer.q, layer.k_f32())
+    for u in range(f):
+        est = orc.page_estimate(layer.q[0, 0], mu[u], basis[u], coef[u])
+        assert est == pytest.approx(exact[0, 0, u], abs=1e-12)
+
+
+def test_build_pool_matches_units(wl, orc):
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=[200, 70], batch=2, carriers=1)
+    mu, basis, coef = orc.build_pool(lay, spec.rank, layer.k_f32(), spec.num_blocks)
+    units = np.array([[b, 0, j] for b in range(2) for j in range(spec.seq_lens[b] // 16)],
+                     np.int32)
+    mu_u, basis_u, coef_u, _ = orc.build_units(lay, spec.rank, layer.k_f32(), units)
+    for n, (b, g, j) in enumerate(units):
+        blk = layer.block_table[b, j]
+        np.testing.assert_array_equal(mu[blk, g], mu_u[n].astype(np.float32))
+        np.testing.assert_array_equal(basis[blk, g], basis_u[n].astype(np.float32))
+        np.testing.assert_array_equal(coef[blk, g], coef_u[n].astype(np.float32))
+
+
+# ---------------------------------------------------------------- selection
+
+def _brute_topk(mass, k):
+    order = sorted(range(len(mass)), key=lambda j: (-float(mass[j]), j))
+    return sorted(order[:k])
+
+
+@pytest.mark.parametrize("trial", range(40))
+def test_select_matches_brute_force(orc, trial):
+    g = np.random.default_rng(trial)
+    n = int(g.integers(0, 70))
+    # few distinct values -> many exact ties
+    levels = g.standard_normal(max(1, int(g.integers(1, 6)))).astype(np.float32)
+    mass = levels[g.integers(0, levels.size, n)] if trial % 2 else \
+        g.standard_normal(n).astype(np.float32)
+    if n and trial % 5 == 0:
+        mass[g.integers(0, n)] = -np.inf
+    k = int(g.integers(0, 80))
+    width = max(k, 1) + int(g.integers(0, 3))
+    sel, sm, kk = orc.select_topk(mass, k, width)
+    ref = _brute_topk(mass, min(k, n))
+    assert kk == len(ref)
+    assert list(sel[:kk]) == ref
+    assert np.all(sel[kk:] == -1) and np.all(sm[kk:] == -np.inf)
+    np.testing.assert_array_equal(sm[:kk], mass[ref])
+
+
+def test_select_matches_numpy_stable_sort(orc):
+    mass = np.round(np.random.default_rng(0).standard_normal(5000), 1).astype(np.float32)
+    sel, _, _ = orc.select_topk(mass, 300)
+    ref = np.sort(np.argsort(-mass, kind="stable")[:300])
+    np.testing.assert_array_equal(sel, ref)
+
+
+def test_select_pool_budget_rules(wl, orc):
+    """k = floor(budget / P) pages, at most the full pages; the partial last
+    page is never a candidate; a budget below one page selects nothing."""
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=[100], carriers=1)
+    pm = np.zeros((1, 1, spec.max_pages), np.float32)
+    pm[0, 0, :] = np.arange(spec.max_pages, dtype=np.float32)  # the tail page would win
+    sel, sm = orc.select_pool(lay, 10 * 16, pm, 10)
+    assert list(sel[0, 0]) == [0, 1, 2, 3, 4, 5, -1, -1, -1, -1]  # 6 full pages of 7
+    sel, _ = orc.select_pool(lay, 3 * 16 + 15, pm, 3)
+    assert list(sel[0, 0]) == [3, 4, 5]
+    sel, _ = orc.select_pool(lay, 15, pm, 1)
+    assert list(sel[0, 0]) == [-1]
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa_ref(q, K, V):
+    """torch's scaled-dot-product attention (CPU, float64) for one query."""
+    qt = torch.from_numpy(np.asarray(q, np.float64)).view(1, 1, 1, -1)
+    kt = torch.from_numpy(np.asarray(K, np.float64)).view(1, 1, K.shape[0], -1)
+    vt = torch.from_numpy(np.asarray(V, np.float64)).view(1, 1, V.shape[0], -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).view(-1).numpy()
+
+
+def test_attend_tokens_matches_sdpa(orc):
+    g = np.random.default_rng(7)
+    for n, d in [(1, 8), (17, 64), (300, 128)]:
+        q = g.standard_normal(d)
+        K, V = g.standard_normal((n, d)), g.standard_normal((n, d))
+        out, l = orc.attend_tokens(q, K, V)
+        np.testing.assert_allclose(out, _sdpa_ref(q, K, V), atol=1e-12)
+        assert l == pytest.approx(logsumexp(K @ q / math.sqrt(d)), abs=1e-12)
+    out, l = orc.attend_tokens(np.ones(4), np.zeros((0, 4)), np.zeros((0, 4)))
+    assert l == -np.inf and not out.any()
+
+
+def test_dense_attend_pool_matches_sdpa(wl, orc):
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=[1000, 333], batch=2, num_q_heads=4,
+                                     num_kv_heads=2, carriers=2)
+    out, lse = orc.attend_pool(lay, layer.q, layer.k_f32(), layer.v_f32(), None)
+    for b in range(2):
+        for h in range(4):
+            K = _tokens(layer, spec, b, h // 2, layer.k_f32())
+            V = _tokens(layer, spec, b, h // 2, layer.v_f32())
+            np.testing.assert_allclose(out[b, h], _sdpa_ref(layer.q[b, h], K, V), atol=1e-12)
+
+
+def test_select_all_pages_reproduces_dense(wl, orc):
+    """A budget covering every page gives exactly dense attention, including
+    a partial last page (attended outside the budget)."""
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=[1000, 333], batch=2, num_q_heads=4,
+                                     num_kv_heads=2, carriers=2)
+    mu, basis, coef = orc.build_pool(lay, spec.rank, layer.k_f32(), spec.num_blocks)
+    _, page = orc.scan_pool(lay, spec.rank, layer.q, mu, basis, coef)
+    width = spec.max_pages
+    sel, _ = orc.select_pool(lay, 10 ** 6, page.astype(np.float32), width)
+    o_s, l_s = orc.attend_pool(lay, layer.q, layer.k_f32(), layer.v_f32(), sel)
+    o_d, l_d = orc.attend_pool(lay, layer.q, layer.k_f32(), layer.v_f32(), None)
+    np.testing.assert_allclose(o_s, o_d, atol=1e-13)
+    np.testing.assert_allclose(l_s, l_d, atol=1e-13)
+
+
+def test_sparse_attend_uses_only_listed_pages(wl, orc):
+    """Attention over a page list equals SDPA over exactly those tokens plus
+    the partial last page."""
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=[1000], carriers=2)
+    sel = np.full((1, 1, 5), -1, np.int32)
+    sel[0, 0, :3] = [2, 17, 40]
+    out, _ = orc.attend_pool(lay, layer.q, layer.k_f32(), layer.v_f32(), sel)
+    P = spec.page_size
+    K, V = layer.k_f32(), layer.v_f32()
+    pages = [2, 17, 40, 62]
+    Kt = np.concatenate([K[layer.block_table[0, j], 0, :min(P, 1000 - j * P)] for j in pages])
+    Vt = np.concatenate([V[layer.block_table[0, j], 0, :min(P, 1000 - j * P)] for j in pages])
+    np.testing.assert_allclose(out[0, 0], _sdpa_ref(layer.q[0, 0], Kt, Vt), atol=1e-12)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def test_pins_catch_planted_mistakes(orc):
+    """The pins above fail on plausible slips.  Each mutant is a deliberate
+    mistake applied to oracle outputs on the CPU (a dropped centroid term, a
+    wrong scale, a transposed basis) and must be caught by one pin."""
+    P, d = 16, 64
+    K = _page(P, d, offset=1.0, seed=99)
+    q = np.random.default_rng(3).standard_normal(d)
+    mu, basis, coef, _, _ = orc.page_summary(K, min(P, d))
+    exact = orc.page_exact_lse(q, K)
+    # dropped centroid term
+    assert abs(orc.page_estimate(q, np.zeros(d), basis, coef) - exact) > 1e-3
+    # logits scaled by 1/d instead of 1/sqrt(d)
+    assert abs(orc.page_estimate(q / math.sqrt(d), mu, basis, coef) - exact) > 1e-3
+    # basis used transposed within the page's subspace: coefficient columns permuted
+    assert abs(orc.page_estimate(q, mu, basis, coef[:, ::-1]) - exact) > 1e-3
