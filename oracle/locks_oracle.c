@@ -445,7 +445,7 @@ int orc_attend_pool(const orc_layout* L, const float* q, const float* k_pool,
     for (int64_t bh = 0; bh < rows; ++bh) {
         const int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h / G;
         const int full = full_pages(L, b), np = all_pages(L, b);
-        /* gather the attended pages, in ascending order */
+        /* the attended pages, in ascending order */
         int32_t* pages = (int32_t*)malloc(sizeof(int32_t) * (size_t)(np > 0 ? np : 1));
         int n_pages = 0;
         if (sel_pages) {
@@ -456,25 +456,45 @@ int orc_attend_pool(const orc_layout* L, const float* q, const float* k_pool,
         } else {
             for (int j = 0; j < np; ++j) pages[n_pages++] = j;
         }
-        double* keys = (double*)malloc(sizeof(double) * (size_t)(n_pages > 0 ? n_pages : 1) * P * d);
-        double* vals = (double*)malloc(sizeof(double) * (size_t)(n_pages > 0 ? n_pages : 1) * P * d);
         double* qh = (double*)malloc(sizeof(double) * (size_t)d);
+        widen((size_t)d, q + (size_t)bh * d, qh);
+        /* pass 1: logits of every attended token, and their LSE */
         int n_tok = 0;
         for (int t = 0; t < n_pages; ++t) {
             const int j = pages[t];
-            const int valid = L->seq_lens[b] - j * P < P ? L->seq_lens[b] - j * P : P;
-            widen((size_t)valid * d, page_ptr(L, k_pool, b, g, j), keys + (size_t)n_tok * d);
-            widen((size_t)valid * d, page_ptr(L, v_pool, b, g, j), vals + (size_t)n_tok * d);
-            n_tok += valid;
+            n_tok += L->seq_lens[b] - j * P < P ? L->seq_lens[b] - j * P : P;
         }
-        widen((size_t)d, q + (size_t)bh * d, qh);
-        double l;
-        orc_attend_tokens(n_tok, d, qh, keys, vals, out + (size_t)bh * d, &l);
-        if (lse) lse[bh] = l;
+        double* logit = (double*)malloc(sizeof(double) * (size_t)(n_tok > 0 ? n_tok : 1));
+        const double scale = 1.0 / sqrt((double)d);
+        int idx = 0;
+        for (int t = 0; t < n_pages; ++t) {
+            const int j = pages[t];
+            const int valid = L->seq_lens[b] - j * P < P ? L->seq_lens[b] - j * P : P;
+            const float* kp = page_ptr(L, k_pool, b, g, j);
+            for (int i = 0; i < valid; ++i) {
+                double sdot = 0.0;
+                for (int e = 0; e < d; ++e) sdot += qh[e] * (double)kp[(size_t)i * d + e];
+                logit[idx++] = sdot * scale;
+            }
+        }
+        const double Lse = orc_lse(n_tok, logit);
+        /* pass 2: out = sum_i exp(logit_i - LSE) v_i */
+        double* o = out + (size_t)bh * d;
+        for (int e = 0; e < d; ++e) o[e] = 0.0;
+        idx = 0;
+        for (int t = 0; t < n_pages; ++t) {
+            const int j = pages[t];
+            const int valid = L->seq_lens[b] - j * P < P ? L->seq_lens[b] - j * P : P;
+            const float* vp = page_ptr(L, v_pool, b, g, j);
+            for (int i = 0; i < valid; ++i) {
+                const double p = exp(logit[idx++] - Lse);
+                for (int e = 0; e < d; ++e) o[e] += p * (double)vp[(size_t)i * d + e];
+            }
+        }
+        if (lse) lse[bh] = n_tok > 0 ? Lse : -INFINITY;
         free(pages);
-        free(keys);
-        free(vals);
         free(qh);
+        free(logit);
     }
     return 0;
 }
