@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the page-summary hot path on one MI355X.
+
+One step = one layer's decode step as a replayed HIP graph: summary scan +
+page-mass aggregation, top-k page selection, sparse paged flash-decode over
+the selected pages (+ partial last pages) and the LSE merge.  Inputs are
+resident in HBM before timing.  Layer copies are rotated so that repeated
+steps do not hit in the 256 MB Infinity Cache.
+
+Also measured in the same run: the summary-scan kernel alone (the dominant
+kernel, for the roofline), the dense paged flash-decode baseline (speedup),
+the summary build (prefill-time throughput), and the CPU oracle on a bounded
+sample (cpu_baseline).
+
+Prints ONE JSON line.  Default workload: GLM-4-9B-shaped layer, 1M tokens,
+r = 8, budget 2048 (the headline configuration).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/decode step at 1M ctx r=8 + HBM GB/s (% peak); speedup vs dense decode"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=0, help="layer copies rotated (0 = auto)")
+    ap.add_argument("--budget", type=int, default=0, help="override the token budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-target-s", type=float, default=12.0,
+                    help="approximate CPU seconds spent on the oracle sample")
+    ap.add_argument("--threads", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def time_events(fn, iters, torch):
+    """Average device time per call of fn() over `iters` calls, each bracketed
+    by events on the current stream (the stream the library launches on)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return statistics.mean(ms) * 1e3, statistics.median(ms) * 1e3, ms
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path is single-GPU; see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_page_rank_amd as lk
+    import workload
+    from kv_cache_page_rank_amd import traffic
+    from workload.device import upload
+
+    if not os.path.exists(lk.LIB_PATH):
+        from kv_cache_page_rank_amd import build as _b
+        _b.build()
+    lk.lib()
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+
+    spec = workload.config(args.config)
+    if args.budget:
+        spec = spec.with_(budget_tokens=args.budget)
+    threads = args.threads or cpu_threads()
+    t0 = time.time()
+    layer = workload.make(spec, threads=threads)
+    log(f"generated {spec.name} in {time.time() - t0:.1f}s")
+    q, kv0, pages = upload(layer, "cuda")
+    B, Hq, Hkv, d, P, r = (spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                           spec.page_size, spec.rank)
+    NB, MP, k = spec.num_blocks, spec.max_pages, spec.k_pages
+    full = [n // P for n in spec.seq_lens]
+    partial = sum(1 for n in spec.seq_lens if n % P)
+    full_total = sum(full)
+
+    # layer copies: summary + K/V working set per copy; rotate beyond 2 x 256 MB of MALL
+    sum_bytes = NB * Hkv * traffic.summary_unit_bytes(d, P, r)
+    L = args.layers or max(1, min(8, math.ceil(2 * 256e6 / max(sum_bytes, 1)) + 1))
+    kvs = [kv0] + [lk.PagedKV(kv0.k.clone(), kv0.v.clone()) for _ in range(L - 1)]
+    summs = [lk.Summaries.empty(NB, Hkv, P, d, r) for _ in range(L)]
+
+    # --- build (prefill-time summary construction), timed on layer 0
+    torch.cuda.synchronize()
+    bstart, bend = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bstart.record()
+    lk.locks_build_summaries(kvs[0], pages, summs[0])
+    bend.record()
+    torch.cuda.synchronize()
+    build_ms = bstart.elapsed_time(bend)
+    for i in range(1, L):
+        lk.locks_build_summaries(kvs[i], pages, summs[i])
+    torch.cuda.synchronize()
+    log(f"built {full_total * Hkv} page summaries in {build_ms:.2f} ms (x{L} layers)")
+
+    # --- one step graph per layer copy
+    ws_step = lk.workspace_bytes(lk.OP_STEP, B, MP, Hq, Hkv, P, d, r, k)
+    bufs = []
+    graphs = []
+    for i in range(L):
+        sel = torch.empty((B, Hkv, k), dtype=torch.int32, device="cuda")
+        mass = torch.empty((B, Hkv, k), device="cuda")
+        out = torch.empty((B, Hq, d), dtype=kv0.k.dtype, device="cuda")
+        lse = torch.empty((B, Hq), device="cuda")
+        ws = lk.workspace(ws_step)
+        bufs.append((sel, mass, out, lse, ws))
+        graphs.append(lk.StepGraph(q, summs[i], kvs[i], pages, spec.budget_tokens, sel, mass, out,
+                                   lse, ws=ws))
+
+    for i in range(args.warmup):
+        graphs[i % L].launch()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % L].launch()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    step_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    log(f"step: {step_us:.2f} us (graph replay, {L} layer copies), wall {wall_s * 1e6 / args.steps:.2f} us")
+
+    # --- dominant kernel: the summary scan alone, per-launch events on the launch stream
+    pms = [torch.empty((B, Hkv, MP), device="cuda") for _ in range(L)]
+    for i in range(args.warmup):
+        lk.locks_scan(q, summs[i % L], pages, pms[i % L])
+    scan_mean, scan_med, _ = time_events(
+        lambda i: lk.locks_scan(q, summs[i % L], pages, pms[i % L]), args.steps, torch)
+    scan_b = traffic.scan_bytes(B, Hq, Hkv, MP, full_total, d, P, r)
+    scan_gbs = scan_b / (scan_mean * 1e-6) / 1e9
+    log(f"scan: {scan_mean:.2f} us mean ({scan_med:.2f} median), {scan_gbs:.0f} GB/s")
+
+    # --- select alone and sparse attention alone
+    sel_ws = lk.workspace(lk.workspace_bytes(lk.OP_SELECT, B, MP, Hq, Hkv, P, d, r, k))
+    sel_mean, _, _ = time_events(
+        lambda i: lk.locks_select(q, summs[i % L], pages, spec.budget_tokens, bufs[i % L][0],
+                                  bufs[i % L][1], ws=sel_ws), args.steps, torch)
+    att_ws = lk.workspace(lk.workspace_bytes(lk.OP_SPARSE_ATTEND, B, MP, Hq, Hkv, P, d, r, k))
+    sparse_mean, _, _ = time_events(
+        lambda i: lk.locks_sparse_attend(q, kvs[i % L], pages, bufs[i % L][0], bufs[i % L][2],
+                                         bufs[i % L][3], ws=att_ws), args.steps, torch)
+    step_b = traffic.step_bytes(full_total, partial, Hkv, d, P, r, B * Hkv * k)
+    log(f"select (scan+topk): {sel_mean:.2f} us, sparse attend+merge: {sparse_mean:.2f} us")
+
+    # --- dense baseline
+    dense_mean = None
+    dense_b = traffic.dense_bytes(sum(-(-n // P) for n in spec.seq_lens), Hkv, d, P)
+    if not args.no_dense:
+        dws = lk.workspace(lk.workspace_bytes(lk.OP_DENSE_ATTEND, B, MP, Hq, Hkv, P, d, r, 0))
+        dout = torch.empty((B, Hq, d), dtype=kv0.k.dtype, device="cuda")
+        dlse = torch.empty((B, Hq), device="cuda")
+        for i in range(2):
+            lk.locks_dense_attend(q, kvs[i % L], pages, dout, dlse, ws=dws)
+        dense_mean, _, _ = time_events(
+            lambda i: lk.locks_dense_attend(q, kvs[i % L], pages, dout, dlse, ws=dws),
+            max(5, args.steps // 5), torch)
+        log(f"dense: {dense_mean:.2f} us, {dense_b / (dense_mean * 1e-6) / 1e9:.0f} GB/s")
+
+    # --- CPU baseline: the oracle on a bounded sample of the same step
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, layer, summs[0], sel_np=bufs[0][0].cpu().numpy(),
+                           target_s=args.cpu_target_s, threads=threads)
+
+    ratio = traffic.summary_to_cache_ratio(d, P, r)
+    result = {
+        "metric": METRIC,
+        "value": round(step_us, 3),
+        "unit": "µs/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": d, "page_size": P, "context_tokens": spec.seq_lens
+                   if B > 1 else spec.seq_lens[0], "rank": r, "budget_tokens": spec.budget_tokens,
+                   "kv_dtype": "bf16" if spec.kv_bf16 else "f32", "summary_dtype": "f32",
+                   "layer_copies_rotated": L, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": "summary scan",
+                     "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": scan_b, "avg_launch_us": round(scan_mean, 3)},
+        "cpu_baseline": cpu,
+        "breakdown": {
+            "scan_us": round(scan_mean, 3),
+            "select_us": round(sel_mean, 3),
+            "sparse_attend_us": round(sparse_mean, 3),
+            "dense_attend_us": None if dense_mean is None else round(dense_mean, 3),
+            "speedup_vs_dense": None if dense_mean is None else round(dense_mean / step_us, 3),
+            "step_bytes": step_b,
+            "dense_bytes": dense_b,
+            "byte_reduction": round(dense_b / step_b, 3),
+            "step_GBps": round(step_b / (step_us * 1e-6) / 1e9, 1),
+            "dense_GBps": None if dense_mean is None else
+            round(dense_b / (dense_mean * 1e-6) / 1e9, 1),
+            "summary_to_cache_ratio": round(ratio, 4),
+            "build_ms": round(build_ms, 3),
+            "build_pages_per_s": round(full_total * Hkv / (build_ms * 1e-3), 1),
+        },
+    }
+    for g in graphs:
+        g.close()
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(spec, layer, summ0, sel_np, target_s, threads):
+    """Time the oracle's decode step on the host cores: scan + aggregation
+    over every full page (from the same summaries), selection from those
+    masses, and attention over the GPU-selected page list.  The whole step
+    is repeated until about target_s seconds of CPU time have been spent
+    (or, when one step alone is longer, a prefix of the pages is scanned and
+    scaled).  Returns the record for the JSON line."""
+    import numpy as np
+
+    import oracle
+
+    P, Hkv = spec.page_size, spec.num_kv_heads
+    mu = summ0.mu.cpu().numpy()
+    basis = summ0.basis.cpu().numpy()
+    coef = summ0.coef.cpu().numpy()
+    full_total = sum(n // P for n in spec.seq_lens)
+    kf, vf = layer.k_f32(), layer.v_f32()  # widened once, outside the timed calls
+
+    def step(npages):
+        """One oracle step over the first npages full pages of each sequence."""
+        seq = np.array([min(n, npages * P) for n in spec.seq_lens], np.int32)
+        lay = oracle.Layout(spec.num_q_heads, Hkv, spec.head_dim, P, layer.block_table, seq)
+        t0 = time.perf_counter()
+        _, pm = oracle.scan_pool(lay, spec.rank, layer.q, mu, basis, coef, threads=threads,
+                                 heads=False)
+        t1 = time.perf_counter()
+        oracle.select_pool(lay, spec.budget_tokens, pm.astype(np.float32), spec.k_pages)
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1, int(sum(s // P for s in seq))
+
+    lay_full = oracle.Layout(spec.num_q_heads, Hkv, spec.head_dim, P, layer.block_table,
+                             layer.seq_lens)
+    t0 = time.perf_counter()
+    oracle.attend_pool(lay_full, layer.q, kf, vf, sel_np, threads=threads)
+    att_s = time.perf_counter() - t0
+
+    npages = max(full_total, 1)
+    scan_s, sel_s, done = step(npages)
+    reps = 1
+    if scan_s + sel_s + att_s > target_s:  # one step is already long: scan a prefix
+        npages = max(1, int(npages * target_s / (scan_s + sel_s + att_s)))
+        scan_s, sel_s, done = step(npages)
+        scan_s *= full_total / max(done, 1)
+        sample = f"scan+aggregation+selection over the first {done} of {full_total} full pages " \
+                 f"(x{Hkv} KV heads), scaled to all pages; attention over the selected pages"
+    else:
+        reps = max(1, int(target_s / (scan_s + sel_s + att_s)))
+        tot_scan = tot_sel = tot_att = 0.0
+        for _ in range(reps):
+            a, s_, _ = step(npages)
+            t0 = time.perf_counter()
+            oracle.attend_pool(lay_full, layer.q, kf, vf, sel_np, threads=threads)
+            tot_att += time.perf_counter() - t0
+            tot_scan += a
+            tot_sel += s_
+        scan_s, sel_s, att_s = tot_scan / reps, tot_sel / reps, tot_att / reps
+        sample = f"the full step (scan+aggregation over all {full_total} full pages x{Hkv} KV " \
+                 f"heads, selection, attention over the selected pages), mean of {reps} repeats"
+    step_s = scan_s + sel_s + att_s
+    log(f"cpu oracle: scan {scan_s * 1e3:.1f} ms, select {sel_s * 1e3:.1f} ms, attend "
+        f"{att_s * 1e3:.1f} ms -> {step_s * 1e6:.0f} us/step on {threads} threads ({sample})")
+    return {"value": round(step_s * 1e6, 1), "unit": "µs/step", "cores": threads,
+            "kind": "oracle", "sample": sample}
+
+
+if __name__ == "__main__":
+    main()

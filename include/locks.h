@@ -1,0 +1,254 @@
+/*
+ * locks.h - C ABI of the MI355X (gfx950) library for the decode-step hot
+ * path of page-local key summaries (LOCKS, "Page-Local Compact Key Summaries
+ * for Efficient Long-Context Decoding", arXiv 2607.24555).
+ *
+ * The decode step has three parts, each an entry point here:
+ *   1. locks_build_summaries - a rank-r spectral summary per finished page:
+ *      centroid, top-r eigenvectors of the centred keys, per-token
+ *      coefficients (gist.science technical summary, section 2, subsection
+ *      Pagina-lokale Spectrale Decompositie);
+ *   2. locks_select - scan every summary, reconstruct within-page logits and
+ *      take their log-sum-exp as the page's estimated attention mass, share
+ *      one page table per GQA group, keep the top pages within a token
+ *      budget; it reads no key or value (same section, subsections
+ *      Reconstructie en Selectie and Group-Shared Selection; English
+ *      abstract on the insight.aitobox.com page);
+ *   3. locks_sparse_attend - attention over the selected pages only
+ *      (abstract), against the locks_dense_attend baseline (abstract:
+ *      latency compared with dense attention).
+ * The whole step (2 + 3) can be captured once and replayed as a HIP graph
+ * (technical summary, section 2, subsection Implementatie: the decode step
+ * runs inside full graphs).
+ *
+ * Conventions
+ *  - All tensor pointers are DEVICE pointers owned by the caller; sizes are
+ *    element counts.  The library allocates nothing on the step path and
+ *    keeps no state between calls except caller-owned graph handles.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
+ *    are asynchronous on it and do no host synchronisation, so they can be
+ *    captured into a graph.
+ *  - Validation happens on the host before any launch; a failed check
+ *    returns a status and launches nothing.  Device-side contents (block
+ *    table entries, sequence lengths) cannot be checked on the host: kernels
+ *    clamp page counts to max_pages and skip block ids outside
+ *    [0, num_blocks), so bad contents give wrong values, never a fault.
+ *  - Launch failures return LOCKS_ERR_HIP; locks_last_hip_error() gives the
+ *    hipError_t of the last failure on the calling thread.
+ *  - Page indices returned by selection are LOGICAL page numbers j within a
+ *    sequence (page j holds tokens [jP, jP + P)); the block table maps them
+ *    to physical blocks.
+ *  - Only full pages (j < seq_len / P) have summaries and compete for the
+ *    budget; a partial last page is always attended, outside the budget.
+ *
+ * Layouts (row-major, innermost last)
+ *   q            [B][H_q][d]             float32, one decode query per head
+ *   K pool       [NB][H_kv][P][d]        bf16 or float32 (keys of a page contiguous)
+ *   V pool       [NB][H_kv][d][P]        bf16 or float32 (each page stored transposed)
+ *   block_table  [B][max_pages]          int32, logical page -> physical block
+ *   seq_lens     [B]                     int32 tokens per sequence
+ *   mu           [NB][H_kv][d]           float32 page centroid
+ *   basis        [NB][H_kv][r][d]        float32, row k = k-th eigenvector
+ *   coef         [NB][H_kv][P][r]        float32, coef[i][k] = basis_k . (k_i - mu)
+ *   page_logmass [B][H_kv][max_pages]    float32 group log-mass, -inf if not a full page
+ *   sel_pages    [B][H_kv][width]        int32 ascending logical pages, -1 padded
+ *   sel_logmass  [B][H_kv][width]        float32 their log-masses, -inf padded
+ *   out          [B][H_q][d]             cache dtype (bf16 rounded to nearest even)
+ *   out_lse      [B][H_q]                float32 natural-log LSE of the attended logits
+ * Query head h reads KV head g = h / (H_q / H_kv).  Logits are q.k / sqrt(d).
+ *
+ * Supported shapes (others return LOCKS_ERR_UNSUPPORTED):
+ *   P in {16, 64}; d in {64, 128}; 1 <= r <= min(P, d, 16);
+ *   G = H_q / H_kv in 1..16; max_pages <= 32768;
+ *   bf16 caches need P = 64; float32 caches any supported P.
+ */
+#ifndef LOCKS_H
+#define LOCKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LOCKS_OK = 0,
+    LOCKS_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shapes */
+    LOCKS_ERR_UNSUPPORTED = 2, /* valid but not instantiated (see supported shapes) */
+    LOCKS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than locks_workspace_bytes() */
+    LOCKS_ERR_HIP = 4          /* a HIP call failed; see locks_last_hip_error() */
+} locks_status;
+
+typedef enum { LOCKS_F32 = 0, LOCKS_BF16 = 1 } locks_dtype;
+
+/* Operations for locks_workspace_bytes(). */
+typedef enum {
+    LOCKS_OP_BUILD = 0,
+    LOCKS_OP_SELECT = 1,
+    LOCKS_OP_SPARSE_ATTEND = 2,
+    LOCKS_OP_DENSE_ATTEND = 3,
+    LOCKS_OP_STEP = 4 /* select + sparse attend, as captured by locks_step_graph_create */
+} locks_op;
+
+/* Paged K/V cache of one layer.  v may be NULL for locks_build_summaries. */
+typedef struct {
+    int32_t dtype; /* locks_dtype of both pools */
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t page_size;
+    int32_t head_dim;
+    const void* k; /* [NB][H_kv][P][d] */
+    const void* v; /* [NB][H_kv][d][P] */
+} locks_kv_cache;
+
+/* Resident summaries of one layer, stored by physical block. */
+typedef struct {
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t page_size;
+    int32_t head_dim;
+    int32_t rank;
+    float* mu;    /* [NB][H_kv][d] */
+    float* basis; /* [NB][H_kv][r][d] */
+    float* coef;  /* [NB][H_kv][P][r] */
+} locks_summaries;
+
+/* Block table of a batch of sequences. */
+typedef struct {
+    int32_t batch;
+    int32_t max_pages;
+    const int32_t* block_table; /* [B][max_pages] */
+    const int32_t* seq_lens;    /* [B] */
+} locks_page_table;
+
+/* Bytes of workspace an operation needs for these shapes (0 if none).
+ * k_pages is the selection width floor(budget_tokens / page_size). */
+size_t locks_workspace_bytes(int32_t op, int32_t batch, int32_t max_pages, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t page_size, int32_t head_dim,
+                             int32_t rank, int32_t k_pages);
+
+/*
+ * Step 1 - build the summary of every full page j with
+ * page_begin[b] <= j < seq_lens[b] / P, for every KV head
+ * (technical summary, section 2, Pagina-lokale Spectrale Decompositie: a
+ * small eigendecomposition of the page's centred keys when the page is
+ * final; the summary keeps the top-r eigenvectors and each token's
+ * coefficients).  Per (page, KV head): mu = mean key; Kc = K - 1 mu^T;
+ * the top-r eigenpairs (lambda_k, u_k) of the P x P Gram Kc Kc^T;
+ * basis_k = Kc^T u_k / sqrt(lambda_k); coef[i][k] = sqrt(lambda_k) u_k[i].
+ * Eigenvalues below 3e-5 * lambda_max give zero basis/coef (numerically null).
+ * page_begin: device [B] or NULL (= all full pages).  Summaries of other
+ * blocks are left untouched.  summaries->rank is r.  Needs no workspace
+ * (ws may be NULL).
+ */
+locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
+                                   const int32_t* page_begin, const locks_summaries* out,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 2 - score every full page from its summary alone and select the top
+ * pages per (sequence, KV group).  For each head h of group g:
+ *   t = V_j^T q_h, beta = q_h . mu_j,
+ *   s_hat_{j,h} = log sum_i exp((beta + t . c_i) / sqrt(d))
+ * (technical summary, section 2, Reconstructie en Selectie, the displayed
+ * estimator; the LSE of the reconstructed logits is the page's mass).
+ * Group score a_{j,g} = log sum_{h in g} exp(s_hat_{j,h}): one shared
+ * selection per GQA group (section 2, Group-Shared Selection; the group
+ * score is read here as the sum of the heads' unnormalised masses).
+ * Selection: k_b = min(floor(budget_tokens / P), full pages of b) pages
+ * with the largest a (equal fp32 values: lowest j first), written in
+ * ascending j to sel_pages / sel_logmass rows of width floor(budget/P),
+ * padded with -1 / -inf.  No K or V pointer is taken: selection reads no
+ * candidate key or value (abstract).
+ * page_logmass: optional device [B][H_kv][max_pages] output (NULL: the
+ * workspace holds it).  Workspace: locks_workspace_bytes(LOCKS_OP_SELECT,..).
+ */
+locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
+                          const locks_page_table* pages, int32_t budget_tokens,
+                          int32_t* sel_pages, float* sel_logmass, float* page_logmass, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Step 2 alone: the page masses without selection (same definitions as
+ * locks_select).  page_logmass [B][H_kv][max_pages] is required;
+ * head_logmass [B][H_q][max_pages] (per-head s_hat) is optional.
+ * Entries of pages that are not full, or past max_pages' valid range, are -inf.
+ */
+locks_status locks_scan(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
+                        const locks_page_table* pages, float* page_logmass, float* head_logmass,
+                        void* stream);
+
+/*
+ * Step 2's selection alone, from given group masses page_logmass
+ * [B][H_kv][max_pages] (only entries j < seq_lens[b] / P are read), with the
+ * rule of locks_select.  width = row width of sel_pages / sel_logmass.
+ */
+locks_status locks_topk(const float* page_logmass, const locks_page_table* pages,
+                        int32_t num_kv_heads, int32_t page_size, int32_t budget_tokens,
+                        int32_t width, int32_t* sel_pages, float* sel_logmass, void* stream);
+
+/*
+ * Step 3 - attention of every query head over the tokens of its group's
+ * selected pages plus the sequence's partial last page (abstract: only the
+ * top pages are attended).  The softmax is renormalised over exactly these
+ * tokens.  sel_pages [B][H_kv][k_pages] as written by locks_select (-1 and
+ * indices that are not full pages are ignored).  Split-K: one partial
+ * (max, sum, output) per selected page, merged by log-sum-exp in page-list
+ * order.  out: cache dtype; out_lse optional.
+ * Workspace: locks_workspace_bytes(LOCKS_OP_SPARSE_ATTEND, ...).
+ */
+locks_status locks_sparse_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,
+                                 const locks_page_table* pages, const int32_t* sel_pages,
+                                 int32_t k_pages, void* out, float* out_lse, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
+ * Baseline - the same attention over every token of every sequence (the
+ * dense attention the pages compare decode latency against; abstract).
+ * Workspace: locks_workspace_bytes(LOCKS_OP_DENSE_ATTEND, ...).
+ */
+locks_status locks_dense_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,
+                                const locks_page_table* pages, void* out, float* out_lse,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Everything one decode step needs (select + sparse attend). */
+typedef struct {
+    const float* q;
+    int32_t num_q_heads;
+    int32_t budget_tokens;
+    locks_summaries summaries;
+    locks_kv_cache cache;
+    locks_page_table pages;
+    int32_t* sel_pages;   /* [B][H_kv][floor(budget/P)] */
+    float* sel_logmass;   /* same shape */
+    float* page_logmass;  /* optional [B][H_kv][max_pages] */
+    void* out;            /* [B][H_q][d] cache dtype */
+    float* out_lse;       /* optional [B][H_q] */
+    void* ws;             /* locks_workspace_bytes(LOCKS_OP_STEP, ...) */
+    size_t ws_bytes;
+} locks_step_args;
+
+typedef struct locks_step_graph locks_step_graph;
+
+/*
+ * Capture one decode step (locks_select then locks_sparse_attend, with the
+ * argument pointers given) into an instantiated HIP graph (technical
+ * summary, section 2, Implementatie: scoring, selection and sparse attention
+ * run inside full graphs).  The pointers are baked in: replay reads the
+ * current contents of the same buffers.  *graph receives a handle owned by
+ * the caller.
+ */
+locks_status locks_step_graph_create(const locks_step_args* args, locks_step_graph** graph);
+locks_status locks_step_graph_launch(locks_step_graph* graph, void* stream);
+void locks_step_graph_destroy(locks_step_graph* graph);
+
+const char* locks_status_string(int32_t status);
+int32_t locks_last_hip_error(void);
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t locks_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,264 @@
+"""Python binding of liblocks.so, the gfx950 library for the decode-step hot
+path of page-local key summaries (see include/locks.h for the C ABI).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: if the library is not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblocks.so")
+
+LOCKS_OK, LOCKS_ERR_INVALID_ARG, LOCKS_ERR_UNSUPPORTED, LOCKS_ERR_WORKSPACE, LOCKS_ERR_HIP = \
+    range(5)
+LOCKS_F32, LOCKS_BF16 = 0, 1
+OP_BUILD, OP_SELECT, OP_SPARSE_ATTEND, OP_DENSE_ATTEND, OP_STEP = range(5)
+
+EXPORTED = ("locks_workspace_bytes", "locks_build_summaries", "locks_select", "locks_scan",
+            "locks_topk", "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
+            "locks_step_graph_launch", "locks_step_graph_destroy", "locks_status_string",
+            "locks_last_hip_error", "locks_version")
+
+
+class LocksError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.locks_status_string(status).decode() if _lib else str(status)
+        extra = f" (hipError {_lib.locks_last_hip_error()})" if _lib and status == LOCKS_ERR_HIP \
+            else ""
+        super().__init__(f"{where}: {msg}{extra}")
+        self.status = status
+
+
+class CKVCache(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+class CSummaries(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("mu", ctypes.c_void_p), ("basis", ctypes.c_void_p),
+                ("coef", ctypes.c_void_p)]
+
+
+class CPageTable(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+class CStepArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("num_q_heads", ctypes.c_int32),
+                ("budget_tokens", ctypes.c_int32), ("summaries", CSummaries),
+                ("cache", CKVCache), ("pages", CPageTable), ("sel_pages", ctypes.c_void_p),
+                ("sel_logmass", ctypes.c_void_p), ("page_logmass", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("out_lse", ctypes.c_void_p), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblocks.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run python -m kv_cache_page_rank_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, vp, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        P = ctypes.POINTER
+        L.locks_workspace_bytes.argtypes = [i32] * 9
+        L.locks_workspace_bytes.restype = sz
+        L.locks_build_summaries.argtypes = [P(CKVCache), P(CPageTable), vp, P(CSummaries), vp, sz,
+                                            vp]
+        L.locks_select.argtypes = [vp, i32, P(CSummaries), P(CPageTable), i32, vp, vp, vp, vp, sz,
+                                   vp]
+        L.locks_scan.argtypes = [vp, i32, P(CSummaries), P(CPageTable), vp, vp, vp]
+        L.locks_topk.argtypes = [vp, P(CPageTable), i32, i32, i32, i32, vp, vp, vp]
+        L.locks_sparse_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, i32, vp, vp,
+                                          vp, sz, vp]
+        L.locks_dense_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, vp, vp, sz, vp]
+        L.locks_step_graph_create.argtypes = [P(CStepArgs), P(vp)]
+        L.locks_step_graph_launch.argtypes = [vp, vp]
+        L.locks_step_graph_destroy.argtypes = [vp]
+        L.locks_step_graph_destroy.restype = None
+        L.locks_status_string.argtypes = [i32]
+        L.locks_status_string.restype = ctypes.c_char_p
+        L.locks_last_hip_error.restype = i32
+        L.locks_version.restype = i32
+        for fn in ("locks_build_summaries", "locks_select", "locks_scan", "locks_topk",
+                   "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
+                   "locks_step_graph_launch"):
+            getattr(L, fn).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != LOCKS_OK:
+        raise LocksError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------- containers
+
+@dataclass
+class PagedKV:
+    """K pool [NB][H_kv][P][d] and V pool [NB][H_kv][d][P] (bf16 or float32)."""
+    k: torch.Tensor
+    v: torch.Tensor | None
+
+    def c(self) -> CKVCache:
+        NB, H, P, d = self.k.shape
+        dt = {torch.bfloat16: LOCKS_BF16, torch.float32: LOCKS_F32}[self.k.dtype]
+        if self.v is not None:
+            assert self.v.shape == (NB, H, d, P) and self.v.dtype == self.k.dtype
+            assert self.v.is_contiguous()
+        assert self.k.is_contiguous()
+        return CKVCache(dt, NB, H, P, d, self.k.data_ptr(),
+                        self.v.data_ptr() if self.v is not None else None)
+
+
+@dataclass
+class PageTable:
+    block_table: torch.Tensor  # [B][max_pages] int32
+    seq_lens: torch.Tensor     # [B] int32
+
+    def c(self) -> CPageTable:
+        assert self.block_table.dtype == torch.int32 and self.seq_lens.dtype == torch.int32
+        assert self.block_table.is_contiguous() and self.seq_lens.is_contiguous()
+        B, MP = self.block_table.shape
+        return CPageTable(B, MP, self.block_table.data_ptr(), self.seq_lens.data_ptr())
+
+
+@dataclass
+class Summaries:
+    mu: torch.Tensor     # [NB][H_kv][d]
+    basis: torch.Tensor  # [NB][H_kv][r][d]
+    coef: torch.Tensor   # [NB][H_kv][P][r]
+
+    @staticmethod
+    def empty(num_blocks, num_kv_heads, page_size, head_dim, rank, device="cuda"):
+        f = dict(dtype=torch.float32, device=device)
+        return Summaries(torch.empty(num_blocks, num_kv_heads, head_dim, **f),
+                         torch.empty(num_blocks, num_kv_heads, rank, head_dim, **f),
+                         torch.empty(num_blocks, num_kv_heads, page_size, rank, **f))
+
+    def c(self) -> CSummaries:
+        NB, H, r, d = self.basis.shape
+        P = self.coef.shape[2]
+        for t in (self.mu, self.basis, self.coef):
+            assert t.dtype == torch.float32 and t.is_contiguous()
+        return CSummaries(NB, H, P, d, r, self.mu.data_ptr(), self.basis.data_ptr(),
+                          self.coef.data_ptr())
+
+
+def workspace_bytes(op, batch, max_pages, num_q_heads, num_kv_heads, page_size, head_dim, rank,
+                    k_pages) -> int:
+    return lib().locks_workspace_bytes(op, batch, max_pages, num_q_heads, num_kv_heads, page_size,
+                                       head_dim, rank, k_pages)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- entry points
+
+def locks_build_summaries(cache: PagedKV, pages: PageTable, out: Summaries, page_begin=None,
+                          stream=None):
+    cc, pc, sc = cache.c(), pages.c(), out.c()
+    _check(lib().locks_build_summaries(ctypes.byref(cc), ctypes.byref(pc), _ptr(page_begin),
+                                       ctypes.byref(sc), None, 0, _stream(stream)),
+           "locks_build_summaries")
+
+
+def locks_scan(q, summaries: Summaries, pages: PageTable, page_logmass, head_logmass=None,
+               stream=None):
+    sc, pc = summaries.c(), pages.c()
+    _check(lib().locks_scan(_ptr(q), q.shape[1], ctypes.byref(sc), ctypes.byref(pc),
+                            _ptr(page_logmass), _ptr(head_logmass), _stream(stream)), "locks_scan")
+
+
+def locks_topk(page_logmass, pages: PageTable, page_size, budget_tokens, sel_pages,
+               sel_logmass=None, stream=None):
+    pc = pages.c()
+    _check(lib().locks_topk(_ptr(page_logmass), ctypes.byref(pc), page_logmass.shape[1],
+                            page_size, budget_tokens, sel_pages.shape[-1], _ptr(sel_pages),
+                            _ptr(sel_logmass), _stream(stream)), "locks_topk")
+
+
+def locks_select(q, summaries: Summaries, pages: PageTable, budget_tokens, sel_pages, sel_logmass,
+                 page_logmass=None, ws=None, stream=None):
+    sc, pc = summaries.c(), pages.c()
+    _check(lib().locks_select(_ptr(q), q.shape[1], ctypes.byref(sc), ctypes.byref(pc),
+                              budget_tokens, _ptr(sel_pages), _ptr(sel_logmass),
+                              _ptr(page_logmass), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(stream)), "locks_select")
+
+
+def locks_sparse_attend(q, cache: PagedKV, pages: PageTable, sel_pages, out, out_lse=None, ws=None,
+                        stream=None):
+    cc, pc = cache.c(), pages.c()
+    k = sel_pages.shape[-1]
+    _check(lib().locks_sparse_attend(_ptr(q), q.shape[1], ctypes.byref(cc), ctypes.byref(pc),
+                                     _ptr(sel_pages), k, _ptr(out), _ptr(out_lse), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream)),
+           "locks_sparse_attend")
+
+
+def locks_dense_attend(q, cache: PagedKV, pages: PageTable, out, out_lse=None, ws=None,
+                       stream=None):
+    cc, pc = cache.c(), pages.c()
+    _check(lib().locks_dense_attend(_ptr(q), q.shape[1], ctypes.byref(cc), ctypes.byref(pc),
+                                    _ptr(out), _ptr(out_lse), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream)),
+           "locks_dense_attend")
+
+
+class StepGraph:
+    """One decode step (select + sparse attend) captured as a HIP graph."""
+
+    def __init__(self, q, summaries: Summaries, cache: PagedKV, pages: PageTable, budget_tokens,
+                 sel_pages, sel_logmass, out, out_lse=None, page_logmass=None, ws=None):
+        self._keep = (q, summaries, cache, pages, sel_pages, sel_logmass, out, out_lse,
+                      page_logmass, ws)
+        a = CStepArgs(q.data_ptr(), q.shape[1], budget_tokens, summaries.c(), cache.c(),
+                      pages.c(), sel_pages.data_ptr(), sel_logmass.data_ptr(),
+                      None if page_logmass is None else page_logmass.data_ptr(), out.data_ptr(),
+                      None if out_lse is None else out_lse.data_ptr(),
+                      None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel())
+        h = ctypes.c_void_p()
+        _check(lib().locks_step_graph_create(ctypes.byref(a), ctypes.byref(h)),
+               "locks_step_graph_create")
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(lib().locks_step_graph_launch(self._h, _stream(stream)), "locks_step_graph_launch")
+
+    def close(self):
+        if self._h:
+            lib().locks_step_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

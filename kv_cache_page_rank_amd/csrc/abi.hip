@@ -1,0 +1,375 @@
+// C ABI of the library (declared in include/locks.h): host-side validation,
+// workspace sizing, dispatch to the kernel launchers and graph capture.
+// Nothing here allocates device memory; nothing here reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <new>
+
+#include "../../include/locks.h"
+#include "launchers.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+locks_status hip_fail(hipError_t e) {
+    g_last_hip_error = (int32_t)e;
+    return LOCKS_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool head_dims_ok(int32_t hq, int32_t hkv) {
+    return hq > 0 && hkv > 0 && hq % hkv == 0 && hq / hkv <= 16;
+}
+
+locks_status check_page_table(const locks_page_table* pt) {
+    if (!pt || !pt->block_table || !pt->seq_lens || pt->batch <= 0 || pt->max_pages <= 0)
+        return LOCKS_ERR_INVALID_ARG;
+    if (pt->max_pages > locks::kTopkMaxPages) return LOCKS_ERR_UNSUPPORTED;
+    return LOCKS_OK;
+}
+
+locks_status check_summaries(const locks_summaries* s, bool need_data) {
+    if (!s || s->num_blocks <= 0 || s->num_kv_heads <= 0 || s->page_size <= 0 ||
+        s->head_dim <= 0 || s->rank <= 0)
+        return LOCKS_ERR_INVALID_ARG;
+    if (need_data && (!s->mu || !s->basis || !s->coef)) return LOCKS_ERR_INVALID_ARG;
+    if (!locks::scan_supported(s->page_size, s->head_dim, s->rank)) return LOCKS_ERR_UNSUPPORTED;
+    return LOCKS_OK;
+}
+
+locks_status check_cache(const locks_kv_cache* kv, bool need_v) {
+    if (!kv || !kv->k || (need_v && !kv->v) || kv->num_blocks <= 0 || kv->num_kv_heads <= 0 ||
+        kv->page_size <= 0 || kv->head_dim <= 0)
+        return LOCKS_ERR_INVALID_ARG;
+    if (kv->dtype != LOCKS_F32 && kv->dtype != LOCKS_BF16) return LOCKS_ERR_INVALID_ARG;
+    return LOCKS_OK;
+}
+
+size_t select_ws(int32_t batch, int32_t max_pages, int32_t hkv) {
+    return align_up((size_t)batch * hkv * max_pages * sizeof(float));
+}
+
+size_t attend_ws(int32_t batch, int32_t hq, int32_t d, int32_t splits) {
+    const size_t rows = (size_t)batch * hq * splits;
+    return align_up(rows * 2 * sizeof(float)) + align_up(rows * d * sizeof(float));
+}
+
+int32_t dense_splits(int32_t batch, int32_t hkv, int32_t max_pages) {
+    const int pps = locks::dense_pages_per_split(batch, hkv, max_pages);
+    return (max_pages + pps - 1) / pps;
+}
+
+// Shared body of the attention entry points.
+locks_status attend_common(const float* q, int32_t hq, const locks_kv_cache* kv,
+                           const locks_page_table* pt, const int32_t* sel, int32_t k_pages,
+                           void* out, float* out_lse, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+    locks_status st = check_cache(kv, true);
+    if (st != LOCKS_OK) return st;
+    if ((st = check_page_table(pt)) != LOCKS_OK) return st;
+    if (!q || !out || !head_dims_ok(hq, kv->num_kv_heads)) return LOCKS_ERR_INVALID_ARG;
+    const bool sparse = sel != nullptr;
+    if (sparse && k_pages < 0) return LOCKS_ERR_INVALID_ARG;
+    if (!locks::attend_supported(kv->dtype == LOCKS_BF16, kv->page_size, kv->head_dim))
+        return LOCKS_ERR_UNSUPPORTED;
+    const int32_t splits = sparse ? k_pages + 1 : dense_splits(pt->batch, kv->num_kv_heads, pt->max_pages);
+    const size_t need = attend_ws(pt->batch, hq, kv->head_dim, splits);
+    if (!ws || ws_bytes < need) return LOCKS_ERR_WORKSPACE;
+    locks::AttnParams p{};
+    p.q = q;
+    p.k = kv->k;
+    p.v = kv->v;
+    p.bf16 = kv->dtype == LOCKS_BF16;
+    p.block_table = pt->block_table;
+    p.seq_lens = pt->seq_lens;
+    p.sel_pages = sel;
+    p.batch = pt->batch;
+    p.num_q_heads = hq;
+    p.num_kv_heads = kv->num_kv_heads;
+    p.max_pages = pt->max_pages;
+    p.num_blocks = kv->num_blocks;
+    p.page_size = kv->page_size;
+    p.head_dim = kv->head_dim;
+    p.k_sel = sparse ? k_pages : 0;
+    p.pages_per_split = sparse ? 1 : locks::dense_pages_per_split(pt->batch, kv->num_kv_heads, pt->max_pages);
+    p.num_splits = splits;
+    const size_t rows = (size_t)pt->batch * hq * splits;
+    p.part_ml = static_cast<float*>(ws);
+    p.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(rows * 2 * sizeof(float)));
+    p.out = out;
+    p.out_lse = out_lse;
+    const hipError_t e = locks::launch_attend(p, stream);
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
+locks_status scan_common(const float* q, int32_t hq, const locks_summaries* s,
+                         const locks_page_table* pt, float* page_logmass, float* head_logmass,
+                         hipStream_t stream) {
+    locks::ScanParams p{};
+    p.q = q;
+    p.mu = s->mu;
+    p.basis = s->basis;
+    p.coef = s->coef;
+    p.block_table = pt->block_table;
+    p.seq_lens = pt->seq_lens;
+    p.batch = pt->batch;
+    p.num_q_heads = hq;
+    p.num_kv_heads = s->num_kv_heads;
+    p.max_pages = pt->max_pages;
+    p.num_blocks = s->num_blocks;
+    p.page_size = s->page_size;
+    p.head_dim = s->head_dim;
+    p.rank = s->rank;
+    p.page_logmass = page_logmass;
+    p.head_logmass = head_logmass;
+    const hipError_t e = locks::launch_scan(p, stream);
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
+locks_status topk_common(const float* page_logmass, const locks_page_table* pt, int32_t hkv,
+                         int32_t page_size, int32_t budget, int32_t width, int32_t* sel,
+                         float* sel_mass, hipStream_t stream) {
+    locks::TopkParams p{};
+    p.page_logmass = page_logmass;
+    p.seq_lens = pt->seq_lens;
+    p.batch = pt->batch;
+    p.num_kv_heads = hkv;
+    p.max_pages = pt->max_pages;
+    p.page_size = page_size;
+    const int32_t k = budget / page_size;
+    p.k_req = k < width ? k : width;
+    p.width = width;
+    p.sel_pages = sel;
+    p.sel_logmass = sel_mass;
+    const hipError_t e = locks::launch_topk(p, stream);
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
+}  // namespace
+
+struct locks_step_graph {
+    hipGraphExec_t exec;
+};
+
+extern "C" {
+
+size_t locks_workspace_bytes(int32_t op, int32_t batch, int32_t max_pages, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t page_size, int32_t head_dim,
+                             int32_t rank, int32_t k_pages) {
+    (void)page_size;
+    (void)rank;
+    if (batch <= 0 || max_pages <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return 0;
+    switch (op) {
+        case LOCKS_OP_BUILD:
+            return 0;
+        case LOCKS_OP_SELECT:
+            return select_ws(batch, max_pages, num_kv_heads);
+        case LOCKS_OP_SPARSE_ATTEND:
+            return attend_ws(batch, num_q_heads, head_dim, (k_pages < 0 ? 0 : k_pages) + 1);
+        case LOCKS_OP_DENSE_ATTEND:
+            return attend_ws(batch, num_q_heads, head_dim, dense_splits(batch, num_kv_heads, max_pages));
+        case LOCKS_OP_STEP:
+            return select_ws(batch, max_pages, num_kv_heads) +
+                   attend_ws(batch, num_q_heads, head_dim, (k_pages < 0 ? 0 : k_pages) + 1);
+        default:
+            return 0;
+    }
+}
+
+locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
+                                   const int32_t* page_begin, const locks_summaries* out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    locks_status st = check_cache(cache, false);
+    if (st != LOCKS_OK) return st;
+    if ((st = check_page_table(pages)) != LOCKS_OK) return st;
+    if ((st = check_summaries(out, true)) != LOCKS_OK) return st;
+    if (out->num_blocks != cache->num_blocks || out->num_kv_heads != cache->num_kv_heads ||
+        out->page_size != cache->page_size || out->head_dim != cache->head_dim)
+        return LOCKS_ERR_INVALID_ARG;
+    if (!locks::build_supported(cache->page_size, cache->head_dim, out->rank))
+        return LOCKS_ERR_UNSUPPORTED;
+    locks::BuildParams p{};
+    p.k = cache->k;
+    p.bf16 = cache->dtype == LOCKS_BF16;
+    p.block_table = pages->block_table;
+    p.seq_lens = pages->seq_lens;
+    p.page_begin = page_begin;
+    p.batch = pages->batch;
+    p.num_kv_heads = cache->num_kv_heads;
+    p.max_pages = pages->max_pages;
+    p.num_blocks = cache->num_blocks;
+    p.page_size = cache->page_size;
+    p.head_dim = cache->head_dim;
+    p.rank = out->rank;
+    p.mu = out->mu;
+    p.basis = out->basis;
+    p.coef = out->coef;
+    const hipError_t e = locks::launch_build(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
+locks_status locks_scan(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
+                        const locks_page_table* pages, float* page_logmass, float* head_logmass,
+                        void* stream) {
+    locks_status st = check_summaries(summaries, true);
+    if (st != LOCKS_OK) return st;
+    if ((st = check_page_table(pages)) != LOCKS_OK) return st;
+    if (!q || !page_logmass || !head_dims_ok(num_q_heads, summaries->num_kv_heads))
+        return LOCKS_ERR_INVALID_ARG;
+    return scan_common(q, num_q_heads, summaries, pages, page_logmass, head_logmass,
+                       static_cast<hipStream_t>(stream));
+}
+
+locks_status locks_topk(const float* page_logmass, const locks_page_table* pages,
+                        int32_t num_kv_heads, int32_t page_size, int32_t budget_tokens,
+                        int32_t width, int32_t* sel_pages, float* sel_logmass, void* stream) {
+    locks_status st = check_page_table(pages);
+    if (st != LOCKS_OK) return st;
+    if (!page_logmass || !sel_pages || num_kv_heads <= 0 || page_size <= 0 || budget_tokens < 0 ||
+        width < 0)
+        return LOCKS_ERR_INVALID_ARG;
+    if (width == 0) return LOCKS_OK;
+    return topk_common(page_logmass, pages, num_kv_heads, page_size, budget_tokens, width,
+                       sel_pages, sel_logmass, static_cast<hipStream_t>(stream));
+}
+
+locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
+                          const locks_page_table* pages, int32_t budget_tokens,
+                          int32_t* sel_pages, float* sel_logmass, float* page_logmass, void* ws,
+                          size_t ws_bytes, void* stream) {
+    locks_status st = check_summaries(summaries, true);
+    if (st != LOCKS_OK) return st;
+    if ((st = check_page_table(pages)) != LOCKS_OK) return st;
+    if (!q || budget_tokens < 0 || !head_dims_ok(num_q_heads, summaries->num_kv_heads))
+        return LOCKS_ERR_INVALID_ARG;
+    const int32_t width = budget_tokens / summaries->page_size;
+    if (width > 0 && !sel_pages) return LOCKS_ERR_INVALID_ARG;
+    float* masses = page_logmass;
+    if (!masses) {
+        if (!ws || ws_bytes < select_ws(pages->batch, pages->max_pages, summaries->num_kv_heads))
+            return LOCKS_ERR_WORKSPACE;
+        masses = static_cast<float*>(ws);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = scan_common(q, num_q_heads, summaries, pages, masses, nullptr, s)) != LOCKS_OK)
+        return st;
+    if (width == 0) return LOCKS_OK;
+    return topk_common(masses, pages, summaries->num_kv_heads, summaries->page_size, budget_tokens,
+                       width, sel_pages, sel_logmass, s);
+}
+
+locks_status locks_sparse_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,
+                                 const locks_page_table* pages, const int32_t* sel_pages,
+                                 int32_t k_pages, void* out, float* out_lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    if (k_pages > 0 && !sel_pages) return LOCKS_ERR_INVALID_ARG;
+    // With k_pages == 0 the sparse path still attends the partial last page; a
+    // non-null marker selects that path and is never dereferenced.
+    static const int32_t kNoPages = -1;
+    const int32_t* sel = sel_pages ? sel_pages : &kNoPages;
+    return attend_common(q, num_q_heads, cache, pages, sel, k_pages, out, out_lse, ws, ws_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+locks_status locks_dense_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,
+                                const locks_page_table* pages, void* out, float* out_lse,
+                                void* ws, size_t ws_bytes, void* stream) {
+    return attend_common(q, num_q_heads, cache, pages, nullptr, 0, out, out_lse, ws, ws_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+locks_status locks_step_graph_create(const locks_step_args* a, locks_step_graph** graph) {
+    if (!a || !graph) return LOCKS_ERR_INVALID_ARG;
+    *graph = nullptr;
+    const int32_t k = a->summaries.page_size > 0 ? a->budget_tokens / a->summaries.page_size : 0;
+    const size_t sel_bytes = a->page_logmass
+                                 ? 0
+                                 : select_ws(a->pages.batch, a->pages.max_pages,
+                                             a->summaries.num_kv_heads);
+    const size_t need = locks_workspace_bytes(LOCKS_OP_STEP, a->pages.batch, a->pages.max_pages,
+                                              a->num_q_heads, a->summaries.num_kv_heads,
+                                              a->summaries.page_size, a->summaries.head_dim,
+                                              a->summaries.rank, k);
+    if (!a->ws || a->ws_bytes < need) return LOCKS_ERR_WORKSPACE;
+    if (a->cache.page_size != a->summaries.page_size || a->cache.head_dim != a->summaries.head_dim ||
+        a->cache.num_kv_heads != a->summaries.num_kv_heads)
+        return LOCKS_ERR_INVALID_ARG;
+
+    hipStream_t s;
+    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(s);
+        return hip_fail(e);
+    }
+    locks_status st = locks_select(a->q, a->num_q_heads, &a->summaries, &a->pages, a->budget_tokens,
+                                   a->sel_pages, a->sel_logmass, a->page_logmass, a->ws, a->ws_bytes,
+                                   s);
+    if (st == LOCKS_OK) {
+        void* attn_ws = static_cast<char*>(a->ws) + sel_bytes;
+        st = locks_sparse_attend(a->q, a->num_q_heads, &a->cache, &a->pages, a->sel_pages, k, a->out,
+                                 a->out_lse, attn_ws, a->ws_bytes - sel_bytes, s);
+    }
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(s, &g);
+    (void)hipStreamDestroy(s);
+    if (st != LOCKS_OK) {
+        if (g) (void)hipGraphDestroy(g);
+        return st;
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    hipGraphExec_t exec;
+    e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) return hip_fail(e);
+    locks_step_graph* h = new (std::nothrow) locks_step_graph{exec};
+    if (!h) {
+        (void)hipGraphExecDestroy(exec);
+        return LOCKS_ERR_INVALID_ARG;
+    }
+    *graph = h;
+    return LOCKS_OK;
+}
+
+locks_status locks_step_graph_launch(locks_step_graph* graph, void* stream) {
+    if (!graph) return LOCKS_ERR_INVALID_ARG;
+    const hipError_t e = hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
+void locks_step_graph_destroy(locks_step_graph* graph) {
+    if (!graph) return;
+    (void)hipGraphExecDestroy(graph->exec);
+    delete graph;
+}
+
+const char* locks_status_string(int32_t status) {
+    switch (status) {
+        case LOCKS_OK:
+            return "ok";
+        case LOCKS_ERR_INVALID_ARG:
+            return "invalid argument";
+        case LOCKS_ERR_UNSUPPORTED:
+            return "unsupported shape or dtype";
+        case LOCKS_ERR_WORKSPACE:
+            return "workspace missing or too small";
+        case LOCKS_ERR_HIP:
+            return "HIP error";
+        default:
+            return "unknown status";
+    }
+}
+
+int32_t locks_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t locks_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,637 @@
+// Split-K paged flash-decode over a page list, and the log-sum-exp merge.
+//
+// Sparse: for each (b, g) one split per selected page plus one split for the
+// sequence's partial last page (abstract: only the top pages are attended;
+// the partial page has no summary yet and is always attended).  Dense: each
+// split is a run of consecutive pages (the dense-attention baseline).
+// A split emits, per query head, the running max m and sum l (log2 units)
+// and the unnormalised output o; the merge combines the splits of a head in
+// split order: M = max m_s, L = sum l_s 2^(m_s - M), out = sum o_s 2^(m_s - M) / L,
+// lse = (M + log2 L) ln 2.
+//
+// bf16 caches (P = 64): MFMA for both products with the group's (up to 16)
+// heads as the 16-wide MFMA dimension; q and p are split into two bf16
+// parts so the products carry ~16 significant bits.  V pages are stored
+// transposed ([d][P]) so that each lane's contraction elements (tokens) are
+// contiguous.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace locks {
+
+namespace {
+
+struct SplitPages {
+    int first, count;  // consecutive logical pages [first, first + count) (count 0 or 1 for sparse)
+};
+
+__device__ __forceinline__ SplitPages split_pages(const AttnParams& a, bool sparse, int b, int g,
+                                                  int s, int full, int n_all) {
+    SplitPages r{0, 0};
+    if (sparse) {
+        if (s < a.k_sel) {
+            const int j = a.sel_pages[((size_t)b * a.num_kv_heads + g) * a.k_sel + s];
+            if (j >= 0 && j < full) r = {j, 1};
+        } else if (n_all > full) {
+            r = {full, 1};  // partial last page
+        }
+    } else {
+        const int lo = s * a.pages_per_split;
+        const int hi = lo + a.pages_per_split < n_all ? lo + a.pages_per_split : n_all;
+        if (lo < hi) r = {lo, hi - lo};
+    }
+    return r;
+}
+
+// Combine the (m, l, o) partials of the 4 waves of a workgroup (4
+// consecutive splits of one (b, g)) into one partial, in wave order.
+// sm_o[w][h][d]; thread t combines head t/16, dims [8*(t%16), +8).
+template <int D>
+__device__ __forceinline__ void combine_waves(const AttnParams& a, float (*sm_m)[16],
+                                              float (*sm_l)[16], float (*sm_o)[16][D + 4], int b,
+                                              int g, int G, int part, int nparts) {
+    const int t = threadIdx.x;
+    const int h = t >> 4;
+    constexpr int DPT = D / 16;  // dims per thread
+    const int d0 = (t & 15) * DPT;
+    if (h >= G) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        if (sm_l[w][h] > 0.f) M = fmaxf(M, sm_m[w][h]);
+    float L = 0.f, o[DPT];
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) o[e] = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float l = sm_l[w][h];
+            const float wt = l > 0.f ? fast_exp2(sm_m[w][h] - M) : 0.f;
+            L += l * wt;
+#pragma unroll
+            for (int e = 0; e < DPT; ++e) o[e] += sm_o[w][h][d0 + e] * wt;
+        }
+    }
+    const size_t row = ((size_t)b * a.num_q_heads + g * G + h) * nparts + part;
+    if ((t & 15) == 0) {
+        a.part_ml[2 * row] = M;
+        a.part_ml[2 * row + 1] = L;
+    }
+    float* dst = a.part_o + row * D + d0;
+#pragma unroll
+    for (int e = 0; e < DPT; e += 4)
+        *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+}
+
+// One wave per split (sparse: one selected page or the partial page; dense:
+// a run of pages); the 4 waves of a workgroup take 4 consecutive splits of
+// one (b, g) and are combined in LDS into one partial.  Per page and wave,
+// with the group's heads as the 16-wide MFMA dimension:
+//   S^T (64 tok x 16 h) = K (64 x d) . q^T   v_mfma_f32_16x16x32_bf16 (q as hi + lo)
+//   O^T (d x 16 h)     += V^T (d x 64) . p^T v_mfma_f32_16x16x32_bf16 (p as hi + lo)
+// All of a page's K and V fragments (32 KB per wave) are requested before
+// any is used.  The token order inside the score tiles is chosen so that
+// each lane's scores are exactly its 8 contraction elements of the value
+// product: score tile mt, A row m  <->  token 32*(mt/2) + 8*(m/4) + 4*(mt%2) + m%4,
+// and the value operand is 8 consecutive tokens of one V^T row (16 bytes).
+template <int P, int D, bool kSparse>
+__global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
+    static_assert(P == 64 && D % 32 == 0, "bf16 path: 64-token pages");
+    constexpr int KS = D / 32;   // K-steps of the score product
+    constexpr int MT = P / 16;   // score tiles (16 tokens each)
+    constexpr int KS2 = P / 32;  // K-steps of the value product
+    constexpr int MD = D / 16;   // output tiles (16 dims each)
+    __shared__ float sm_m[4][16], sm_l[4][16];
+    __shared__ float sm_o[4][16][D + 4];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int w = lane >> 4;
+    const int c = lane & 15;
+    const int S = a.num_splits;
+    const int NPART = a.num_parts;
+    const int item = blockIdx.x;
+    const int part = item % NPART;
+    const int g = (item / NPART) % a.num_kv_heads;
+    const int b = item / (NPART * a.num_kv_heads);
+    const int s = part * 4 + wv;  // this wave's split (may be past the last)
+    const int Hkv = a.num_kv_heads;
+    const int G = a.num_q_heads / Hkv;
+    const bool head_ok = c < G;
+    const int hq = g * G + (head_ok ? c : 0);
+
+    const int seq = a.seq_lens[b] < 0 ? 0 : a.seq_lens[b];
+    int full = seq / P, n_all = (seq + P - 1) / P;
+    full = full > a.max_pages ? a.max_pages : full;
+    n_all = n_all > a.max_pages ? a.max_pages : n_all;
+    SplitPages sp{0, 0};
+    if (s < S) sp = split_pages(a, kSparse, b, g, s, full, n_all);
+
+    // q fragment (log2 units), split into bf16 hi + lo: q[hq][32ks + 8w + e]
+    bf16x8 qhi[KS], qlo[KS];
+    {
+        const float qscale = kLog2e / sqrtf((float)D);
+        const float* qp = a.q + ((size_t)b * a.num_q_heads + hq) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
+            u32x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v0 = head_ok ? (e < 2 ? x0[2 * e] : x1[2 * e - 4]) * qscale : 0.f;
+                const float v1 = head_ok ? (e < 2 ? x0[2 * e + 1] : x1[2 * e - 3]) * qscale : 0.f;
+                uint16_t h0, l0, h1, l1;
+                split_bf16(v0, h0, l0);
+                split_bf16(v1, h1, l1);
+                hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lo[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            qhi[ks] = as_bf16x8(hi);
+            qlo[ks] = as_bf16x8(lo);
+        }
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
+    const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
+    const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+
+    for (int pi = 0; pi < sp.count; ++pi) {
+        const int j = sp.first + pi;
+        const int phys = bt[j];
+        if (phys < 0 || phys >= a.num_blocks) continue;
+        const int nv = seq - j * P < P ? seq - j * P : P;  // valid tokens of this page
+        const uint16_t* kp = kpool + ((size_t)phys * Hkv + g) * P * D;
+        const uint16_t* vp = vpool + ((size_t)phys * Hkv + g) * D * P;
+
+        u32x4 kraw[MT][KS], vraw[KS2][MD];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int tok = 32 * (mt >> 1) + 8 * (c >> 2) + 4 * (mt & 1) + (c & 3);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kraw[mt][ks] =
+                    *reinterpret_cast<const u32x4*>(kp + (size_t)tok * D + 32 * ks + 8 * w);
+        }
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS2; ++ks2)
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+                vraw[ks2][md] = *reinterpret_cast<const u32x4*>(vp + (size_t)(16 * md + c) * P +
+                                                                32 * ks2 + 8 * w);
+
+        f32x4 sc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 kf = as_bf16x8(kraw[mt][ks]);
+                sc[mt] = mfma_16x16x32_bf16(kf, qhi[ks], sc[mt]);
+                sc[mt] = mfma_16x16x32_bf16(kf, qlo[ks], sc[mt]);
+            }
+        }
+        // lane (w, c) element v of tile mt: token 32(mt/2) + 8w + 4(mt%2) + v, head c
+        if (nv < P) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int tok = 32 * (mt >> 1) + 8 * w + 4 * (mt & 1) + v;
+                    sc[mt][v] = tok < nv ? sc[mt][v] : -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sc[mt][v]);
+        mx = max_over_rows(mx);
+        const float m_new = fmaxf(m_run, mx);
+        if (m_new == -INFINITY) continue;
+        const float alpha = fast_exp2(m_run - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                sc[mt][v] = fast_exp2(sc[mt][v] - m_new);
+                psum += sc[mt][v];
+            }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) acc[md] *= alpha;
+
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS2; ++ks2) {
+            // p operand: slot e2 = 4e + v <-> token 32ks2 + 8w + e2 <-> tile 2ks2 + e, element v
+            u32x4 phi, plo;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float p0 = sc[2 * ks2 + (e2 >> 1)][(2 * e2) & 3];
+                const float p1 = sc[2 * ks2 + (e2 >> 1)][(2 * e2 + 1) & 3];
+                uint16_t h0, l0, h1, l1;
+                split_bf16(p0, h0, l0);
+                split_bf16(p1, h1, l1);
+                phi[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                plo[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            const bf16x8 bhi = as_bf16x8(phi), blo = as_bf16x8(plo);
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+                u32x4 vr = vraw[ks2][md];
+                if (nv < P) {  // zero values of absent tokens (their p is 0, their bits may be NaN)
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        const int tok = 32 * ks2 + 8 * w + 2 * e2;
+                        vr[e2] &= (tok < nv ? 0x0000ffffu : 0u) | (tok + 1 < nv ? 0xffff0000u : 0u);
+                    }
+                }
+                const bf16x8 vf = as_bf16x8(vr);
+                acc[md] = mfma_16x16x32_bf16(vf, bhi, acc[md]);
+                acc[md] = mfma_16x16x32_bf16(vf, blo, acc[md]);
+            }
+        }
+    }
+
+    const float l_tot = sum_over_rows(l_run);
+    if (w == 0) {
+        sm_m[wv][c] = m_run;
+        sm_l[wv][c] = l_tot;
+    }
+    // lane (w, c) element v of tile md: O^T[16md + 4w + v][c]
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm_o[wv][c][16 * md + 4 * w + v] = acc[md][v];
+    __syncthreads();
+    combine_waves<D>(a, sm_m, sm_l, sm_o, b, g, G, part, NPART);
+}
+
+// Sparse path (bf16, latency-bound at small batch): one workgroup per split
+// (one selected page, or the partial last page), wave wv owns tokens
+// [16wv, 16wv + 16), so each page is fetched by 4 waves at once.  Per wave:
+//   S^T (16 tok x 16 h) = K_tile (16 x d) . q^T   v_mfma_f32_16x16x32_bf16, q as hi + lo
+//   O^T (d x 16 h)     += V^T (d x 16 tok) . p^T  v_mfma_f32_16x16x16bf16_1k, p as hi + lo
+// Lane (w, c) receives the scores of tokens 4w..4w+3 of its slice for head c,
+// which are exactly its 4 contraction elements of the value product; its
+// value operand is 4 consecutive tokens of one V^T row (8 bytes).
+template <int P, int D>
+__global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) {
+    static_assert(P == 64 && D % 32 == 0, "bf16 path: 64-token pages");
+    constexpr int KS = D / 32;
+    constexpr int MD = D / 16;
+    __shared__ float sm_m[4][16], sm_l[4][16];
+    __shared__ float sm_o[4][16][D + 4];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int w = lane >> 4;
+    const int c = lane & 15;
+    const int S = a.num_splits;
+    const int item = blockIdx.x;
+    const int s = item % S;
+    const int g = (item / S) % a.num_kv_heads;
+    const int b = item / (S * a.num_kv_heads);
+    const int Hkv = a.num_kv_heads;
+    const int G = a.num_q_heads / Hkv;
+    const bool head_ok = c < G;
+    const int hq = g * G + (head_ok ? c : 0);
+    const int tok0 = 16 * wv;
+
+    const int seq = a.seq_lens[b] < 0 ? 0 : a.seq_lens[b];
+    int full = seq / P, n_all = (seq + P - 1) / P;
+    full = full > a.max_pages ? a.max_pages : full;
+    n_all = n_all > a.max_pages ? a.max_pages : n_all;
+    const SplitPages sp = split_pages(a, true, b, g, s, full, n_all);
+    int phys = sp.count ? a.block_table[(size_t)b * a.max_pages + sp.first] : -1;
+    const bool page_ok = sp.count && phys >= 0 && phys < a.num_blocks;
+    phys = page_ok ? phys : 0;
+
+    // page slice: K rows tok0 + c (4 x 16 B), V^T rows 16md + c at tokens tok0 + 4w (MD x 8 B)
+    u32x4 kraw[KS];
+    u32x2 vraw[MD];
+    {
+        const uint16_t* kp = static_cast<const uint16_t*>(a.k) + ((size_t)phys * Hkv + g) * P * D +
+                             (size_t)(tok0 + c) * D;
+        const uint16_t* vp = static_cast<const uint16_t*>(a.v) + ((size_t)phys * Hkv + g) * D * P +
+                             tok0 + 4 * w;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kraw[ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks + 8 * w);
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+            vraw[md] = *reinterpret_cast<const u32x2*>(vp + (size_t)(16 * md + c) * P);
+    }
+
+    bf16x8 qhi[KS], qlo[KS];
+    {
+        const float qscale = kLog2e / sqrtf((float)D);
+        const float* qp = a.q + ((size_t)b * a.num_q_heads + hq) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
+            u32x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v0 = head_ok ? (e < 2 ? x0[2 * e] : x1[2 * e - 4]) * qscale : 0.f;
+                const float v1 = head_ok ? (e < 2 ? x0[2 * e + 1] : x1[2 * e - 3]) * qscale : 0.f;
+                uint16_t h0, l0, h1, l1;
+                split_bf16(v0, h0, l0);
+                split_bf16(v1, h1, l1);
+                hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lo[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            qhi[ks] = as_bf16x8(hi);
+            qlo[ks] = as_bf16x8(lo);
+        }
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (page_ok) {
+        const int nv = seq - sp.first * P < P ? seq - sp.first * P : P;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kf = as_bf16x8(kraw[ks]);
+            sc = mfma_16x16x32_bf16(kf, qhi[ks], sc);
+            sc = mfma_16x16x32_bf16(kf, qlo[ks], sc);
+        }
+        if (nv < P) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sc[v] = tok0 + 4 * w + v < nv ? sc[v] : -INFINITY;
+        }
+        const float mx = max_over_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        if (mx != -INFINITY) {
+            uint32_t ph[2], pl[2];
+            float psum = 0.f;
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                const float p0 = fast_exp2(sc[2 * e2] - mx);
+                const float p1 = fast_exp2(sc[2 * e2 + 1] - mx);
+                psum += p0 + p1;
+                uint16_t h0, l0, h1, l1;
+                split_bf16(p0, h0, l0);
+                split_bf16(p1, h1, l1);
+                ph[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                pl[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            m_run = mx;
+            l_run = psum;
+            const bf16x4 bhi = as_bf16x4(u32x2{ph[0], ph[1]});
+            const bf16x4 blo = as_bf16x4(u32x2{pl[0], pl[1]});
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+                u32x2 vr = vraw[md];
+                if (nv < P) {  // absent tokens: p is 0, their bits may be NaN
+#pragma unroll
+                    for (int e2 = 0; e2 < 2; ++e2) {
+                        const int tk = tok0 + 4 * w + 2 * e2;
+                        vr[e2] &= (tk < nv ? 0x0000ffffu : 0u) | (tk + 1 < nv ? 0xffff0000u : 0u);
+                    }
+                }
+                const bf16x4 vf = as_bf16x4(vr);
+                acc[md] = mfma_16x16x16_bf16(vf, bhi, acc[md]);
+                acc[md] = mfma_16x16x16_bf16(vf, blo, acc[md]);
+            }
+        }
+    }
+    const float l_tot = sum_over_rows(l_run);
+    if (w == 0) {
+        sm_m[wv][c] = m_run;
+        sm_l[wv][c] = l_tot;
+    }
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm_o[wv][c][16 * md + 4 * w + v] = acc[md][v];
+    __syncthreads();
+    combine_waves<D>(a, sm_m, sm_l, sm_o, b, g, G, s, S);
+}
+
+// fp32 caches: plain VALU loops, one workgroup per split (small shapes).
+template <int P, int D, bool kSparse>
+__global__ __launch_bounds__(256) void attend_f32_kernel(const AttnParams a) {
+    __shared__ float qs[16][D];
+    __shared__ float sc[16][P];
+    __shared__ float os[16][D];
+    __shared__ float mrun[16], lrun[16], alpha[16];
+
+    const int S = a.num_splits;
+    const int item = blockIdx.x;
+    const int s = item % S;
+    const int g = (item / S) % a.num_kv_heads;
+    const int b = item / (S * a.num_kv_heads);
+    const int Hkv = a.num_kv_heads;
+    const int G = a.num_q_heads / Hkv;
+    const int t = threadIdx.x;
+    const int seq = a.seq_lens[b] < 0 ? 0 : a.seq_lens[b];
+    int full = seq / P, n_all = (seq + P - 1) / P;
+    full = full > a.max_pages ? a.max_pages : full;
+    n_all = n_all > a.max_pages ? a.max_pages : n_all;
+    const SplitPages sp = split_pages(a, kSparse, b, g, s, full, n_all);
+
+    const float qscale = kLog2e / sqrtf((float)D);
+    for (int i = t; i < G * D; i += 256) {
+        const int h = i / D, d = i % D;
+        qs[h][d] = a.q[((size_t)b * a.num_q_heads + g * G + h) * D + d] * qscale;
+        os[h][d] = 0.f;
+    }
+    if (t < G) {
+        mrun[t] = -INFINITY;
+        lrun[t] = 0.f;
+    }
+    __syncthreads();
+
+    const float* kpool = static_cast<const float*>(a.k);
+    const float* vpool = static_cast<const float*>(a.v);
+    for (int pi = 0; pi < sp.count; ++pi) {
+        const int j = sp.first + pi;
+        const int phys = a.block_table[(size_t)b * a.max_pages + j];
+        if (phys < 0 || phys >= a.num_blocks) continue;  // uniform
+        const int nv = seq - j * P < P ? seq - j * P : P;
+        const float* kp = kpool + ((size_t)phys * Hkv + g) * P * D;
+        const float* vp = vpool + ((size_t)phys * Hkv + g) * D * P;
+        for (int i = t; i < G * P; i += 256) {
+            const int h = i / P, tok = i % P;
+            float x = -INFINITY;
+            if (tok < nv) {
+                x = 0.f;
+                for (int d = 0; d < D; ++d) x += qs[h][d] * kp[(size_t)tok * D + d];
+            }
+            sc[h][tok] = x;
+        }
+        __syncthreads();
+        if (t < G) {
+            float mx = -INFINITY;
+            for (int tok = 0; tok < nv; ++tok) mx = fmaxf(mx, sc[t][tok]);
+            const float m_new = fmaxf(mrun[t], mx);
+            const float al = m_new == -INFINITY ? 1.f : fast_exp2(mrun[t] - m_new);
+            float sum = 0.f;
+            for (int tok = 0; tok < P; ++tok) {
+                const float p = tok < nv && m_new != -INFINITY ? fast_exp2(sc[t][tok] - m_new) : 0.f;
+                sc[t][tok] = p;
+                sum += p;
+            }
+            lrun[t] = lrun[t] * al + sum;
+            mrun[t] = m_new;
+            alpha[t] = al;
+        }
+        __syncthreads();
+        for (int i = t; i < G * D; i += 256) {
+            const int h = i / D, d = i % D;
+            float o = os[h][d] * alpha[h];
+            for (int tok = 0; tok < nv; ++tok) o += sc[h][tok] * vp[(size_t)d * P + tok];
+            os[h][d] = o;
+        }
+        __syncthreads();
+    }
+    for (int i = t; i < G * D; i += 256) {
+        const int h = i / D, d = i % D;
+        const size_t row = ((size_t)b * a.num_q_heads + g * G + h) * a.num_parts + s;
+        a.part_o[row * D + d] = os[h][d];
+        if (d == 0) {
+            a.part_ml[2 * row] = mrun[h];
+            a.part_ml[2 * row + 1] = lrun[h];
+        }
+    }
+}
+
+// Merge of the partials of one (b, h), in partial order.  Grid: (b, h) x
+// 32-dim chunk; thread t handles dims [32*chunk + 4*(t%8), +4) over the
+// partials p = t/8, t/8 + 32, ...; the 32 part sums are added in order.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const AttnParams a) {
+    __shared__ float red[256];
+    __shared__ f32x4 pacc[32][8];
+    __shared__ float pl[32];
+    const int bh = blockIdx.x;
+    const int chunk = blockIdx.y;
+    const int t = threadIdx.x;
+    const int NP = a.num_parts;
+    const float* ml = a.part_ml + (size_t)bh * NP * 2;
+    const float* po = a.part_o + (size_t)bh * NP * D;
+
+    float mx = -INFINITY;
+    for (int s = t; s < NP; s += 256)
+        if (ml[2 * s + 1] > 0.f) mx = fmaxf(mx, ml[2 * s]);
+    red[t] = mx;
+    __syncthreads();
+    for (int stride = 128; stride > 0; stride >>= 1) {
+        if (t < stride) red[t] = fmaxf(red[t], red[t + stride]);
+        __syncthreads();
+    }
+    const float M = red[0];
+
+    const int d4 = t & 7, part = t >> 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+    if (M != -INFINITY) {
+        for (int s = part; s < NP; s += 32) {
+            const float l = ml[2 * s + 1];
+            const float wt = l > 0.f ? fast_exp2(ml[2 * s] - M) : 0.f;
+            const f32x4 o = *reinterpret_cast<const f32x4*>(po + (size_t)s * D + 32 * chunk + 4 * d4);
+            acc += o * wt;
+            lsum += l * wt;
+        }
+    }
+    pacc[part][d4] = acc;
+    if (d4 == 0) pl[part] = lsum;
+    __syncthreads();
+    if (t < 8) {
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        float L = 0.f;
+#pragma unroll 8
+        for (int pp = 0; pp < 32; ++pp) {
+            o += pacc[pp][t];
+            L += pl[pp];
+        }
+        const size_t base = (size_t)bh * D + 32 * chunk + 4 * t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float res = L > 0.f ? o[e] / L : 0.f;
+            if (a.bf16)
+                static_cast<uint16_t*>(a.out)[base + e] = f32_to_bf16_bits(res);
+            else
+                static_cast<float*>(a.out)[base + e] = res;
+        }
+        if (chunk == 0 && t == 0 && a.out_lse)
+            a.out_lse[bh] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+    }
+}
+
+template <int P, int D>
+hipError_t launch_pd(AttnParams p, hipStream_t s) {
+    const bool sparse = p.sel_pages != nullptr;
+    if (p.bf16) {
+        if constexpr (P == 64) {
+            if (sparse) {  // one workgroup per selected page
+                p.num_parts = p.num_splits;
+                const unsigned blocks = (unsigned)((long)p.batch * p.num_kv_heads * p.num_splits);
+                if (blocks > 0)
+                    hipLaunchKernelGGL((attend_sparse_kernel<P, D>), dim3(blocks), dim3(256), 0, s,
+                                       p);
+            } else {  // one wave per run of pages, 4 runs per workgroup
+                p.num_parts = (p.num_splits + 3) / 4;
+                const unsigned blocks = (unsigned)((long)p.batch * p.num_kv_heads * p.num_parts);
+                if (blocks > 0)
+                    hipLaunchKernelGGL((attend_mfma_kernel<P, D, false>), dim3(blocks), dim3(256),
+                                       0, s, p);
+            }
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else {
+        p.num_parts = p.num_splits;
+        const unsigned blocks = (unsigned)((long)p.batch * p.num_kv_heads * p.num_splits);
+        if (blocks > 0) {
+            if (sparse)
+                hipLaunchKernelGGL((attend_f32_kernel<P, D, true>), dim3(blocks), dim3(256), 0, s,
+                                   p);
+            else
+                hipLaunchKernelGGL((attend_f32_kernel<P, D, false>), dim3(blocks), dim3(256), 0, s,
+                                   p);
+        }
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned rows = (unsigned)(p.batch * p.num_q_heads);
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL((merge_kernel<D>), dim3(rows, D / 32), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool attend_supported(int bf16, int page_size, int head_dim) {
+    if (head_dim != 64 && head_dim != 128) return false;
+    if (bf16) return page_size == 64;
+    return page_size == 16 || page_size == 64;
+}
+
+int dense_pages_per_split(int batch, int num_kv_heads, int max_pages) {
+    // one wave per split; aim for ~2048 waves (8 per CU, the occupancy of the
+    // dense kernel) so that one round covers the cache
+    long pps = (long)batch * num_kv_heads * max_pages / 2048;
+    if (pps < 1) pps = 1;
+    if (pps > 256) pps = 256;
+    return (int)pps;
+}
+
+hipError_t launch_attend(const AttnParams& p, hipStream_t s) {
+    if (p.page_size == 16 && p.head_dim == 64) return launch_pd<16, 64>(p, s);
+    if (p.page_size == 16 && p.head_dim == 128) return launch_pd<16, 128>(p, s);
+    if (p.page_size == 64 && p.head_dim == 64) return launch_pd<64, 64>(p, s);
+    return launch_pd<64, 128>(p, s);
+}
+
+}  // namespace locks

@@ -1,0 +1,74 @@
+// Host-side launchers of the gfx950 kernels (defined next to each kernel).
+// Each returns the hipError_t of its launch.  Shapes are validated by the
+// C-ABI layer before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace locks {
+
+struct ScanParams {
+    const float* q;        // [B][Hq][D]
+    const float* mu;       // [NB][Hkv][D]
+    const float* basis;    // [NB][Hkv][r][D]
+    const float* coef;     // [NB][Hkv][P][r]
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int32_t batch, num_q_heads, num_kv_heads, max_pages, num_blocks;
+    int32_t page_size, head_dim, rank;
+    float* page_logmass;   // [B][Hkv][max_pages]
+    float* head_logmass;   // [B][Hq][max_pages] or null
+};
+hipError_t launch_scan(const ScanParams& p, hipStream_t s);
+bool scan_supported(int page_size, int head_dim, int rank);
+
+struct TopkParams {
+    const float* page_logmass;  // [B][Hkv][max_pages]
+    const int32_t* seq_lens;
+    int32_t batch, num_kv_heads, max_pages, page_size, k_req, width;
+    int32_t* sel_pages;         // [B][Hkv][width]
+    float* sel_logmass;         // [B][Hkv][width] or null
+};
+constexpr int kTopkMaxPages = 32768;
+hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+
+struct AttnParams {
+    const float* q;            // [B][Hq][D]
+    const void* k;             // [NB][Hkv][P][D]
+    const void* v;             // [NB][Hkv][D][P]
+    int32_t bf16;              // cache dtype
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const int32_t* sel_pages;  // [B][Hkv][k_sel] (sparse) or null (dense)
+    int32_t batch, num_q_heads, num_kv_heads, max_pages, num_blocks;
+    int32_t page_size, head_dim;
+    int32_t k_sel;             // sparse: selected slots per (b, g)
+    int32_t pages_per_split;   // dense: pages per split
+    int32_t num_splits;        // sparse: k_sel + 1 (last = partial page); dense: ceil(max_pages / pps)
+    int32_t num_parts;         // partials per (b, h) after the in-workgroup combine (set by the launcher)
+    float* part_ml;            // [B][Hq][num_parts][2] (max, sum) in log2 units, num_parts <= num_splits
+    float* part_o;             // [B][Hq][num_parts][D] unnormalised outputs
+    void* out;                 // [B][Hq][D] cache dtype
+    float* out_lse;            // [B][Hq] or null
+};
+hipError_t launch_attend(const AttnParams& p, hipStream_t s);
+bool attend_supported(int bf16, int page_size, int head_dim);
+int dense_pages_per_split(int batch, int num_kv_heads, int max_pages);
+
+struct BuildParams {
+    const void* k;             // [NB][Hkv][P][D]
+    int32_t bf16;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const int32_t* page_begin; // [B] or null
+    int32_t batch, num_kv_heads, max_pages, num_blocks;
+    int32_t page_size, head_dim, rank;
+    float* mu;
+    float* basis;
+    float* coef;
+};
+hipError_t launch_build(const BuildParams& p, hipStream_t s);
+bool build_supported(int page_size, int head_dim, int rank);
+
+}  // namespace locks

@@ -1,0 +1,320 @@
+// Summary scan: per-page estimated attention mass from the resident summary
+// alone (gist.science technical summary, section 2, Reconstructie en
+// Selectie, displayed estimator), aggregated over each GQA group by
+// log-sum-exp (section 2, Group-Shared Selection, read as the sum of the
+// heads' unnormalised masses).
+//
+// For page j of (b, g) and head h of the group, in log2 units with q
+// pre-scaled by log2(e)/sqrt(d):
+//   T[k][h]   = basis_k . q_h                       (MFMA 16x16x4 fp32)
+//   beta[h]   = mu . q_h                            (MFMA, 16 pages per tile)
+//   L[i][h]   = sum_k coef[i][k] T[k][h]            (MFMA 16x16x4 fp32)
+//   s2[h]     = beta[h] + log2 sum_i 2^L[i][h]      (VALU: max, exp2, sum)
+//   a2        = log2 sum_h 2^s2[h]                  (VALU, 16-lane row)
+// and the outputs are s2 * ln 2 and a2 * ln 2.
+//
+// One wave scans 16 consecutive logical pages of one (b, g).  Its query
+// fragment (16 heads x d, heads >= G zero) stays in registers.  All loads
+// are 16-byte vector loads; each MFMA operand is taken straight from the
+// loaded registers thanks to the free choice of contraction order:
+// MFMA step s of a tile contracts d = 16*(s/4) + 4*(l/16) + s%4, so lane l
+// loads d-chunks [16t + 4*(l/16), +4) of its row (64 contiguous bytes per
+// row per load instruction).
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace locks {
+
+namespace {
+
+// State of one wave's batch, shared by the two specialisations below.
+template <int D>
+struct WaveCtx {
+    int b, g, j0, G, Hkv, r, lane, w, c;
+    bool head_ok;
+    int my_phys;  // block of page j0 + c (-1: absent)
+    float* out_page;
+    float qf[D / 4];
+};
+
+// One wave's batch of BATCH pages.  kMasked: some page of the batch is
+// absent or the rank is padded, so loads are zeroed per row; otherwise no
+// masking code is emitted.  kPipe: the basis product of tile tt+1 is issued
+// before the log-sum-exp of tile tt so the matrix core and the vector unit
+// overlap inside the wave.
+template <int P, int D, int RR, bool kExact, int BATCH, int PF, int NACC, bool kMasked, bool kPipe>
+__device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>& x) {
+    constexpr int PPT = 16 / RR;         // pages per basis tile (16 rows = PPT pages x RR rows)
+    constexpr int NTILE = BATCH / PPT;   // basis tiles per batch
+    constexpr int KS2 = RR / 4;          // K-steps of the coefficient product
+    constexpr int MT = P / 16;           // token tiles per page
+    constexpr int DS = D / 4;            // K-steps of the d contraction
+    constexpr int DT = D / 16;           // 16-byte loads per row slice
+    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
+    const int my_phys = x.my_phys;
+    auto phys_at = [&](int pb) { return __shfl(my_phys, pb, kWave); };
+    auto phys_uniform = [&](int pb) { return __builtin_amdgcn_readlane(my_phys, pb); };
+
+    // Basis-tile row assignment for the loading lane (row m = c):
+    //   page-in-tile p = (m%4) / KS2, k-step ks = (m%4) % KS2, basis row kk = KS2*(m/4) + ks.
+    // After the MFMA, lane (w, c) element v holds T[page v/KS2][KS2*w + v%KS2][head c],
+    // which is exactly its B operand for k-step v%KS2 of page v/KS2.
+    const int a_pin = (c & 3) / KS2;
+    const int a_kk = KS2 * (c >> 2) + ((c & 3) % KS2);
+
+    struct Tile {
+        float v[DS];
+        float cf[PPT][MT][KS2];
+    };
+    // Loads are unconditional (absent rows read a clamped, valid address and
+    // are zeroed afterwards) so that the next tiles' loads stay in flight
+    // while the current tile is computed.
+    auto load_tile = [&](int tt, Tile& T) {
+        const int pj = phys_at(tt * PPT + a_pin);
+        const bool row_ok = !kMasked || (pj >= 0 && a_kk < r);
+        const float* src = a.basis + (((size_t)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
+                                      (kMasked && a_kk >= r ? r - 1 : a_kk)) * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(src + 16 * t + 4 * w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) T.v[4 * t + e] = row_ok ? v[e] : 0.0f;
+        }
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int pp = phys_uniform(tt * PPT + p);
+            const bool ok = !kMasked || pp >= 0;
+            const float* csrc = a.coef + ((size_t)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float* row = csrc + (size_t)(16 * mt + c) * r;
+                if constexpr (kExact) {
+                    if constexpr (KS2 == 1) {
+                        const float v = row[w];
+                        T.cf[p][mt][0] = ok ? v : 0.0f;
+                    } else if constexpr (KS2 == 2) {
+                        const f32x2 v = *reinterpret_cast<const f32x2*>(row + 2 * w);
+                        T.cf[p][mt][0] = ok ? v[0] : 0.0f;
+                        T.cf[p][mt][1] = ok ? v[1] : 0.0f;
+                    } else {
+                        const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * w);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) T.cf[p][mt][e] = ok ? v[e] : 0.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < KS2; ++ks) {
+                        const int kk = KS2 * w + ks;
+                        const float v = row[kk < r ? kk : r - 1];
+                        T.cf[p][mt][ks] = (ok && kk < r) ? v : 0.0f;
+                    }
+                }
+            }
+        }
+    };
+    auto basis_product = [&](const Tile& tl) {
+        f32x4 tacc[NACC];
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+            tacc[s % NACC] = mfma_16x16x4_f32(tl.v[s], x.qf[s], tacc[s % NACC]);
+        f32x4 T = tacc[0];
+#pragma unroll
+        for (int i = 1; i < NACC; ++i) T += tacc[i];
+        return T;
+    };
+
+    // ring of tiles: the loads of tiles tt+1 .. tt+PF are in flight while
+    // tile tt is computed
+    Tile ring[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF && i < NTILE; ++i) load_tile(i, ring[i]);
+
+    // beta tile: A row m = page j0 + m (lane column c supplies row c).
+    f32x4 beta;
+    {
+        const float* src = a.mu + ((size_t)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D;
+        float mv[DS];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(src + 16 * t + 4 * w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mv[4 * t + e] = (!kMasked || my_phys >= 0) ? v[e] : 0.0f;
+        }
+        f32x4 bacc[NACC];
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) bacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) bacc[s % NACC] = mfma_16x16x4_f32(mv[s], x.qf[s], bacc[s % NACC]);
+        beta = bacc[0];
+#pragma unroll
+        for (int i = 1; i < NACC; ++i) beta += bacc[i];
+    }
+    // lane (w, c) now holds beta[page j0 + 4w + v][head c] in element v.
+
+    f32x4 Tcur;
+    if constexpr (kPipe) Tcur = basis_product(ring[0]);
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) {
+        if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
+        const Tile& cur = ring[tt % (PF + 1)];
+        if constexpr (!kPipe) Tcur = basis_product(cur);
+
+        f32x4 L[PPT][MT];
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                L[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS2; ++ks)
+                    L[p][mt] = mfma_16x16x4_f32(cur.cf[p][mt][ks], Tcur[p * KS2 + ks], L[p][mt]);
+            }
+        if constexpr (kPipe) {
+            if (tt + 1 < NTILE) Tcur = basis_product(ring[(tt + 1) % (PF + 1)]);
+        }
+
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int pb = tt * PPT + p;  // page index within the batch
+            const int j = x.j0 + pb;
+            // lane (w, c) holds logits of tokens 16*mt + 4w + v for head c.
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) mx = fmaxf(mx, L[p][mt][v]);
+            mx = max_over_rows(mx);
+            float sum = 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) sum += fast_exp2(L[p][mt][v] - mx);
+            sum = sum_over_rows(sum);
+            // per-head estimate; beta of page pb sits in row pb/4, element pb%4
+            const float s2 = mx + fast_log2(sum) + beta[pb & 3];
+            const float xv = x.head_ok ? s2 : -INFINITY;
+            const float gm = max_in_row(xv);
+            const float gs = sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f);
+            const float a2 = gm + fast_log2(gs);
+            if (w == (pb >> 2) && j < a.max_pages) {
+                const bool ok = !kMasked || phys_uniform(pb) >= 0;
+                if (c == 0) x.out_page[j] = ok ? a2 * kLn2 : -INFINITY;
+                if (a.head_logmass && x.head_ok)
+                    a.head_logmass[((size_t)x.b * a.num_q_heads + g * x.G + c) * a.max_pages + j] =
+                        ok ? s2 * kLn2 : -INFINITY;
+            }
+        }
+    }
+}
+
+// Tuning: BATCH pages per wave (8 or 16), PF tiles prefetched ahead, NACC
+// independent accumulator chains for the d contraction, kPipe software
+// pipelining of the tile loop.
+template <int P, int D, int RR, bool kExact, int BATCH = 16, int PF = 2, int NACC = 2,
+          bool kPipe = false>
+__global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
+    static_assert(P % 16 == 0 && D % 16 == 0, "P and d must be multiples of 16");
+    static_assert(RR == 4 || RR == 8 || RR == 16, "padded rank");
+    static_assert(BATCH == 8 || BATCH == 16, "pages per wave");
+    constexpr int DS = D / 4;
+    constexpr int DT = D / 16;
+
+    WaveCtx<D> x;
+    x.lane = threadIdx.x & 63;
+    x.w = x.lane >> 4;
+    x.c = x.lane & 15;
+    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nbatch = (a.max_pages + BATCH - 1) / BATCH;
+    if (wave >= a.batch * a.num_kv_heads * nbatch) return;
+    const int jb = wave % nbatch;
+    x.g = (wave / nbatch) % a.num_kv_heads;
+    x.b = wave / (nbatch * a.num_kv_heads);
+    x.Hkv = a.num_kv_heads;
+    x.G = a.num_q_heads / x.Hkv;
+    x.r = a.rank;
+    x.head_ok = x.c < x.G;
+    x.j0 = jb * BATCH;
+    const int c = x.c, w = x.w;
+
+    int full = a.seq_lens[x.b] / P;
+    full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
+    x.out_page = a.page_logmass + ((size_t)x.b * x.Hkv + x.g) * a.max_pages;
+    if (x.j0 >= full) {  // whole batch past the full pages
+        if (w == 0 && c < BATCH && x.j0 + c < a.max_pages) {
+            x.out_page[x.j0 + c] = -INFINITY;
+            if (a.head_logmass)
+                for (int hh = 0; hh < x.G; ++hh)
+                    a.head_logmass[((size_t)x.b * a.num_q_heads + x.g * x.G + hh) * a.max_pages +
+                                   x.j0 + c] = -INFINITY;
+        }
+        return;
+    }
+
+    x.my_phys = -1;
+    if (c < BATCH && x.j0 + c < full) {
+        const int p = a.block_table[(size_t)x.b * a.max_pages + x.j0 + c];
+        x.my_phys = (p >= 0 && p < a.num_blocks) ? p : -1;
+    }
+
+    // Query fragment: q[h][16t + 4w + e] for head h = c, scaled to log2 units.
+    const float qscale = kLog2e / sqrtf((float)D);
+    {
+        const float* qp =
+            a.q + ((size_t)x.b * a.num_q_heads + x.g * x.G + (x.head_ok ? c : 0)) * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            f32x4 v = *reinterpret_cast<const f32x4*>(qp + 16 * t + 4 * w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x.qf[4 * t + e] = x.head_ok ? v[e] * qscale : 0.0f;
+        }
+    }
+    (void)DS;
+
+    // every page of the batch present and the rank not padded: no masking
+    if constexpr (kExact) {
+        if (x.j0 + BATCH <= full && __ballot(c < BATCH && x.my_phys < 0) == 0ull) {
+            scan_batch<P, D, RR, kExact, BATCH, PF, NACC, false, kPipe>(a, x);
+            return;
+        }
+    }
+    scan_batch<P, D, RR, kExact, BATCH, PF, NACC, true, kPipe>(a, x);
+}
+
+template <int P, int D, int RR, int BATCH = 16, int PF = 1, int NACC = 4, bool kPipe = false>
+hipError_t launch(const ScanParams& p, hipStream_t s) {
+    const long waves = (long)p.batch * p.num_kv_heads * ((p.max_pages + BATCH - 1) / BATCH);
+    const unsigned blocks = (unsigned)((waves + 3) / 4);
+    if (blocks == 0) return hipSuccess;
+    if (p.rank == RR)
+        hipLaunchKernelGGL((scan_kernel<P, D, RR, true, BATCH, PF, NACC, kPipe>), dim3(blocks),
+                           dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((scan_kernel<P, D, RR, false, BATCH, PF, NACC, kPipe>), dim3(blocks),
+                           dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int P, int D>
+hipError_t launch_rr(const ScanParams& p, hipStream_t s) {
+    if (p.rank <= 4) return launch<P, D, 4>(p, s);
+    if (p.rank <= 8) return launch<P, D, 8>(p, s);
+    return launch<P, D, 16>(p, s);
+}
+
+}  // namespace
+
+bool scan_supported(int page_size, int head_dim, int rank) {
+    return (page_size == 16 || page_size == 64) && (head_dim == 64 || head_dim == 128) &&
+           rank >= 1 && rank <= 16 && rank <= page_size && rank <= head_dim;
+}
+
+hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
+    if (p.page_size == 16 && p.head_dim == 64) return launch_rr<16, 64>(p, s);
+    if (p.page_size == 16 && p.head_dim == 128) return launch_rr<16, 128>(p, s);
+    if (p.page_size == 64 && p.head_dim == 64) return launch_rr<64, 64>(p, s);
+    return launch_rr<64, 128>(p, s);
+}
+
+}  // namespace locks

@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments on the host
+before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "locks.h")
+
+
+@pytest.fixture(scope="module")
+def lk():
+    import kv_cache_page_rank_amd as lk
+    if not os.path.exists(lk.LIB_PATH):
+        from kv_cache_page_rank_amd import build
+        build.build()
+    lk.lib()
+    return lk
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(locks_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lk):
+    names = _declared()
+    assert "locks_select" in names and "locks_build_summaries" in names
+    lib = lk.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert isinstance(getattr(lib, n), ctypes._CFuncPtr)
+    assert set(lk.EXPORTED) == set(names)
+
+
+def test_version_and_status_strings(lk):
+    lib = lk.lib()
+    assert lib.locks_version() == 100
+    assert lib.locks_status_string(0) == b"ok"
+    assert b"workspace" in lib.locks_status_string(3)
+    assert lib.locks_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes(lk):
+    ws = lk.workspace_bytes
+    # select: page masses [B][Hkv][max_pages] fp32, 256-byte aligned
+    assert ws(lk.OP_SELECT, 1, 16384, 32, 2, 64, 128, 8, 32) == 2 * 16384 * 4
+    # sparse attend: (k + 1) splits of (2 + d) floats per query head
+    assert ws(lk.OP_SPARSE_ATTEND, 1, 16384, 32, 2, 64, 128, 8, 32) == \
+        256 * ((32 * 33 * 2 * 4 + 255) // 256) + 32 * 33 * 128 * 4
+    assert ws(lk.OP_STEP, 1, 16384, 32, 2, 64, 128, 8, 32) == \
+        ws(lk.OP_SELECT, 1, 16384, 32, 2, 64, 128, 8, 32) + \
+        ws(lk.OP_SPARSE_ATTEND, 1, 16384, 32, 2, 64, 128, 8, 32)
+    assert ws(lk.OP_BUILD, 1, 16384, 32, 2, 64, 128, 8, 32) == 0
+    assert ws(lk.OP_DENSE_ATTEND, 1, 16384, 32, 2, 64, 128, 8, 32) > 0
+    assert ws(lk.OP_SELECT, 0, 16384, 32, 2, 64, 128, 8, 32) == 0
+
+
+def _fake(lk, P=64, d=128, r=8, H=2, NB=4, B=1, MP=4, dtype=1):
+    # non-null "device" addresses: validation never dereferences them
+    addr = 0x1000
+    kv = lk.CKVCache(dtype, NB, H, P, d, addr, addr)
+    sm = lk.CSummaries(NB, H, P, d, r, addr, addr, addr)
+    pt = lk.CPageTable(B, MP, addr, addr)
+    return kv, sm, pt, ctypes.c_void_p(addr)
+
+
+def test_host_validation_rejects_without_launch(lk):
+    lib = lk.lib()
+    by = ctypes.byref
+    kv, sm, pt, p = _fake(lk)
+    # null query
+    assert lib.locks_select(None, 32, by(sm), by(pt), 2048, p, p, p, p, 1 << 20, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    # H_q not a multiple of H_kv
+    assert lib.locks_scan(p, 31, by(sm), by(pt), p, None, None) == lk.LOCKS_ERR_INVALID_ARG
+    # group wider than 16
+    assert lib.locks_scan(p, 64, by(sm), by(pt), p, None, None) == lk.LOCKS_ERR_INVALID_ARG
+    # rank above min(P, d, 16)
+    _, sm_bad, _, _ = _fake(lk, r=17)
+    assert lib.locks_scan(p, 32, by(sm_bad), by(pt), p, None, None) == lk.LOCKS_ERR_UNSUPPORTED
+    # unsupported page size / head dim
+    _, sm_p, _, _ = _fake(lk, P=32)
+    assert lib.locks_scan(p, 32, by(sm_p), by(pt), p, None, None) == lk.LOCKS_ERR_UNSUPPORTED
+    kv_p, _, _, _ = _fake(lk, P=16, dtype=1)
+    assert lib.locks_dense_attend(p, 32, by(kv_p), by(pt), p, None, p, 1 << 30, None) == \
+        lk.LOCKS_ERR_UNSUPPORTED
+    # workspace missing / too small
+    assert lib.locks_select(p, 32, by(sm), by(pt), 2048, p, p, None, None, 0, None) == \
+        lk.LOCKS_ERR_WORKSPACE
+    assert lib.locks_sparse_attend(p, 32, by(kv), by(pt), p, 32, p, None, p, 16, None) == \
+        lk.LOCKS_ERR_WORKSPACE
+    # too many pages for the selection kernel
+    _, _, pt_big, _ = _fake(lk, MP=40000)
+    assert lib.locks_scan(p, 32, by(sm), by(pt_big), p, None, None) == lk.LOCKS_ERR_UNSUPPORTED
+    # negative budget, bad dtype, mismatched build shapes
+    assert lib.locks_select(p, 32, by(sm), by(pt), -1, p, p, p, p, 1 << 20, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    kv_bad, _, _, _ = _fake(lk, dtype=7)
+    assert lib.locks_dense_attend(p, 32, by(kv_bad), by(pt), p, None, p, 1 << 30, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    _, sm_d, _, _ = _fake(lk, d=64)
+    assert lib.locks_build_summaries(by(kv), by(pt), None, by(sm_d), None, 0, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    # sparse attend with pages requested but no list
+    assert lib.locks_sparse_attend(p, 32, by(kv), by(pt), None, 4, p, None, p, 1 << 30, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    # graph creation validates before capturing
+    h = ctypes.c_void_p()
+    assert lib.locks_step_graph_create(None, by(h)) == lk.LOCKS_ERR_INVALID_ARG
+    args = lk.CStepArgs(0x1000, 32, 2048, sm, kv, pt, 0x1000, 0x1000, None, 0x1000, None, None, 0)
+    assert lib.locks_step_graph_create(by(args), by(h)) == lk.LOCKS_ERR_WORKSPACE
+    assert lib.locks_step_graph_launch(None, None) == lk.LOCKS_ERR_INVALID_ARG
+    lib.locks_step_graph_destroy(None)
+
+
+def test_python_binding_fails_loudly_without_library(lk, tmp_path, monkeypatch):
+    monkeypatch.setattr(lk, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(lk, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        lk.lib()

@@ -1,0 +1,53 @@
+"""The decode step captured as one HIP graph: replays equal eager runs
+bitwise, also with eager work and synchronisation between replays."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_cases import DEV, Case, bf16_small, say, tiny
+from workload.device import summaries_to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("mk", [lambda: tiny(), lambda: bf16_small()], ids=["tiny", "bf16"])
+def test_graph_replay_equals_eager(mk):
+    import kv_cache_page_rank_amd as lk
+    case = Case(mk())
+    s = case.spec
+    summ = summaries_to_device(*case.oracle_summaries())
+    k = s.k_pages
+    ws_b = lk.workspace_bytes(lk.OP_STEP, s.batch, s.max_pages, s.num_q_heads, s.num_kv_heads,
+                              s.page_size, s.head_dim, s.rank, k)
+
+    def bufs():
+        return dict(sel=torch.full((s.batch, s.num_kv_heads, k), -9, dtype=torch.int32,
+                                   device=DEV),
+                    mass=torch.zeros((s.batch, s.num_kv_heads, k), device=DEV),
+                    out=torch.zeros((s.batch, s.num_q_heads, s.head_dim), dtype=case.kv.k.dtype,
+                                    device=DEV),
+                    lse=torch.zeros((s.batch, s.num_q_heads), device=DEV),
+                    ws=lk.workspace(ws_b))
+
+    e = bufs()
+    say("eager step")
+    lk.locks_select(case.q, summ, case.pages, s.budget_tokens, e["sel"], e["mass"], ws=e["ws"])
+    attn_ws = e["ws"][lk.workspace_bytes(lk.OP_SELECT, s.batch, s.max_pages, s.num_q_heads,
+                                         s.num_kv_heads, s.page_size, s.head_dim, s.rank, k):]
+    lk.locks_sparse_attend(case.q, case.kv, case.pages, e["sel"], e["out"], e["lse"], ws=attn_ws)
+    torch.cuda.synchronize()
+
+    g = bufs()
+    say("graph create")
+    graph = lk.StepGraph(case.q, summ, case.kv, case.pages, s.budget_tokens, g["sel"], g["mass"],
+                         g["out"], g["lse"], ws=g["ws"])
+    for rep in range(4):
+        for t in (g["sel"], g["mass"], g["out"], g["lse"]):
+            t.zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        say("graph replay", rep)
+        graph.launch()
+        torch.cuda.synchronize()
+        for key in ("sel", "mass", "out", "lse"):
+            assert torch.equal(g[key], e[key]), (rep, key)
+    graph.close()

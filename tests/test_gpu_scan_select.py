@@ -1,0 +1,152 @@
+"""GPU parity of the summary scan (page masses) and the top-k selection,
+against the oracle on the same seeded inputs, through the C ABI."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_cases import DEV, Case, band_ok, bf16_small, masses_close, say, tiny, to_np
+from workload.device import summaries_to_device
+
+pytestmark = pytest.mark.gpu
+
+SCAN_CASES = [
+    ("tiny-r4", lambda: tiny()),
+    ("tiny-r16", lambda: tiny(rank=16)),
+    ("tiny-G4-r3-ragged", lambda: tiny(num_q_heads=4, num_kv_heads=1, rank=3, seq_lens=[1000])),
+    ("bf16-G16-r8", lambda: bf16_small()),
+    ("bf16-G16-r2", lambda: bf16_small(rank=2)),
+    ("bf16-G4-r16-offset", lambda: bf16_small(num_kv_heads=8, rank=16, page_offset_std=1.0)),
+    ("bf16-G1-r5", lambda: bf16_small(num_q_heads=2, rank=5)),
+]
+
+
+@pytest.mark.parametrize("name,mk", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
+def test_scan_matches_oracle(name, mk):
+    """Scan alone, fed the oracle's (fp32) summaries: per-head and group
+    log-masses within 1e-4, -inf exactly where a page is not full."""
+    case = Case(mk())
+    s = case.spec
+    mu, basis, coef = case.oracle_summaries()
+    head_o, page_o = oracle.scan_pool(case.lay, s.rank, case.layer.q, mu, basis, coef)
+    summ = summaries_to_device(mu, basis, coef)
+    import kv_cache_page_rank_amd as lk
+    pm = torch.full((s.batch, s.num_kv_heads, s.max_pages), 7.0, device=DEV)
+    hm = torch.full((s.batch, s.num_q_heads, s.max_pages), 7.0, device=DEV)
+    say("scan", name, s)
+    lk.locks_scan(case.q, summ, case.pages, pm, hm)
+    torch.cuda.synchronize()
+    assert masses_close(to_np(pm), page_o) <= 1e-4
+    assert masses_close(to_np(hm), head_o) <= 1e-4
+
+
+def test_scan_full_rank_is_exact_lse():
+    """r = min(P, d): the GPU estimate from oracle summaries equals the exact
+    page LSE (the selection that reads every key)."""
+    case = Case(tiny(rank=16))
+    mu, basis, coef = case.oracle_summaries()
+    _, exact = oracle.exact_pool(case.lay, case.layer.q, case.k_f32)
+    import kv_cache_page_rank_amd as lk
+    s = case.spec
+    pm = torch.empty((1, 1, s.max_pages), device=DEV)
+    say("scan full rank", s)
+    lk.locks_scan(case.q, summaries_to_device(mu, basis, coef), case.pages, pm)
+    torch.cuda.synchronize()
+    assert masses_close(to_np(pm), exact) <= 1e-4
+
+
+# ------------------------------------------------------------------ top-k
+
+def _topk_case(rng, B, H, MP, P, lens, levels=None, neg_inf=0.0):
+    if levels:
+        vals = rng.standard_normal(levels).astype(np.float32)
+        pm = vals[rng.integers(0, levels, (B, H, MP))]
+    else:
+        pm = rng.standard_normal((B, H, MP)).astype(np.float32)
+    if neg_inf:
+        pm[rng.random(pm.shape) < neg_inf] = -np.inf
+    bt = np.zeros((B, MP), np.int32)
+    return pm, bt, np.asarray(lens, np.int32)
+
+
+TOPK_CASES = [
+    # name, B, H, max_pages, P, seq_lens, budget, width, levels, -inf fraction
+    ("one-page", 1, 1, 1, 64, [64], 2048, 32, None, 0.0),
+    ("fewer-pages-than-k", 2, 2, 10, 64, [640, 64 * 7 + 5], 2048, 32, None, 0.0),
+    ("budget-below-page", 1, 2, 50, 64, [3200], 63, 1, None, 0.0),
+    ("ties", 2, 3, 3000, 64, [64 * 3000, 64 * 1777 + 1], 2048, 32, 3, 0.0),
+    ("ties-many-k", 1, 2, 5000, 16, [16 * 5000], 16 * 700, 700, 5, 0.0),
+    ("neg-inf", 1, 2, 2100, 64, [64 * 2100], 2048, 32, None, 0.5),
+    ("all-equal", 1, 1, 4096, 64, [64 * 4096], 2048, 32, 1, 0.0),
+    ("max-pages", 1, 2, 32768, 64, [64 * 32768], 4096, 64, 50, 0.0),
+    ("empty-seq", 2, 1, 8, 64, [0, 63], 2048, 32, None, 0.0),
+    ("wide-rows", 1, 1, 1500, 64, [64 * 1500], 2048, 40, None, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_topk_bit_exact(case):
+    """Integer work: identical fp32 inputs give identical page lists and
+    masses (ties to the lowest page index, ascending order, -1/-inf pads)."""
+    name, B, H, MP, P, lens, budget, width, levels, ninf = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    pm, bt, sl = _topk_case(rng, B, H, MP, P, lens, levels, ninf)
+    lay = oracle.Layout(H, H, 64, P, bt, sl)
+    sel_o, mass_o = oracle.select_pool(lay, budget, pm, width)
+    import kv_cache_page_rank_amd as lk
+    pages = lk.PageTable(torch.from_numpy(bt).to(DEV), torch.from_numpy(sl).to(DEV))
+    sel = torch.full((B, H, width), -7, dtype=torch.int32, device=DEV)
+    mass = torch.full((B, H, width), 7.0, device=DEV)
+    say("topk", name)
+    lk.locks_topk(torch.from_numpy(pm).to(DEV), pages, P, budget, sel, mass)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), sel_o)
+    np.testing.assert_array_equal(mass.cpu().numpy(), mass_o)
+
+
+@pytest.mark.parametrize("mk", [lambda: tiny(), lambda: bf16_small(), lambda: bf16_small(rank=2)])
+def test_select_end_to_end_band(mk):
+    """locks_select (scan + top-k) from oracle summaries against the oracle's
+    selection: identical except pages within 1e-3 of the k-th mass."""
+    case = Case(mk())
+    s = case.spec
+    mu, basis, coef = case.oracle_summaries()
+    _, page_o = oracle.scan_pool(case.lay, s.rank, case.layer.q, mu, basis, coef, heads=False)
+    width = s.k_pages
+    sel_o, _ = oracle.select_pool(case.lay, s.budget_tokens, page_o.astype(np.float32), width)
+    import kv_cache_page_rank_amd as lk
+    sel = torch.empty((s.batch, s.num_kv_heads, width), dtype=torch.int32, device=DEV)
+    mass = torch.empty((s.batch, s.num_kv_heads, width), device=DEV)
+    ws = lk.workspace(lk.workspace_bytes(lk.OP_SELECT, s.batch, s.max_pages, s.num_q_heads,
+                                         s.num_kv_heads, s.page_size, s.head_dim, s.rank, width))
+    say("select e2e", s)
+    lk.locks_select(case.q, summaries_to_device(mu, basis, coef), case.pages, s.budget_tokens,
+                    sel, mass, ws=ws)
+    torch.cuda.synchronize()
+    sel_g = sel.cpu().numpy()
+    for b in range(s.batch):
+        f = s.seq_lens[b] // s.page_size
+        for g in range(s.num_kv_heads):
+            assert band_ok(sel_g[b, g], sel_o[b, g], page_o[b, g, :f], min(width, f)), (b, g)
+            assert list(sel_g[b, g]) == sorted(sel_g[b, g][sel_g[b, g] >= 0]) + \
+                [-1] * int((sel_g[b, g] < 0).sum())
+
+
+def test_select_deterministic():
+    case = Case(bf16_small())
+    s = case.spec
+    summ = summaries_to_device(*case.oracle_summaries())
+    import kv_cache_page_rank_amd as lk
+    outs = []
+    for _ in range(2):
+        sel = torch.empty((s.batch, s.num_kv_heads, s.k_pages), dtype=torch.int32, device=DEV)
+        mass = torch.empty((s.batch, s.num_kv_heads, s.k_pages), device=DEV)
+        pm = torch.empty((s.batch, s.num_kv_heads, s.max_pages), device=DEV)
+        say("select determinism")
+        lk.locks_select(case.q, summ, case.pages, s.budget_tokens, sel, mass, page_logmass=pm)
+        torch.cuda.synchronize()
+        outs.append((sel.cpu(), mass.cpu(), pm.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

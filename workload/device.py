@@ -1,0 +1,33 @@
+"""Upload a generated layer to the GPU in the library's cache layout.
+
+Layout marshalling only: K pool [NB][H_kv][P][d], V pool stored per page
+transposed as [NB][H_kv][d][P], int32 page table, float32 queries.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def kv_tensor(arr: np.ndarray, device) -> torch.Tensor:
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(arr).to(device)
+
+
+def upload(layer, device="cuda"):
+    """Returns (q, PagedKV, PageTable) for a workload.Layer."""
+    import kv_cache_page_rank_amd as lk
+    q = torch.from_numpy(layer.q).to(device)
+    k = kv_tensor(layer.k, device)
+    v = kv_tensor(layer.v, device).transpose(-1, -2).contiguous()
+    pages = lk.PageTable(torch.from_numpy(layer.block_table).to(device),
+                         torch.from_numpy(layer.seq_lens).to(device))
+    return q, lk.PagedKV(k, v), pages
+
+
+def summaries_to_device(mu, basis, coef, device="cuda"):
+    import kv_cache_page_rank_amd as lk
+    return lk.Summaries(torch.from_numpy(np.ascontiguousarray(mu, np.float32)).to(device),
+                        torch.from_numpy(np.ascontiguousarray(basis, np.float32)).to(device),
+                        torch.from_numpy(np.ascontiguousarray(coef, np.float32)).to(device))
