@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-target-s", type=float, default=12.0,
                     help="approximate CPU seconds spent on the oracle sample")
     ap.add_argument("--threads", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
 
 
@@ -58,6 +60,59 @@ def cpu_threads():
     except AttributeError:
         n = os.cpu_count() or 1
     return max(1, min(n, 16))
+
+
+# Kernel sources whose HBM traffic the committed counter summary describes.
+SCAN_SOURCES = ["kv_cache_page_rank_amd/csrc/scan.hip", "kv_cache_page_rank_amd/csrc/device_common.hpp",
+                "kv_cache_page_rank_amd/csrc/launchers.hpp"]
+SCAN_COUNTERS = "profiles/scan_kernel_glm4-9b-layer-1m_hbm_counters.txt"
+
+
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counted_traffic(summary, sources, workload_name):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the copy calibration), or None
+    when there is none for this workload or the kernel's sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, summary)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("workload") != workload_name or kv.get("source_sha256") != sources_sha256(sources):
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(args):
+    """A plain device-to-device copy of 1 GiB, repeated: under rocprofv3
+    --pmc its FETCH_SIZE / WRITE_SIZE per dispatch against the known 1 GiB
+    read and 1 GiB written give the counters' scale factors."""
+    import torch
+
+    n = 1 << 28  # fp32 elements = 1 GiB
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(max(1, args.steps)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                      "dispatches": max(1, args.steps)}), flush=True)
 
 
 def time_events(fn, iters, torch):
@@ -81,6 +136,10 @@ def main():
               "(the hot path is single-GPU; see DESIGN.md for how it would shard).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
 
     import numpy as np
     import torch
@@ -222,7 +281,8 @@ def main():
                    "layer_copies_rotated": L, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "summary scan",
                      "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic(SCAN_COUNTERS, SCAN_SOURCES, spec.name),
                      "bytes_per_launch": scan_b, "avg_launch_us": round(scan_mean, 3)},
         "cpu_baseline": cpu,
         "breakdown": {
