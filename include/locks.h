@@ -162,7 +162,10 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
  * padded with -1 / -inf.  No K or V pointer is taken: selection reads no
  * candidate key or value (abstract).
  * page_logmass: optional device [B][H_kv][max_pages] output (NULL: the
- * workspace holds it).  Workspace: locks_workspace_bytes(LOCKS_OP_SELECT,..).
+ * workspace holds it).  Workspace: locks_workspace_bytes(LOCKS_OP_SELECT,..);
+ * it also receives the run maxima (see locks_scan) that let the top-k read
+ * only the runs able to hold a winner.  A workspace is required unless
+ * page_logmass is given (then, without one, the top-k reads every mass).
  */
 locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
                           const locks_page_table* pages, int32_t budget_tokens,
@@ -174,19 +177,29 @@ locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summa
  * locks_select).  page_logmass [B][H_kv][max_pages] is required;
  * head_logmass [B][H_q][max_pages] (per-head s_hat) is optional.
  * Entries of pages that are not full, or past max_pages' valid range, are -inf.
+ * run_max (optional) [B][H_kv][ceil(max_pages / LOCKS_RUN_PAGES)]: entry r is
+ * the largest page_logmass value of pages r*LOCKS_RUN_PAGES ..
+ * (r+1)*LOCKS_RUN_PAGES - 1 (exactly one of those fp32 values; -inf when
+ * none is a full page).  An index for locks_topk, not part of the method.
  */
+#define LOCKS_RUN_PAGES 16
 locks_status locks_scan(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
                         const locks_page_table* pages, float* page_logmass, float* head_logmass,
-                        void* stream);
+                        float* run_max, void* stream);
 
 /*
  * Step 2's selection alone, from given group masses page_logmass
  * [B][H_kv][max_pages] (only entries j < seq_lens[b] / P are read), with the
  * rule of locks_select.  width = row width of sel_pages / sel_logmass.
+ * run_max (optional): the run maxima of these masses as locks_scan writes
+ * them; with them the kernel reads only the runs whose maximum reaches a
+ * lower bound of the k-th largest mass.  Maxima that do not match the
+ * masses give an unspecified selection.
  */
 locks_status locks_topk(const float* page_logmass, const locks_page_table* pages,
                         int32_t num_kv_heads, int32_t page_size, int32_t budget_tokens,
-                        int32_t width, int32_t* sel_pages, float* sel_logmass, void* stream);
+                        int32_t width, int32_t* sel_pages, float* sel_logmass,
+                        const float* run_max, void* stream);
 
 /*
  * Step 3 - attention of every query head over the tokens of its group's

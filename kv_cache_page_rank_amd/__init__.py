@@ -20,6 +20,7 @@ LOCKS_OK, LOCKS_ERR_INVALID_ARG, LOCKS_ERR_UNSUPPORTED, LOCKS_ERR_WORKSPACE, LOC
     range(5)
 LOCKS_F32, LOCKS_BF16 = 0, 1
 OP_BUILD, OP_SELECT, OP_SPARSE_ATTEND, OP_DENSE_ATTEND, OP_STEP = range(5)
+RUN_PAGES = 16  # pages per run maximum (LOCKS_RUN_PAGES)
 
 EXPORTED = ("locks_workspace_bytes", "locks_build_summaries", "locks_select", "locks_scan",
             "locks_topk", "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
@@ -81,8 +82,8 @@ def lib() -> ctypes.CDLL:
                                             vp]
         L.locks_select.argtypes = [vp, i32, P(CSummaries), P(CPageTable), i32, vp, vp, vp, vp, sz,
                                    vp]
-        L.locks_scan.argtypes = [vp, i32, P(CSummaries), P(CPageTable), vp, vp, vp]
-        L.locks_topk.argtypes = [vp, P(CPageTable), i32, i32, i32, i32, vp, vp, vp]
+        L.locks_scan.argtypes = [vp, i32, P(CSummaries), P(CPageTable), vp, vp, vp, vp]
+        L.locks_topk.argtypes = [vp, P(CPageTable), i32, i32, i32, i32, vp, vp, vp, vp]
         L.locks_sparse_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, i32, vp, vp,
                                           vp, sz, vp]
         L.locks_dense_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, vp, vp, sz, vp]
@@ -190,18 +191,19 @@ def locks_build_summaries(cache: PagedKV, pages: PageTable, out: Summaries, page
 
 
 def locks_scan(q, summaries: Summaries, pages: PageTable, page_logmass, head_logmass=None,
-               stream=None):
+               run_max=None, stream=None):
     sc, pc = summaries.c(), pages.c()
     _check(lib().locks_scan(_ptr(q), q.shape[1], ctypes.byref(sc), ctypes.byref(pc),
-                            _ptr(page_logmass), _ptr(head_logmass), _stream(stream)), "locks_scan")
+                            _ptr(page_logmass), _ptr(head_logmass), _ptr(run_max),
+                            _stream(stream)), "locks_scan")
 
 
 def locks_topk(page_logmass, pages: PageTable, page_size, budget_tokens, sel_pages,
-               sel_logmass=None, stream=None):
+               sel_logmass=None, run_max=None, stream=None):
     pc = pages.c()
     _check(lib().locks_topk(_ptr(page_logmass), ctypes.byref(pc), page_logmass.shape[1],
                             page_size, budget_tokens, sel_pages.shape[-1], _ptr(sel_pages),
-                            _ptr(sel_logmass), _stream(stream)), "locks_topk")
+                            _ptr(sel_logmass), _ptr(run_max), _stream(stream)), "locks_topk")
 
 
 def locks_select(q, summaries: Summaries, pages: PageTable, budget_tokens, sel_pages, sel_logmass,

@@ -49,8 +49,15 @@ locks_status check_cache(const locks_kv_cache* kv, bool need_v) {
     return LOCKS_OK;
 }
 
-size_t select_ws(int32_t batch, int32_t max_pages, int32_t hkv) {
+int32_t num_runs(int32_t max_pages) { return (max_pages + locks::kRunPages - 1) / locks::kRunPages; }
+
+// Selection workspace: page masses, then the run maxima.
+size_t select_mass_bytes(int32_t batch, int32_t max_pages, int32_t hkv) {
     return align_up((size_t)batch * hkv * max_pages * sizeof(float));
+}
+size_t select_ws(int32_t batch, int32_t max_pages, int32_t hkv) {
+    return select_mass_bytes(batch, max_pages, hkv) +
+           align_up((size_t)batch * hkv * num_runs(max_pages) * sizeof(float));
 }
 
 size_t attend_ws(int32_t batch, int32_t hq, int32_t d, int32_t splits) {
@@ -108,7 +115,7 @@ locks_status attend_common(const float* q, int32_t hq, const locks_kv_cache* kv,
 
 locks_status scan_common(const float* q, int32_t hq, const locks_summaries* s,
                          const locks_page_table* pt, float* page_logmass, float* head_logmass,
-                         hipStream_t stream) {
+                         float* run_max, hipStream_t stream) {
     locks::ScanParams p{};
     p.q = q;
     p.mu = s->mu;
@@ -126,13 +133,14 @@ locks_status scan_common(const float* q, int32_t hq, const locks_summaries* s,
     p.rank = s->rank;
     p.page_logmass = page_logmass;
     p.head_logmass = head_logmass;
+    p.run_max = run_max;
     const hipError_t e = locks::launch_scan(p, stream);
     return e == hipSuccess ? LOCKS_OK : hip_fail(e);
 }
 
 locks_status topk_common(const float* page_logmass, const locks_page_table* pt, int32_t hkv,
                          int32_t page_size, int32_t budget, int32_t width, int32_t* sel,
-                         float* sel_mass, hipStream_t stream) {
+                         float* sel_mass, const float* run_max, hipStream_t stream) {
     locks::TopkParams p{};
     p.page_logmass = page_logmass;
     p.seq_lens = pt->seq_lens;
@@ -145,6 +153,7 @@ locks_status topk_common(const float* page_logmass, const locks_page_table* pt, 
     p.width = width;
     p.sel_pages = sel;
     p.sel_logmass = sel_mass;
+    p.run_max = run_max;
     const hipError_t e = locks::launch_topk(p, stream);
     return e == hipSuccess ? LOCKS_OK : hip_fail(e);
 }
@@ -217,19 +226,20 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
 
 locks_status locks_scan(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
                         const locks_page_table* pages, float* page_logmass, float* head_logmass,
-                        void* stream) {
+                        float* run_max, void* stream) {
     locks_status st = check_summaries(summaries, true);
     if (st != LOCKS_OK) return st;
     if ((st = check_page_table(pages)) != LOCKS_OK) return st;
     if (!q || !page_logmass || !head_dims_ok(num_q_heads, summaries->num_kv_heads))
         return LOCKS_ERR_INVALID_ARG;
-    return scan_common(q, num_q_heads, summaries, pages, page_logmass, head_logmass,
+    return scan_common(q, num_q_heads, summaries, pages, page_logmass, head_logmass, run_max,
                        static_cast<hipStream_t>(stream));
 }
 
 locks_status locks_topk(const float* page_logmass, const locks_page_table* pages,
                         int32_t num_kv_heads, int32_t page_size, int32_t budget_tokens,
-                        int32_t width, int32_t* sel_pages, float* sel_logmass, void* stream) {
+                        int32_t width, int32_t* sel_pages, float* sel_logmass,
+                        const float* run_max, void* stream) {
     locks_status st = check_page_table(pages);
     if (st != LOCKS_OK) return st;
     if (!page_logmass || !sel_pages || num_kv_heads <= 0 || page_size <= 0 || budget_tokens < 0 ||
@@ -237,7 +247,7 @@ locks_status locks_topk(const float* page_logmass, const locks_page_table* pages
         return LOCKS_ERR_INVALID_ARG;
     if (width == 0) return LOCKS_OK;
     return topk_common(page_logmass, pages, num_kv_heads, page_size, budget_tokens, width,
-                       sel_pages, sel_logmass, static_cast<hipStream_t>(stream));
+                       sel_pages, sel_logmass, run_max, static_cast<hipStream_t>(stream));
 }
 
 locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
@@ -251,18 +261,27 @@ locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summa
         return LOCKS_ERR_INVALID_ARG;
     const int32_t width = budget_tokens / summaries->page_size;
     if (width > 0 && !sel_pages) return LOCKS_ERR_INVALID_ARG;
+    // The workspace holds the page masses (unless the caller takes them) and
+    // the run maxima; without a workspace the top-k reads every mass.
+    const bool have_ws =
+        ws && ws_bytes >= select_ws(pages->batch, pages->max_pages, summaries->num_kv_heads);
     float* masses = page_logmass;
     if (!masses) {
-        if (!ws || ws_bytes < select_ws(pages->batch, pages->max_pages, summaries->num_kv_heads))
-            return LOCKS_ERR_WORKSPACE;
+        if (!have_ws) return LOCKS_ERR_WORKSPACE;
         masses = static_cast<float*>(ws);
     }
+    float* run_max = nullptr;
+    if (have_ws)
+        run_max = reinterpret_cast<float*>(
+            static_cast<char*>(ws) +
+            select_mass_bytes(pages->batch, pages->max_pages, summaries->num_kv_heads));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = scan_common(q, num_q_heads, summaries, pages, masses, nullptr, s)) != LOCKS_OK)
+    if ((st = scan_common(q, num_q_heads, summaries, pages, masses, nullptr, run_max, s)) !=
+        LOCKS_OK)
         return st;
     if (width == 0) return LOCKS_OK;
     return topk_common(masses, pages, summaries->num_kv_heads, summaries->page_size, budget_tokens,
-                       width, sel_pages, sel_logmass, s);
+                       width, sel_pages, sel_logmass, run_max, s);
 }
 
 locks_status locks_sparse_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,
@@ -289,10 +308,8 @@ locks_status locks_step_graph_create(const locks_step_args* a, locks_step_graph*
     if (!a || !graph) return LOCKS_ERR_INVALID_ARG;
     *graph = nullptr;
     const int32_t k = a->summaries.page_size > 0 ? a->budget_tokens / a->summaries.page_size : 0;
-    const size_t sel_bytes = a->page_logmass
-                                 ? 0
-                                 : select_ws(a->pages.batch, a->pages.max_pages,
-                                             a->summaries.num_kv_heads);
+    const size_t sel_bytes =
+        select_ws(a->pages.batch, a->pages.max_pages, a->summaries.num_kv_heads);
     const size_t need = locks_workspace_bytes(LOCKS_OP_STEP, a->pages.batch, a->pages.max_pages,
                                               a->num_q_heads, a->summaries.num_kv_heads,
                                               a->summaries.page_size, a->summaries.head_dim,
@@ -370,6 +387,6 @@ const char* locks_status_string(int32_t status) {
 
 int32_t locks_last_hip_error(void) { return g_last_hip_error; }
 
-int32_t locks_version(void) { return 100; }
+int32_t locks_version(void) { return 101; }
 
 }  // extern "C"

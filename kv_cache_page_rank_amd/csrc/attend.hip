@@ -506,54 +506,62 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const AttnParams a) {
     }
 }
 
-// Merge of the partials of one (b, h), in partial order.  Grid: (b, h) x
-// 32-dim chunk; thread t handles dims [32*chunk + 4*(t%8), +4) over the
-// partials p = t/8, t/8 + 32, ...; the 32 part sums are added in order.
+// Merge of the partials of one (b, h).  Grid: (b, h) x 32-dim chunk;
+// thread t handles dims [32*chunk + 4*(t%8), +4) over the partials
+// p = t/8, t/8 + 32, ... with a running (max, sum, output) rescaled as each
+// partial arrives (one round of loads, no max pre-pass); the 32 running
+// states are then combined in order.  Deterministic: the combination order
+// depends only on the shapes.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnParams a) {
-    __shared__ float red[256];
     __shared__ f32x4 pacc[32][8];
-    __shared__ float pl[32];
+    __shared__ float pm[32], pl[32];
     const int bh = blockIdx.x;
     const int chunk = blockIdx.y;
     const int t = threadIdx.x;
     const int NP = a.num_parts;
     const float* ml = a.part_ml + (size_t)bh * NP * 2;
-    const float* po = a.part_o + (size_t)bh * NP * D;
-
-    float mx = -INFINITY;
-    for (int s = t; s < NP; s += 256)
-        if (ml[2 * s + 1] > 0.f) mx = fmaxf(mx, ml[2 * s]);
-    red[t] = mx;
-    __syncthreads();
-    for (int stride = 128; stride > 0; stride >>= 1) {
-        if (t < stride) red[t] = fmaxf(red[t], red[t + stride]);
-        __syncthreads();
-    }
-    const float M = red[0];
+    const float* po = a.part_o + (size_t)bh * NP * D + 32 * chunk;
 
     const int d4 = t & 7, part = t >> 3;
+    float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-    if (M != -INFINITY) {
-        for (int s = part; s < NP; s += 32) {
-            const float l = ml[2 * s + 1];
-            const float wt = l > 0.f ? fast_exp2(ml[2 * s] - M) : 0.f;
-            const f32x4 o = *reinterpret_cast<const f32x4*>(po + (size_t)s * D + 32 * chunk + 4 * d4);
-            acc += o * wt;
-            lsum += l * wt;
-        }
+    // Branch-free so that every partial's loads are issued before any is
+    // used; an empty partial (l = 0) leaves the running state unchanged.
+#pragma unroll 4
+    for (int s = part; s < NP; s += 32) {
+        const f32x2 m_l = *reinterpret_cast<const f32x2*>(ml + 2 * s);
+        const f32x4 o = *reinterpret_cast<const f32x4*>(po + (size_t)s * D + 4 * d4);
+        const bool ok = m_l[1] > 0.f;
+        const float mn = fmaxf(m_run, m_l[0]);
+        const float w_old = fast_exp2(m_run - mn);  // 0 while nothing is held
+        const float w_new = fast_exp2(m_l[0] - mn);
+        const f32x4 acc_n = acc * w_old + o * w_new;
+        const float l_n = l_run * w_old + m_l[1] * w_new;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = ok ? acc_n[e] : acc[e];
+        l_run = ok ? l_n : l_run;
+        m_run = ok ? mn : m_run;
     }
     pacc[part][d4] = acc;
-    if (d4 == 0) pl[part] = lsum;
+    if (d4 == 0) {
+        pm[part] = m_run;  // -inf with l = 0 when the thread held nothing
+        pl[part] = l_run;
+    }
     __syncthreads();
     if (t < 8) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int pp = 0; pp < 32; ++pp) M = fmaxf(M, pm[pp]);
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
         float L = 0.f;
-#pragma unroll 8
-        for (int pp = 0; pp < 32; ++pp) {
-            o += pacc[pp][t];
-            L += pl[pp];
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int pp = 0; pp < 32; ++pp) {
+                const float wt = fast_exp2(pm[pp] - M);  // 0 for empty states (-inf)
+                o += pacc[pp][t] * wt;
+                L += pl[pp] * wt;
+            }
         }
         const size_t base = (size_t)bh * D + 32 * chunk + 4 * t;
 #pragma unroll

@@ -8,6 +8,11 @@
 
 namespace locks {
 
+// Pages per run: the scan may also write, per (b, g), the maximum page mass
+// of every run of kRunPages consecutive pages; the top-k uses these maxima
+// to read only the runs that can hold a winner.
+constexpr int kRunPages = 16;
+
 struct ScanParams {
     const float* q;        // [B][Hq][D]
     const float* mu;       // [NB][Hkv][D]
@@ -19,6 +24,7 @@ struct ScanParams {
     int32_t page_size, head_dim, rank;
     float* page_logmass;   // [B][Hkv][max_pages]
     float* head_logmass;   // [B][Hq][max_pages] or null
+    float* run_max;        // [B][Hkv][ceil(max_pages / kRunPages)] or null
 };
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 bool scan_supported(int page_size, int head_dim, int rank);
@@ -29,6 +35,7 @@ struct TopkParams {
     int32_t batch, num_kv_heads, max_pages, page_size, k_req, width;
     int32_t* sel_pages;         // [B][Hkv][width]
     float* sel_logmass;         // [B][Hkv][width] or null
+    const float* run_max;       // [B][Hkv][ceil(max_pages / kRunPages)] or null
 };
 constexpr int kTopkMaxPages = 32768;
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);

@@ -20,6 +20,8 @@
 // MFMA step s of a tile contracts d = 16*(s/4) + 4*(l/16) + s%4, so lane l
 // loads d-chunks [16t + 4*(l/16), +4) of its row (64 contiguous bytes per
 // row per load instruction).
+// When asked, the wave also writes the largest page mass of its 16 pages
+// (the run maximum the top-k uses to skip runs that cannot hold a winner).
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -153,6 +155,7 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
     }
     // lane (w, c) now holds beta[page j0 + 4w + v][head c] in element v.
 
+    float run_mx = -INFINITY;  // max of the written page masses (row w holds pages 4w..4w+3)
     f32x4 Tcur;
     if constexpr (kPipe) Tcur = basis_product(ring[0]);
 #pragma unroll
@@ -200,16 +203,23 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
             const float a2 = gm + fast_log2(gs);
             if (w == (pb >> 2) && j < a.max_pages) {
                 const bool ok = !kMasked || phys_uniform(pb) >= 0;
-                if (c == 0) x.out_page[j] = ok ? a2 * kLn2 : -INFINITY;
+                const float mass = ok ? a2 * kLn2 : -INFINITY;
+                run_mx = fmaxf(run_mx, mass);
+                if (c == 0) x.out_page[j] = mass;
                 if (a.head_logmass && x.head_ok)
                     a.head_logmass[((size_t)x.b * a.num_q_heads + g * x.G + c) * a.max_pages + j] =
                         ok ? s2 * kLn2 : -INFINITY;
             }
         }
     }
+    if (a.run_max) {
+        run_mx = max_over_rows(run_mx);
+        const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
+        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / BATCH] = run_mx;
+    }
 }
 
-// Tuning: BATCH pages per wave (8 or 16), PF tiles prefetched ahead, NACC
+// Tuning: BATCH pages per wave (one run of pages), PF tiles prefetched ahead, NACC
 // independent accumulator chains for the d contraction, kPipe software
 // pipelining of the tile loop.
 template <int P, int D, int RR, bool kExact, int BATCH = 16, int PF = 2, int NACC = 2,
@@ -217,7 +227,7 @@ template <int P, int D, int RR, bool kExact, int BATCH = 16, int PF = 2, int NAC
 __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     static_assert(P % 16 == 0 && D % 16 == 0, "P and d must be multiples of 16");
     static_assert(RR == 4 || RR == 8 || RR == 16, "padded rank");
-    static_assert(BATCH == 8 || BATCH == 16, "pages per wave");
+    static_assert(BATCH == kRunPages, "one wave per run of pages");
     constexpr int DS = D / 4;
     constexpr int DT = D / 16;
 
@@ -242,6 +252,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
     x.out_page = a.page_logmass + ((size_t)x.b * x.Hkv + x.g) * a.max_pages;
     if (x.j0 >= full) {  // whole batch past the full pages
+        if (a.run_max && x.lane == 0)
+            a.run_max[((size_t)x.b * x.Hkv + x.g) * nbatch + jb] = -INFINITY;
         if (w == 0 && c < BATCH && x.j0 + c < a.max_pages) {
             x.out_page[x.j0 + c] = -INFINITY;
             if (a.head_logmass)

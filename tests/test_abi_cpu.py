@@ -39,7 +39,7 @@ def test_header_symbols_exported(lk):
 
 def test_version_and_status_strings(lk):
     lib = lk.lib()
-    assert lib.locks_version() == 100
+    assert lib.locks_version() == 101
     assert lib.locks_status_string(0) == b"ok"
     assert b"workspace" in lib.locks_status_string(3)
     assert lib.locks_status_string(99) == b"unknown status"
@@ -47,8 +47,10 @@ def test_version_and_status_strings(lk):
 
 def test_workspace_sizes(lk):
     ws = lk.workspace_bytes
-    # select: page masses [B][Hkv][max_pages] fp32, 256-byte aligned
-    assert ws(lk.OP_SELECT, 1, 16384, 32, 2, 64, 128, 8, 32) == 2 * 16384 * 4
+    # select: page masses [B][Hkv][max_pages] fp32, then run maxima
+    # [B][Hkv][ceil(max_pages / 16)], each 256-byte aligned
+    assert ws(lk.OP_SELECT, 1, 16384, 32, 2, 64, 128, 8, 32) == 2 * 16384 * 4 + 2 * 1024 * 4
+    assert ws(lk.OP_SELECT, 1, 100, 32, 2, 64, 128, 8, 32) == 1024 + 256
     # sparse attend: (k + 1) splits of (2 + d) floats per query head
     assert ws(lk.OP_SPARSE_ATTEND, 1, 16384, 32, 2, 64, 128, 8, 32) == \
         256 * ((32 * 33 * 2 * 4 + 255) // 256) + 32 * 33 * 128 * 4
@@ -77,15 +79,15 @@ def test_host_validation_rejects_without_launch(lk):
     assert lib.locks_select(None, 32, by(sm), by(pt), 2048, p, p, p, p, 1 << 20, None) == \
         lk.LOCKS_ERR_INVALID_ARG
     # H_q not a multiple of H_kv
-    assert lib.locks_scan(p, 31, by(sm), by(pt), p, None, None) == lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_scan(p, 31, by(sm), by(pt), p, None, None, None) == lk.LOCKS_ERR_INVALID_ARG
     # group wider than 16
-    assert lib.locks_scan(p, 64, by(sm), by(pt), p, None, None) == lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_scan(p, 64, by(sm), by(pt), p, None, None, None) == lk.LOCKS_ERR_INVALID_ARG
     # rank above min(P, d, 16)
     _, sm_bad, _, _ = _fake(lk, r=17)
-    assert lib.locks_scan(p, 32, by(sm_bad), by(pt), p, None, None) == lk.LOCKS_ERR_UNSUPPORTED
+    assert lib.locks_scan(p, 32, by(sm_bad), by(pt), p, None, None, None) == lk.LOCKS_ERR_UNSUPPORTED
     # unsupported page size / head dim
     _, sm_p, _, _ = _fake(lk, P=32)
-    assert lib.locks_scan(p, 32, by(sm_p), by(pt), p, None, None) == lk.LOCKS_ERR_UNSUPPORTED
+    assert lib.locks_scan(p, 32, by(sm_p), by(pt), p, None, None, None) == lk.LOCKS_ERR_UNSUPPORTED
     kv_p, _, _, _ = _fake(lk, P=16, dtype=1)
     assert lib.locks_dense_attend(p, 32, by(kv_p), by(pt), p, None, p, 1 << 30, None) == \
         lk.LOCKS_ERR_UNSUPPORTED
@@ -96,7 +98,7 @@ def test_host_validation_rejects_without_launch(lk):
         lk.LOCKS_ERR_WORKSPACE
     # too many pages for the selection kernel
     _, _, pt_big, _ = _fake(lk, MP=40000)
-    assert lib.locks_scan(p, 32, by(sm), by(pt_big), p, None, None) == lk.LOCKS_ERR_UNSUPPORTED
+    assert lib.locks_scan(p, 32, by(sm), by(pt_big), p, None, None, None) == lk.LOCKS_ERR_UNSUPPORTED
     # negative budget, bad dtype, mismatched build shapes
     assert lib.locks_select(p, 32, by(sm), by(pt), -1, p, p, p, p, 1 << 20, None) == \
         lk.LOCKS_ERR_INVALID_ARG

@@ -12,6 +12,21 @@ from workload.device import summaries_to_device
 
 pytestmark = pytest.mark.gpu
 
+RUN = 16  # pages per run maximum (LOCKS_RUN_PAGES)
+
+
+def host_run_max(pm, lens, P):
+    """Run maxima of fp32 masses [B][H][MP] over runs of RUN pages, counting
+    only full pages (j < lens[b] // P); -inf for runs without one."""
+    B, H, MP = pm.shape
+    nr = -(-MP // RUN)
+    out = np.full((B, H, nr), -np.inf, np.float32)
+    for b in range(B):
+        n = min(int(lens[b]) // P, MP)
+        for r in range(-(-n // RUN)):
+            out[b, :, r] = pm[b, :, r * RUN:min(n, (r + 1) * RUN)].max(axis=-1)
+    return out
+
 SCAN_CASES = [
     ("tiny-r4", lambda: tiny()),
     ("tiny-r16", lambda: tiny(rank=16)),
@@ -35,11 +50,14 @@ def test_scan_matches_oracle(name, mk):
     import kv_cache_page_rank_amd as lk
     pm = torch.full((s.batch, s.num_kv_heads, s.max_pages), 7.0, device=DEV)
     hm = torch.full((s.batch, s.num_q_heads, s.max_pages), 7.0, device=DEV)
+    rm = torch.full((s.batch, s.num_kv_heads, -(-s.max_pages // RUN)), 7.0, device=DEV)
     say("scan", name, s)
-    lk.locks_scan(case.q, summ, case.pages, pm, hm)
+    lk.locks_scan(case.q, summ, case.pages, pm, hm, run_max=rm)
     torch.cuda.synchronize()
     assert masses_close(to_np(pm), page_o) <= 1e-4
     assert masses_close(to_np(hm), head_o) <= 1e-4
+    # the run maxima are exactly the maxima of the written masses
+    np.testing.assert_array_equal(to_np(rm), host_run_max(to_np(pm), s.seq_lens, s.page_size))
 
 
 def test_scan_full_rank_is_exact_lse():
@@ -86,10 +104,12 @@ TOPK_CASES = [
 ]
 
 
+@pytest.mark.parametrize("runs", [False, True], ids=["all-masses", "run-maxima"])
 @pytest.mark.parametrize("case", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
-def test_topk_bit_exact(case):
+def test_topk_bit_exact(case, runs):
     """Integer work: identical fp32 inputs give identical page lists and
-    masses (ties to the lowest page index, ascending order, -1/-inf pads)."""
+    masses (ties to the lowest page index, ascending order, -1/-inf pads),
+    with and without the run maxima index."""
     name, B, H, MP, P, lens, budget, width, levels, ninf = case
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     pm, bt, sl = _topk_case(rng, B, H, MP, P, lens, levels, ninf)
@@ -99,11 +119,57 @@ def test_topk_bit_exact(case):
     pages = lk.PageTable(torch.from_numpy(bt).to(DEV), torch.from_numpy(sl).to(DEV))
     sel = torch.full((B, H, width), -7, dtype=torch.int32, device=DEV)
     mass = torch.full((B, H, width), 7.0, device=DEV)
-    say("topk", name)
-    lk.locks_topk(torch.from_numpy(pm).to(DEV), pages, P, budget, sel, mass)
+    rm = torch.from_numpy(host_run_max(pm, lens, P)).to(DEV) if runs else None
+    say("topk", name, "runs", runs)
+    lk.locks_topk(torch.from_numpy(pm).to(DEV), pages, P, budget, sel, mass, run_max=rm)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(sel.cpu().numpy(), sel_o)
     np.testing.assert_array_equal(mass.cpu().numpy(), mass_o)
+
+
+def _topk_against_oracle(pm, P, lens, budget, width, offset=0, tag="", runs=False):
+    """locks_topk on pm (placed `offset` floats into its device buffer) against
+    the oracle's selection, bit for bit."""
+    B, H, MP = pm.shape
+    bt = np.zeros((B, MP), np.int32)
+    sl = np.asarray(lens, np.int32)
+    lay = oracle.Layout(H, H, 64, P, bt, sl)
+    sel_o, mass_o = oracle.select_pool(lay, budget, pm, width)
+    import kv_cache_page_rank_amd as lk
+    pages = lk.PageTable(torch.from_numpy(bt).to(DEV), torch.from_numpy(sl).to(DEV))
+    buf = torch.zeros(pm.size + offset, device=DEV)
+    buf[offset:] = torch.from_numpy(pm.ravel()).to(DEV)
+    dev_pm = buf[offset:].view(B, H, MP)
+    sel = torch.full((B, H, width), -7, dtype=torch.int32, device=DEV)
+    mass = torch.full((B, H, width), 7.0, device=DEV)
+    rm = torch.from_numpy(host_run_max(pm, lens, P)).to(DEV) if runs else None
+    say("topk", tag, "offset", offset, "runs", runs)
+    lk.locks_topk(dev_pm, pages, P, budget, sel, mass, run_max=rm)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), sel_o)
+    np.testing.assert_array_equal(mass.cpu().numpy(), mass_o)
+
+
+@pytest.mark.parametrize("offset", [0, 1, 2])
+def test_topk_unaligned_rows(offset):
+    """Rows that do not start on a 16-byte boundary take the scalar-load
+    layout; the result must not depend on it."""
+    rng = np.random.default_rng(4242 + offset)
+    pm = rng.standard_normal((2, 2, 4096)).astype(np.float32)
+    _topk_against_oracle(pm, 64, [64 * 4096, 64 * 3001 + 9], 2048, 32, offset, "unaligned")
+
+
+@pytest.mark.parametrize("runs", [False, True], ids=["all-masses", "run-maxima"])
+@pytest.mark.parametrize("run", [64, 256, 1500])
+def test_topk_planted_run(run, runs):
+    """A run of consecutive pages sharing the top value: the candidates
+    above the bound crowd into few threads (one wave's share overflows for
+    the longer runs) and the k winners are the lowest pages of the run."""
+    rng = np.random.default_rng(run)
+    pm = rng.standard_normal((1, 2, 8192)).astype(np.float32)
+    pm[0, 0, 100:100 + run] = 9.0
+    pm[0, 1, 8192 - run:] = 9.0
+    _topk_against_oracle(pm, 64, [64 * 8192], 64 * 48, 48, 0, f"run{run}", runs)
 
 
 @pytest.mark.parametrize("mk", [lambda: tiny(), lambda: bf16_small(), lambda: bf16_small(rank=2)])
@@ -132,6 +198,30 @@ def test_select_end_to_end_band(mk):
             assert band_ok(sel_g[b, g], sel_o[b, g], page_o[b, g, :f], min(width, f)), (b, g)
             assert list(sel_g[b, g]) == sorted(sel_g[b, g][sel_g[b, g] >= 0]) + \
                 [-1] * int((sel_g[b, g] < 0).sum())
+
+
+@pytest.mark.parametrize("mk", [lambda: tiny(), lambda: bf16_small(), lambda: bf16_small(rank=2)])
+def test_select_equals_topk_of_its_masses(mk):
+    """locks_select (top-k through the run maxima in its workspace) picks
+    exactly what locks_topk over every mass picks from the same masses."""
+    case = Case(mk())
+    s = case.spec
+    summ = summaries_to_device(*case.oracle_summaries())
+    import kv_cache_page_rank_amd as lk
+    k = s.k_pages
+    ws = lk.workspace(lk.workspace_bytes(lk.OP_SELECT, s.batch, s.max_pages, s.num_q_heads,
+                                         s.num_kv_heads, s.page_size, s.head_dim, s.rank, k))
+    sel = torch.empty((s.batch, s.num_kv_heads, k), dtype=torch.int32, device=DEV)
+    mass = torch.empty((s.batch, s.num_kv_heads, k), device=DEV)
+    pm = torch.empty((s.batch, s.num_kv_heads, s.max_pages), device=DEV)
+    say("select vs topk", s)
+    lk.locks_select(case.q, summ, case.pages, s.budget_tokens, sel, mass, page_logmass=pm, ws=ws)
+    sel2 = torch.empty_like(sel)
+    mass2 = torch.empty_like(mass)
+    lk.locks_topk(pm, case.pages, s.page_size, s.budget_tokens, sel2, mass2)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2)
+    assert torch.equal(mass, mass2)
 
 
 def test_select_deterministic():
