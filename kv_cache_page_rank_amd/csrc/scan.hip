@@ -248,6 +248,11 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     x.j0 = jb * BATCH;
     const int c = x.c, w = x.w;
 
+    // The block-table entry of page j0 + c is read together with the
+    // sequence length (clamped index, kept only if the page is full), so the
+    // two loads overlap instead of following each other.
+    const int jc = x.j0 + (c < BATCH ? c : 0);
+    const int p_spec = a.block_table[(size_t)x.b * a.max_pages + (jc < a.max_pages ? jc : a.max_pages - 1)];
     int full = a.seq_lens[x.b] / P;
     full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
     x.out_page = a.page_logmass + ((size_t)x.b * x.Hkv + x.g) * a.max_pages;
@@ -263,12 +268,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
         }
         return;
     }
-
-    x.my_phys = -1;
-    if (c < BATCH && x.j0 + c < full) {
-        const int p = a.block_table[(size_t)x.b * a.max_pages + x.j0 + c];
-        x.my_phys = (p >= 0 && p < a.num_blocks) ? p : -1;
-    }
+    x.my_phys = (c < BATCH && x.j0 + c < full && p_spec >= 0 && p_spec < a.num_blocks) ? p_spec : -1;
 
     // Query fragment: q[h][16t + 4w + e] for head h = c, scaled to log2 units.
     const float qscale = kLog2e / sqrtf((float)D);
