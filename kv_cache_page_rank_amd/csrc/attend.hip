@@ -43,6 +43,18 @@ __device__ __forceinline__ SplitPages split_pages(const AttnParams& a, bool spar
     return r;
 }
 
+// Page of slot `slot` of the sparse list of (b, g): the selected pages
+// (slots < k_sel; -1 entries and pages that are not full are skipped), then
+// the partial last page (slot k_sel).  -1: nothing to attend.
+__device__ __forceinline__ int sparse_slot_page(const AttnParams& a, int b, int g, int slot,
+                                                int full, int n_all) {
+    if (slot < a.k_sel) {
+        const int j = a.sel_pages[((size_t)b * a.num_kv_heads + g) * a.k_sel + slot];
+        return (j >= 0 && j < full) ? j : -1;
+    }
+    return (slot == a.k_sel && n_all > full) ? full : -1;
+}
+
 // Combine the (m, l, o) partials of the 4 waves of a workgroup (4
 // consecutive splits of one (b, g)) into one partial, in wave order.
 // sm_o[w][h][d]; thread t combines head t/16, dims [8*(t%16), +8).
@@ -124,8 +136,19 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     int full = seq / P, n_all = (seq + P - 1) / P;
     full = full > a.max_pages ? a.max_pages : full;
     n_all = n_all > a.max_pages ? a.max_pages : n_all;
+    // dense: consecutive pages [first, first + count); sparse: slots
+    // [first, first + count) of the selected list (pages_per_split per wave)
     SplitPages sp{0, 0};
-    if (s < S) sp = split_pages(a, kSparse, b, g, s, full, n_all);
+    if (s < S) {
+        if constexpr (kSparse) {
+            const int slots = a.k_sel + 1;
+            const int lo = s * a.pages_per_split;
+            const int hi = lo + a.pages_per_split < slots ? lo + a.pages_per_split : slots;
+            sp = {lo, hi > lo ? hi - lo : 0};
+        } else {
+            sp = split_pages(a, false, b, g, s, full, n_all);
+        }
+    }
 
     // q fragment (log2 units), split into bf16 hi + lo: q[hq][32ks + 8w + e]
     bf16x8 qhi[KS], qlo[KS];
@@ -162,7 +185,11 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
 
     for (int pi = 0; pi < sp.count; ++pi) {
-        const int j = sp.first + pi;
+        int j = sp.first + pi;
+        if constexpr (kSparse) {
+            j = sparse_slot_page(a, b, g, j, full, n_all);
+            if (j < 0) continue;
+        }
         const int phys = bt[j];
         if (phys < 0 || phys >= a.num_blocks) continue;
         const int nv = seq - j * P < P ? seq - j * P : P;  // valid tokens of this page
@@ -577,17 +604,34 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnParams a) {
     }
 }
 
+// Sparse lists with at least this many (b, g, slot) pages run on the
+// wave-per-page kernel (bandwidth-bound batches); fewer run one workgroup
+// per page (latency-bound single sequences).
+constexpr long kSparseWavePages = 1024;
+
 template <int P, int D>
 hipError_t launch_pd(AttnParams p, hipStream_t s) {
     const bool sparse = p.sel_pages != nullptr;
     if (p.bf16) {
         if constexpr (P == 64) {
-            if (sparse) {  // one workgroup per selected page
+            const long slots = (long)p.k_sel + 1;
+            const long total = (long)p.batch * p.num_kv_heads * slots;
+            if (sparse && total < kSparseWavePages) {  // few pages: one workgroup per page
                 p.num_parts = p.num_splits;
                 const unsigned blocks = (unsigned)((long)p.batch * p.num_kv_heads * p.num_splits);
                 if (blocks > 0)
                     hipLaunchKernelGGL((attend_sparse_kernel<P, D>), dim3(blocks), dim3(256), 0, s,
                                        p);
+            } else if (sparse) {  // many pages: one wave per run of selected pages
+                long pps = total / 2048;  // ~2048 waves, one round at two waves per SIMD
+                pps = pps < 1 ? 1 : (pps > 16 ? 16 : pps);
+                p.pages_per_split = (int)pps;
+                p.num_splits = (int)((slots + pps - 1) / pps);
+                p.num_parts = (p.num_splits + 3) / 4;
+                const unsigned blocks = (unsigned)((long)p.batch * p.num_kv_heads * p.num_parts);
+                if (blocks > 0)
+                    hipLaunchKernelGGL((attend_mfma_kernel<P, D, true>), dim3(blocks), dim3(256),
+                                       0, s, p);
             } else {  // one wave per run of pages, 4 runs per workgroup
                 p.num_parts = (p.num_splits + 3) / 4;
                 const unsigned blocks = (unsigned)((long)p.batch * p.num_kv_heads * p.num_parts);

@@ -68,6 +68,14 @@ CASES = [
     ("bf16-G4", lambda: bf16_small(num_kv_heads=8), True),
     ("bf16-G1", lambda: bf16_small(num_q_heads=2), True),
     ("bf16-G16-d64", lambda: bf16_small(head_dim=64), True),
+    # many (sequence, KV head, page) items: the wave-per-run kernel (2 and 4 pages per wave)
+    ("bf16-batch16-G4-runs2", lambda: bf16_small(batch=16, num_kv_heads=8,
+                                                 seq_lens=[64 * 40 + (7 * i) % 64 for i in range(16)]),
+     True),
+    ("bf16-batch16-G4-k64-d64", lambda: bf16_small(batch=16, num_kv_heads=8, head_dim=64,
+                                                   budget_tokens=4096,
+                                                   seq_lens=[64 * (36 + i) + 5 * i for i in range(16)]),
+     True),
 ]
 
 

@@ -101,6 +101,9 @@ TOPK_CASES = [
     ("max-pages", 1, 2, 32768, 64, [64 * 32768], 4096, 64, 50, 0.0),
     ("empty-seq", 2, 1, 8, 64, [0, 63], 2048, 32, None, 0.0),
     ("wide-rows", 1, 1, 1500, 64, [64 * 1500], 2048, 40, None, 0.0),
+    ("batch-varied", 4, 2, 4000, 64, [64 * 500, 64 * 3999 + 7, 64 * 40, 64 * 1100], 2048, 32,
+     None, 0.0),
+    ("k64-few-runs", 2, 1, 600, 64, [64 * 600, 64 * 70], 64 * 64, 64, None, 0.0),
 ]
 
 
