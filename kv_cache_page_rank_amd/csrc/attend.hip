@@ -106,13 +106,168 @@ __device__ __forceinline__ void combine_waves(const AttnParams& a, float (*sm_m)
 // each lane's scores are exactly its 8 contraction elements of the value
 // product: score tile mt, A row m  <->  token 32*(mt/2) + 8*(m/4) + 4*(mt%2) + m%4,
 // and the value operand is 8 consecutive tokens of one V^T row (16 bytes).
+// K and V fragments of one page for one wave (32 KB in 64 VGPRs x 2).
+template <int P, int D>
+struct PageFrag {
+    static constexpr int KS = D / 32, MT = P / 16, KS2 = P / 32, MD = D / 16;
+    u32x4 k[MT][KS];
+    u32x4 v[KS2][MD];
+};
+
+template <int P, int D>
+__device__ __forceinline__ void load_page(const uint16_t* kp, const uint16_t* vp, int w, int c,
+                                          PageFrag<P, D>& f) {
+    using F = PageFrag<P, D>;
+#pragma unroll
+    for (int mt = 0; mt < F::MT; ++mt) {
+        const int tok = 32 * (mt >> 1) + 8 * (c >> 2) + 4 * (mt & 1) + (c & 3);
+#pragma unroll
+        for (int ks = 0; ks < F::KS; ++ks)
+            f.k[mt][ks] = *reinterpret_cast<const u32x4*>(kp + (size_t)tok * D + 32 * ks + 8 * w);
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < F::KS2; ++ks2)
+#pragma unroll
+        for (int md = 0; md < F::MD; ++md)
+            f.v[ks2][md] =
+                *reinterpret_cast<const u32x4*>(vp + (size_t)(16 * md + c) * P + 32 * ks2 + 8 * w);
+}
+
+// Online-softmax update of one wave's (m, l, O^T) with one page of nv valid
+// tokens (scores in log2 units).
+template <int P, int D>
+__device__ __forceinline__ void attend_page(const PageFrag<P, D>& f, int nv, int w,
+                                            const bf16x8* qhi, const bf16x8* qlo, float& m_run,
+                                            float& l_run, f32x4* acc) {
+    using F = PageFrag<P, D>;
+    f32x4 sc[F::MT];
+#pragma unroll
+    for (int mt = 0; mt < F::MT; ++mt) {
+        sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < F::KS; ++ks) {
+            const bf16x8 kf = as_bf16x8(f.k[mt][ks]);
+            sc[mt] = mfma_16x16x32_bf16(kf, qhi[ks], sc[mt]);
+            sc[mt] = mfma_16x16x32_bf16(kf, qlo[ks], sc[mt]);
+        }
+    }
+    // lane (w, c) element v of tile mt: token 32(mt/2) + 8w + 4(mt%2) + v, head c
+    if (nv < P) {
+#pragma unroll
+        for (int mt = 0; mt < F::MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tok = 32 * (mt >> 1) + 8 * w + 4 * (mt & 1) + v;
+                sc[mt][v] = tok < nv ? sc[mt][v] : -INFINITY;
+            }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < F::MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sc[mt][v]);
+    mx = max_over_rows(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new == -INFINITY) return;
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < F::MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            sc[mt][v] = fast_exp2(sc[mt][v] - m_new);
+            psum += sc[mt][v];
+        }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int md = 0; md < F::MD; ++md) acc[md] *= alpha;
+
+#pragma unroll
+    for (int ks2 = 0; ks2 < F::KS2; ++ks2) {
+        // p operand: slot e2 = 4e + v <-> token 32ks2 + 8w + e2 <-> tile 2ks2 + e, element v
+        u32x4 phi, plo;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const float p0 = sc[2 * ks2 + (e2 >> 1)][(2 * e2) & 3];
+            const float p1 = sc[2 * ks2 + (e2 >> 1)][(2 * e2 + 1) & 3];
+            uint16_t h0, l0, h1, l1;
+            split_bf16(p0, h0, l0);
+            split_bf16(p1, h1, l1);
+            phi[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            plo[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        const bf16x8 bhi = as_bf16x8(phi), blo = as_bf16x8(plo);
+#pragma unroll
+        for (int md = 0; md < F::MD; ++md) {
+            u32x4 vr = f.v[ks2][md];
+            if (nv < P) {  // zero values of absent tokens (their p is 0, their bits may be NaN)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int tok = 32 * ks2 + 8 * w + 2 * e2;
+                    vr[e2] &= (tok < nv ? 0x0000ffffu : 0u) | (tok + 1 < nv ? 0xffff0000u : 0u);
+                }
+            }
+            const bf16x8 vf = as_bf16x8(vr);
+            acc[md] = mfma_16x16x32_bf16(vf, bhi, acc[md]);
+            acc[md] = mfma_16x16x32_bf16(vf, blo, acc[md]);
+        }
+    }
+}
+
+// q fragment of head hq in log2 units, split into bf16 hi + lo:
+// q[hq][32ks + 8w + e] (zero for padding heads).
+template <int D>
+__device__ __forceinline__ void load_q_split(const AttnParams& a, int b, int hq, bool head_ok,
+                                             int w, bf16x8* qhi, bf16x8* qlo) {
+    const float qscale = kLog2e / sqrtf((float)D);
+    const float* qp = a.q + ((size_t)b * a.num_q_heads + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
+        u32x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v0 = head_ok ? (e < 2 ? x0[2 * e] : x1[2 * e - 4]) * qscale : 0.f;
+            const float v1 = head_ok ? (e < 2 ? x0[2 * e + 1] : x1[2 * e - 3]) * qscale : 0.f;
+            uint16_t h0, l0, h1, l1;
+            split_bf16(v0, h0, l0);
+            split_bf16(v1, h1, l1);
+            hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lo[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        qhi[ks] = as_bf16x8(hi);
+        qlo[ks] = as_bf16x8(lo);
+    }
+}
+
+// Writes the wave's (m, l, O^T) to LDS and combines the 4 waves.
+template <int D>
+__device__ __forceinline__ void finish_waves(const AttnParams& a, float (*sm_m)[16],
+                                             float (*sm_l)[16], float (*sm_o)[16][D + 4],
+                                             float m_run, float l_run, const f32x4* acc, int wv,
+                                             int w, int c, int b, int g, int G, int part,
+                                             int nparts) {
+    const float l_tot = sum_over_rows(l_run);
+    if (w == 0) {
+        sm_m[wv][c] = m_run;
+        sm_l[wv][c] = l_tot;
+    }
+    // lane (w, c) element v of tile md: O^T[16md + 4w + v][c]
+#pragma unroll
+    for (int md = 0; md < D / 16; ++md)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm_o[wv][c][16 * md + 4 * w + v] = acc[md][v];
+    __syncthreads();
+    combine_waves<D>(a, sm_m, sm_l, sm_o, b, g, G, part, nparts);
+}
+
 template <int P, int D, bool kSparse>
 __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     static_assert(P == 64 && D % 32 == 0, "bf16 path: 64-token pages");
-    constexpr int KS = D / 32;   // K-steps of the score product
-    constexpr int MT = P / 16;   // score tiles (16 tokens each)
-    constexpr int KS2 = P / 32;  // K-steps of the value product
-    constexpr int MD = D / 16;   // output tiles (16 dims each)
+    constexpr int KS = D / 32;
+    constexpr int MD = D / 16;
     __shared__ float sm_m[4][16], sm_l[4][16];
     __shared__ float sm_o[4][16][D + 4];
 
@@ -150,30 +305,8 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
         }
     }
 
-    // q fragment (log2 units), split into bf16 hi + lo: q[hq][32ks + 8w + e]
     bf16x8 qhi[KS], qlo[KS];
-    {
-        const float qscale = kLog2e / sqrtf((float)D);
-        const float* qp = a.q + ((size_t)b * a.num_q_heads + hq) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
-            u32x4 hi, lo;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v0 = head_ok ? (e < 2 ? x0[2 * e] : x1[2 * e - 4]) * qscale : 0.f;
-                const float v1 = head_ok ? (e < 2 ? x0[2 * e + 1] : x1[2 * e - 3]) * qscale : 0.f;
-                uint16_t h0, l0, h1, l1;
-                split_bf16(v0, h0, l0);
-                split_bf16(v1, h1, l1);
-                hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                lo[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-            }
-            qhi[ks] = as_bf16x8(hi);
-            qlo[ks] = as_bf16x8(lo);
-        }
-    }
+    load_q_split<D>(a, b, hq, head_ok, w, qhi, qlo);
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[MD];
@@ -193,112 +326,12 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
         const int phys = bt[j];
         if (phys < 0 || phys >= a.num_blocks) continue;
         const int nv = seq - j * P < P ? seq - j * P : P;  // valid tokens of this page
-        const uint16_t* kp = kpool + ((size_t)phys * Hkv + g) * P * D;
-        const uint16_t* vp = vpool + ((size_t)phys * Hkv + g) * D * P;
-
-        u32x4 kraw[MT][KS], vraw[KS2][MD];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int tok = 32 * (mt >> 1) + 8 * (c >> 2) + 4 * (mt & 1) + (c & 3);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kraw[mt][ks] =
-                    *reinterpret_cast<const u32x4*>(kp + (size_t)tok * D + 32 * ks + 8 * w);
-        }
-#pragma unroll
-        for (int ks2 = 0; ks2 < KS2; ++ks2)
-#pragma unroll
-            for (int md = 0; md < MD; ++md)
-                vraw[ks2][md] = *reinterpret_cast<const u32x4*>(vp + (size_t)(16 * md + c) * P +
-                                                                32 * ks2 + 8 * w);
-
-        f32x4 sc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 kf = as_bf16x8(kraw[mt][ks]);
-                sc[mt] = mfma_16x16x32_bf16(kf, qhi[ks], sc[mt]);
-                sc[mt] = mfma_16x16x32_bf16(kf, qlo[ks], sc[mt]);
-            }
-        }
-        // lane (w, c) element v of tile mt: token 32(mt/2) + 8w + 4(mt%2) + v, head c
-        if (nv < P) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int tok = 32 * (mt >> 1) + 8 * w + 4 * (mt & 1) + v;
-                    sc[mt][v] = tok < nv ? sc[mt][v] : -INFINITY;
-                }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sc[mt][v]);
-        mx = max_over_rows(mx);
-        const float m_new = fmaxf(m_run, mx);
-        if (m_new == -INFINITY) continue;
-        const float alpha = fast_exp2(m_run - m_new);
-        float psum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                sc[mt][v] = fast_exp2(sc[mt][v] - m_new);
-                psum += sc[mt][v];
-            }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) acc[md] *= alpha;
-
-#pragma unroll
-        for (int ks2 = 0; ks2 < KS2; ++ks2) {
-            // p operand: slot e2 = 4e + v <-> token 32ks2 + 8w + e2 <-> tile 2ks2 + e, element v
-            u32x4 phi, plo;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const float p0 = sc[2 * ks2 + (e2 >> 1)][(2 * e2) & 3];
-                const float p1 = sc[2 * ks2 + (e2 >> 1)][(2 * e2 + 1) & 3];
-                uint16_t h0, l0, h1, l1;
-                split_bf16(p0, h0, l0);
-                split_bf16(p1, h1, l1);
-                phi[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                plo[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-            }
-            const bf16x8 bhi = as_bf16x8(phi), blo = as_bf16x8(plo);
-#pragma unroll
-            for (int md = 0; md < MD; ++md) {
-                u32x4 vr = vraw[ks2][md];
-                if (nv < P) {  // zero values of absent tokens (their p is 0, their bits may be NaN)
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        const int tok = 32 * ks2 + 8 * w + 2 * e2;
-                        vr[e2] &= (tok < nv ? 0x0000ffffu : 0u) | (tok + 1 < nv ? 0xffff0000u : 0u);
-                    }
-                }
-                const bf16x8 vf = as_bf16x8(vr);
-                acc[md] = mfma_16x16x32_bf16(vf, bhi, acc[md]);
-                acc[md] = mfma_16x16x32_bf16(vf, blo, acc[md]);
-            }
-        }
+        PageFrag<P, D> f;
+        load_page<P, D>(kpool + ((size_t)phys * Hkv + g) * P * D,
+                        vpool + ((size_t)phys * Hkv + g) * D * P, w, c, f);
+        attend_page<P, D>(f, nv, w, qhi, qlo, m_run, l_run, acc);
     }
-
-    const float l_tot = sum_over_rows(l_run);
-    if (w == 0) {
-        sm_m[wv][c] = m_run;
-        sm_l[wv][c] = l_tot;
-    }
-    // lane (w, c) element v of tile md: O^T[16md + 4w + v][c]
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sm_o[wv][c][16 * md + 4 * w + v] = acc[md][v];
-    __syncthreads();
-    combine_waves<D>(a, sm_m, sm_l, sm_o, b, g, G, part, NPART);
+    finish_waves<D>(a, sm_m, sm_l, sm_o, m_run, l_run, acc, wv, w, c, b, g, G, part, NPART);
 }
 
 // Sparse path (bf16, latency-bound at small batch): one workgroup per split
@@ -623,7 +656,9 @@ hipError_t launch_pd(AttnParams p, hipStream_t s) {
                     hipLaunchKernelGGL((attend_sparse_kernel<P, D>), dim3(blocks), dim3(256), 0, s,
                                        p);
             } else if (sparse) {  // many pages: one wave per run of selected pages
-                long pps = total / 2048;  // ~2048 waves, one round at two waves per SIMD
+                // ~1024 waves (one per SIMD), each walking its run of pages: measured
+                // faster than more, shorter runs at two waves per SIMD
+                long pps = (total + 1023) / 1024;
                 pps = pps < 1 ? 1 : (pps > 16 ? 16 : pps);
                 p.pages_per_split = (int)pps;
                 p.num_splits = (int)((slots + pps - 1) / pps);
