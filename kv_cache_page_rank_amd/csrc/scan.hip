@@ -22,12 +22,18 @@
 // row per load instruction).
 // When asked, the wave also writes the largest page mass of its 16 pages
 // (the run maximum the top-k uses to skip runs that cannot hold a winner).
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace locks {
 
 namespace {
+
+constexpr int kBatch = kRunPages;  // pages per wave (one run)
+constexpr int kPrefetch = 1;       // basis tiles in flight ahead of the one computed
+constexpr int kChains = 4;         // independent accumulator chains of the d contraction
 
 // State of one wave's batch, shared by the two specialisations below.
 template <int D>
@@ -39,19 +45,31 @@ struct WaveCtx {
     float qf[D / 4];
 };
 
-// One wave's batch of BATCH pages.  kMasked: some page of the batch is
+// Load of T at element offset `off` of `base`.  kOff32: every summary array
+// is below 4 GiB, so the byte offset is a 32-bit value added to the uniform
+// base (one VALU op per address instead of 64-bit arithmetic).
+template <typename T, bool kOff32>
+__device__ __forceinline__ T load_at(const float* base, size_t off) {
+    if constexpr (kOff32)
+        return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) +
+                                           (uint32_t)((uint32_t)off * 4u));
+    else
+        return *reinterpret_cast<const T*>(base + off);
+}
+
+// One wave's batch of kBatch pages.  kMasked: some page of the batch is
 // absent or the rank is padded, so loads are zeroed per row; otherwise no
-// masking code is emitted.  kPipe: the basis product of tile tt+1 is issued
-// before the log-sum-exp of tile tt so the matrix core and the vector unit
-// overlap inside the wave.
-template <int P, int D, int RR, bool kExact, int BATCH, int PF, int NACC, bool kMasked, bool kPipe>
+// masking code is emitted.  kHeads: per-head masses are written too.
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
 __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>& x) {
-    constexpr int PPT = 16 / RR;         // pages per basis tile (16 rows = PPT pages x RR rows)
-    constexpr int NTILE = BATCH / PPT;   // basis tiles per batch
-    constexpr int KS2 = RR / 4;          // K-steps of the coefficient product
-    constexpr int MT = P / 16;           // token tiles per page
-    constexpr int DS = D / 4;            // K-steps of the d contraction
-    constexpr int DT = D / 16;           // 16-byte loads per row slice
+    constexpr int PPT = 16 / RR;          // pages per basis tile (16 rows = PPT pages x RR rows)
+    constexpr int NTILE = kBatch / PPT;   // basis tiles per batch
+    constexpr int KS2 = RR / 4;           // K-steps of the coefficient product
+    constexpr int MT = P / 16;            // token tiles per page
+    constexpr int DS = D / 4;             // K-steps of the d contraction
+    constexpr int DT = D / 16;            // 16-byte loads per row slice
+    constexpr int PF = kPrefetch, NACC = kChains;
+    using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
     const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
     const int my_phys = x.my_phys;
     auto phys_at = [&](int pb) { return __shfl(my_phys, pb, kWave); };
@@ -69,16 +87,16 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
         float cf[PPT][MT][KS2];
     };
     // Loads are unconditional (absent rows read a clamped, valid address and
-    // are zeroed afterwards) so that the next tiles' loads stay in flight
+    // are zeroed afterwards) so that the next tile's loads stay in flight
     // while the current tile is computed.
     auto load_tile = [&](int tt, Tile& T) {
         const int pj = phys_at(tt * PPT + a_pin);
         const bool row_ok = !kMasked || (pj >= 0 && a_kk < r);
-        const float* src = a.basis + (((size_t)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
-                                      (kMasked && a_kk >= r ? r - 1 : a_kk)) * D;
+        const Off src = (((Off)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
+                         (kMasked && a_kk >= r ? r - 1 : a_kk)) * D + 4 * w;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(src + 16 * t + 4 * w);
+            const f32x4 v = load_at<f32x4, kOff32>(a.basis, src + 16 * t);
 #pragma unroll
             for (int e = 0; e < 4; ++e) T.v[4 * t + e] = row_ok ? v[e] : 0.0f;
         }
@@ -86,20 +104,20 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
         for (int p = 0; p < PPT; ++p) {
             const int pp = phys_uniform(tt * PPT + p);
             const bool ok = !kMasked || pp >= 0;
-            const float* csrc = a.coef + ((size_t)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
+            const Off csrc = ((Off)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const float* row = csrc + (size_t)(16 * mt + c) * r;
+                const Off row = csrc + (Off)(16 * mt + c) * r;
                 if constexpr (kExact) {
                     if constexpr (KS2 == 1) {
-                        const float v = row[w];
+                        const float v = load_at<float, kOff32>(a.coef, row + w);
                         T.cf[p][mt][0] = ok ? v : 0.0f;
                     } else if constexpr (KS2 == 2) {
-                        const f32x2 v = *reinterpret_cast<const f32x2*>(row + 2 * w);
+                        const f32x2 v = load_at<f32x2, kOff32>(a.coef, row + 2 * w);
                         T.cf[p][mt][0] = ok ? v[0] : 0.0f;
                         T.cf[p][mt][1] = ok ? v[1] : 0.0f;
                     } else {
-                        const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * w);
+                        const f32x4 v = load_at<f32x4, kOff32>(a.coef, row + 4 * w);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) T.cf[p][mt][e] = ok ? v[e] : 0.0f;
                     }
@@ -107,7 +125,7 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
 #pragma unroll
                     for (int ks = 0; ks < KS2; ++ks) {
                         const int kk = KS2 * w + ks;
-                        const float v = row[kk < r ? kk : r - 1];
+                        const float v = load_at<float, kOff32>(a.coef, row + (kk < r ? kk : r - 1));
                         T.cf[p][mt][ks] = (ok && kk < r) ? v : 0.0f;
                     }
                 }
@@ -136,11 +154,11 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
     // beta tile: A row m = page j0 + m (lane column c supplies row c).
     f32x4 beta;
     {
-        const float* src = a.mu + ((size_t)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D;
+        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + 4 * w;
         float mv[DS];
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(src + 16 * t + 4 * w);
+            const f32x4 v = load_at<f32x4, kOff32>(a.mu, src + 16 * t);
 #pragma unroll
             for (int e = 0; e < 4; ++e) mv[4 * t + e] = (!kMasked || my_phys >= 0) ? v[e] : 0.0f;
         }
@@ -156,13 +174,11 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
     // lane (w, c) now holds beta[page j0 + 4w + v][head c] in element v.
 
     float run_mx = -INFINITY;  // max of the written page masses (row w holds pages 4w..4w+3)
-    f32x4 Tcur;
-    if constexpr (kPipe) Tcur = basis_product(ring[0]);
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
         if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
         const Tile& cur = ring[tt % (PF + 1)];
-        if constexpr (!kPipe) Tcur = basis_product(cur);
+        const f32x4 Tcur = basis_product(cur);
 
         f32x4 L[PPT][MT];
 #pragma unroll
@@ -174,9 +190,6 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
                 for (int ks = 0; ks < KS2; ++ks)
                     L[p][mt] = mfma_16x16x4_f32(cur.cf[p][mt][ks], Tcur[p * KS2 + ks], L[p][mt]);
             }
-        if constexpr (kPipe) {
-            if (tt + 1 < NTILE) Tcur = basis_product(ring[(tt + 1) % (PF + 1)]);
-        }
 
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
@@ -195,40 +208,43 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
 #pragma unroll
                 for (int v = 0; v < 4; ++v) sum += fast_exp2(L[p][mt][v] - mx);
             sum = sum_over_rows(sum);
-            // per-head estimate; beta of page pb sits in row pb/4, element pb%4
-            const float s2 = mx + fast_log2(sum) + beta[pb & 3];
-            const float xv = x.head_ok ? s2 : -INFINITY;
-            const float gm = max_in_row(xv);
-            const float gs = sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f);
-            const float a2 = gm + fast_log2(gs);
+            // head h's mass is sum * 2^(mx + beta); beta of page pb sits in row
+            // pb/4, element pb%4, so only that row's values are right
+            const float top = mx + beta[pb & 3];
+            float a2, s2 = 0.0f;
+            if constexpr (kHeads) {
+                s2 = top + fast_log2(sum);
+                const float xv = x.head_ok ? s2 : -INFINITY;
+                const float gm = max_in_row(xv);
+                a2 = gm + fast_log2(sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f));
+            } else {  // the group sum without each head's log: sum_h sum_h 2^(top_h - max top)
+                const float gm = max_in_row(x.head_ok ? top : -INFINITY);
+                a2 = gm + fast_log2(sum_in_row(x.head_ok ? sum * fast_exp2(top - gm) : 0.0f));
+            }
             if (w == (pb >> 2) && j < a.max_pages) {
                 const bool ok = !kMasked || phys_uniform(pb) >= 0;
                 const float mass = ok ? a2 * kLn2 : -INFINITY;
                 run_mx = fmaxf(run_mx, mass);
                 if (c == 0) x.out_page[j] = mass;
-                if (a.head_logmass && x.head_ok)
-                    a.head_logmass[((size_t)x.b * a.num_q_heads + g * x.G + c) * a.max_pages + j] =
-                        ok ? s2 * kLn2 : -INFINITY;
+                if constexpr (kHeads) {
+                    if (x.head_ok)
+                        a.head_logmass[((size_t)x.b * a.num_q_heads + g * x.G + c) * a.max_pages +
+                                       j] = ok ? s2 * kLn2 : -INFINITY;
+                }
             }
         }
     }
     if (a.run_max) {
         run_mx = max_over_rows(run_mx);
         const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
-        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / BATCH] = run_mx;
+        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
     }
 }
 
-// Tuning: BATCH pages per wave (one run of pages), PF tiles prefetched ahead, NACC
-// independent accumulator chains for the d contraction, kPipe software
-// pipelining of the tile loop.
-template <int P, int D, int RR, bool kExact, int BATCH = 16, int PF = 2, int NACC = 2,
-          bool kPipe = false>
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32>
 __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     static_assert(P % 16 == 0 && D % 16 == 0, "P and d must be multiples of 16");
     static_assert(RR == 4 || RR == 8 || RR == 16, "padded rank");
-    static_assert(BATCH == kRunPages, "one wave per run of pages");
-    constexpr int DS = D / 4;
     constexpr int DT = D / 16;
 
     WaveCtx<D> x;
@@ -236,7 +252,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     x.w = x.lane >> 4;
     x.c = x.lane & 15;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int nbatch = (a.max_pages + BATCH - 1) / BATCH;
+    const int nbatch = (a.max_pages + kBatch - 1) / kBatch;
     if (wave >= a.batch * a.num_kv_heads * nbatch) return;
     const int jb = wave % nbatch;
     x.g = (wave / nbatch) % a.num_kv_heads;
@@ -245,30 +261,32 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     x.G = a.num_q_heads / x.Hkv;
     x.r = a.rank;
     x.head_ok = x.c < x.G;
-    x.j0 = jb * BATCH;
+    x.j0 = jb * kBatch;
     const int c = x.c, w = x.w;
 
     // The block-table entry of page j0 + c is read together with the
     // sequence length (clamped index, kept only if the page is full), so the
     // two loads overlap instead of following each other.
-    const int jc = x.j0 + (c < BATCH ? c : 0);
-    const int p_spec = a.block_table[(size_t)x.b * a.max_pages + (jc < a.max_pages ? jc : a.max_pages - 1)];
+    const int jc = x.j0 + (c < kBatch ? c : 0);
+    const int p_spec =
+        a.block_table[(size_t)x.b * a.max_pages + (jc < a.max_pages ? jc : a.max_pages - 1)];
     int full = a.seq_lens[x.b] / P;
     full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
     x.out_page = a.page_logmass + ((size_t)x.b * x.Hkv + x.g) * a.max_pages;
     if (x.j0 >= full) {  // whole batch past the full pages
         if (a.run_max && x.lane == 0)
             a.run_max[((size_t)x.b * x.Hkv + x.g) * nbatch + jb] = -INFINITY;
-        if (w == 0 && c < BATCH && x.j0 + c < a.max_pages) {
+        if (w == 0 && c < kBatch && x.j0 + c < a.max_pages) {
             x.out_page[x.j0 + c] = -INFINITY;
-            if (a.head_logmass)
+            if constexpr (kHeads)
                 for (int hh = 0; hh < x.G; ++hh)
                     a.head_logmass[((size_t)x.b * a.num_q_heads + x.g * x.G + hh) * a.max_pages +
                                    x.j0 + c] = -INFINITY;
         }
         return;
     }
-    x.my_phys = (c < BATCH && x.j0 + c < full && p_spec >= 0 && p_spec < a.num_blocks) ? p_spec : -1;
+    x.my_phys =
+        (c < kBatch && x.j0 + c < full && p_spec >= 0 && p_spec < a.num_blocks) ? p_spec : -1;
 
     // Query fragment: q[h][16t + 4w + e] for head h = c, scaled to log2 units.
     const float qscale = kLog2e / sqrtf((float)D);
@@ -282,30 +300,42 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
             for (int e = 0; e < 4; ++e) x.qf[4 * t + e] = x.head_ok ? v[e] * qscale : 0.0f;
         }
     }
-    (void)DS;
 
     // every page of the batch present and the rank not padded: no masking
     if constexpr (kExact) {
-        if (x.j0 + BATCH <= full && __ballot(c < BATCH && x.my_phys < 0) == 0ull) {
-            scan_batch<P, D, RR, kExact, BATCH, PF, NACC, false, kPipe>(a, x);
+        if (x.j0 + kBatch <= full && __ballot(c < kBatch && x.my_phys < 0) == 0ull) {
+            scan_batch<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
             return;
         }
     }
-    scan_batch<P, D, RR, kExact, BATCH, PF, NACC, true, kPipe>(a, x);
+    scan_batch<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
 }
 
-template <int P, int D, int RR, int BATCH = 16, int PF = 1, int NACC = 4, bool kPipe = false>
+template <int P, int D, int RR, bool kHeads, bool kOff32>
+hipError_t launch4(const ScanParams& p, hipStream_t s, unsigned blocks) {
+    if (p.rank == RR)
+        hipLaunchKernelGGL((scan_kernel<P, D, RR, true, kHeads, kOff32>), dim3(blocks), dim3(256),
+                           0, s, p);
+    else
+        hipLaunchKernelGGL((scan_kernel<P, D, RR, false, kHeads, kOff32>), dim3(blocks), dim3(256),
+                           0, s, p);
+    return hipGetLastError();
+}
+
+template <int P, int D, int RR>
 hipError_t launch(const ScanParams& p, hipStream_t s) {
-    const long waves = (long)p.batch * p.num_kv_heads * ((p.max_pages + BATCH - 1) / BATCH);
+    const long waves = (long)p.batch * p.num_kv_heads * ((p.max_pages + kBatch - 1) / kBatch);
     const unsigned blocks = (unsigned)((waves + 3) / 4);
     if (blocks == 0) return hipSuccess;
-    if (p.rank == RR)
-        hipLaunchKernelGGL((scan_kernel<P, D, RR, true, BATCH, PF, NACC, kPipe>), dim3(blocks),
-                           dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((scan_kernel<P, D, RR, false, BATCH, PF, NACC, kPipe>), dim3(blocks),
-                           dim3(256), 0, s, p);
-    return hipGetLastError();
+    // largest summary array (basis or coefficients) in bytes
+    const size_t per_unit = (size_t)p.rank * (D > P ? D : P) * sizeof(float);
+    const bool off32 = (size_t)p.num_blocks * p.num_kv_heads * per_unit < (size_t(1) << 32);
+    const bool heads = p.head_logmass != nullptr;
+    if (heads)
+        return off32 ? launch4<P, D, RR, true, true>(p, s, blocks)
+                     : launch4<P, D, RR, true, false>(p, s, blocks);
+    return off32 ? launch4<P, D, RR, false, true>(p, s, blocks)
+                 : launch4<P, D, RR, false, false>(p, s, blocks);
 }
 
 template <int P, int D>
