@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--budget", type=int, default=0, help="override the token budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-bf16-summaries", action="store_true",
+                    help="skip the extra measurement of the step with bf16 summaries")
     ap.add_argument("--cpu-target-s", type=float, default=12.0,
                     help="approximate CPU seconds spent on the oracle sample")
     ap.add_argument("--threads", type=int, default=0)
@@ -240,6 +242,37 @@ def main():
     step_b = traffic.step_bytes(full_total, partial, Hkv, d, P, r, B * Hkv * k)
     log(f"select (scan+topk): {sel_mean:.2f} us, sparse attend+merge: {sparse_mean:.2f} us")
 
+    # --- the same step with bf16 summaries (reported beside the fp32 headline)
+    bf16_summ = None
+    if not args.no_bf16_summaries:
+        summs16 = [lk.Summaries.empty(NB, Hkv, P, d, r, dtype=torch.bfloat16) for _ in range(L)]
+        for i in range(L):
+            lk.locks_build_summaries(kvs[i], pages, summs16[i])
+        g16 = [lk.StepGraph(q, summs16[i], kvs[i], pages, spec.budget_tokens, *bufs[i][:4],
+                            ws=bufs[i][4]) for i in range(L)]
+        for i in range(args.warmup):
+            g16[i % L].launch()
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            g16[i % L].launch()
+        e1.record()
+        torch.cuda.synchronize()
+        step16 = e0.elapsed_time(e1) * 1e3 / args.steps
+        for i in range(args.warmup):
+            lk.locks_scan(q, summs16[i % L], pages, pms[i % L])
+        scan16, _, _ = time_events(
+            lambda i: lk.locks_scan(q, summs16[i % L], pages, pms[i % L]), args.steps, torch)
+        scan16_b = traffic.scan_bytes(B, Hq, Hkv, MP, full_total, d, P, r, summary_elem=2)
+        gbs16 = scan16_b / (scan16 * 1e-6) / 1e9
+        bf16_summ = {"step_us": round(step16, 3), "scan_us": round(scan16, 3),
+                     "scan_bytes_per_launch": scan16_b, "scan_GBps": round(gbs16, 1),
+                     "scan_frac": round(gbs16 / HBM_PEAK_GBS, 4),
+                     "summary_to_cache_ratio": round(traffic.summary_to_cache_ratio(d, P, r, 2), 4)}
+        for g in g16:
+            g.close()
+        log(f"bf16 summaries: step {step16:.2f} us, scan {scan16:.2f} us, {gbs16:.0f} GB/s")
+
     # --- dense baseline
     dense_mean = None
     dense_b = traffic.dense_bytes(sum(-(-n // P) for n in spec.seq_lens), Hkv, d, P)
@@ -300,6 +333,7 @@ def main():
             "summary_to_cache_ratio": round(ratio, 4),
             "build_ms": round(build_ms, 3),
             "build_pages_per_s": round(full_total * Hkv / (build_ms * 1e-3), 1),
+            "bf16_summaries": bf16_summ,
         },
     }
     for g in graphs:

@@ -102,16 +102,21 @@ typedef struct {
     const void* v; /* [NB][H_kv][d][P] */
 } locks_kv_cache;
 
-/* Resident summaries of one layer, stored by physical block. */
+/* Resident summaries of one layer, stored by physical block.  dtype
+ * LOCKS_F32, or LOCKS_BF16: each value is the fp32 summary rounded to the
+ * nearest bf16 (ties to even), half the bytes for the scan to read
+ * (technical summary, section 2, Kwantisatie: the pages store the summary
+ * at reduced precision; bf16 is the first step, integer codes are not built). */
 typedef struct {
+    int32_t dtype; /* locks_dtype of mu, basis and coef */
     int32_t num_blocks;
     int32_t num_kv_heads;
     int32_t page_size;
     int32_t head_dim;
     int32_t rank;
-    float* mu;    /* [NB][H_kv][d] */
-    float* basis; /* [NB][H_kv][r][d] */
-    float* coef;  /* [NB][H_kv][P][r] */
+    void* mu;    /* [NB][H_kv][d] */
+    void* basis; /* [NB][H_kv][r][d] */
+    void* coef;  /* [NB][H_kv][P][r] */
 } locks_summaries;
 
 /* Block table of a batch of sequences. */
@@ -139,7 +144,8 @@ size_t locks_workspace_bytes(int32_t op, int32_t batch, int32_t max_pages, int32
  * basis_k = Kc^T u_k / sqrt(lambda_k); coef[i][k] = sqrt(lambda_k) u_k[i].
  * Eigenvalues below 3e-5 * lambda_max give zero basis/coef (numerically null).
  * page_begin: device [B] or NULL (= all full pages).  Summaries of other
- * blocks are left untouched.  summaries->rank is r.  Needs no workspace
+ * blocks are left untouched.  summaries->rank is r.  Computed in fp32 and
+ * stored in out->dtype (bf16: rounded to nearest even).  Needs no workspace
  * (ws may be NULL).
  */
 locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page_table* pages,

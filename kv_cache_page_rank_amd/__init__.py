@@ -44,7 +44,8 @@ class CKVCache(ctypes.Structure):
 
 
 class CSummaries(ctypes.Structure):
-    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+    _fields_ = [("dtype", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("mu", ctypes.c_void_p), ("basis", ctypes.c_void_p),
                 ("coef", ctypes.c_void_p)]
@@ -155,8 +156,9 @@ class Summaries:
     coef: torch.Tensor   # [NB][H_kv][P][r]
 
     @staticmethod
-    def empty(num_blocks, num_kv_heads, page_size, head_dim, rank, device="cuda"):
-        f = dict(dtype=torch.float32, device=device)
+    def empty(num_blocks, num_kv_heads, page_size, head_dim, rank, device="cuda",
+              dtype=torch.float32):
+        f = dict(dtype=dtype, device=device)
         return Summaries(torch.empty(num_blocks, num_kv_heads, head_dim, **f),
                          torch.empty(num_blocks, num_kv_heads, rank, head_dim, **f),
                          torch.empty(num_blocks, num_kv_heads, page_size, rank, **f))
@@ -164,10 +166,12 @@ class Summaries:
     def c(self) -> CSummaries:
         NB, H, r, d = self.basis.shape
         P = self.coef.shape[2]
+        dt = self.mu.dtype
+        assert dt in (torch.float32, torch.bfloat16)
         for t in (self.mu, self.basis, self.coef):
-            assert t.dtype == torch.float32 and t.is_contiguous()
-        return CSummaries(NB, H, P, d, r, self.mu.data_ptr(), self.basis.data_ptr(),
-                          self.coef.data_ptr())
+            assert t.dtype == dt and t.is_contiguous()
+        return CSummaries(LOCKS_BF16 if dt == torch.bfloat16 else LOCKS_F32, NB, H, P, d, r,
+                          self.mu.data_ptr(), self.basis.data_ptr(), self.coef.data_ptr())
 
 
 def workspace_bytes(op, batch, max_pages, num_q_heads, num_kv_heads, page_size, head_dim, rank,

@@ -36,6 +36,7 @@ locks_status check_summaries(const locks_summaries* s, bool need_data) {
     if (!s || s->num_blocks <= 0 || s->num_kv_heads <= 0 || s->page_size <= 0 ||
         s->head_dim <= 0 || s->rank <= 0)
         return LOCKS_ERR_INVALID_ARG;
+    if (s->dtype != LOCKS_F32 && s->dtype != LOCKS_BF16) return LOCKS_ERR_INVALID_ARG;
     if (need_data && (!s->mu || !s->basis || !s->coef)) return LOCKS_ERR_INVALID_ARG;
     if (!locks::scan_supported(s->page_size, s->head_dim, s->rank)) return LOCKS_ERR_UNSUPPORTED;
     return LOCKS_OK;
@@ -121,6 +122,7 @@ locks_status scan_common(const float* q, int32_t hq, const locks_summaries* s,
     p.mu = s->mu;
     p.basis = s->basis;
     p.coef = s->coef;
+    p.summ_bf16 = s->dtype == LOCKS_BF16;
     p.block_table = pt->block_table;
     p.seq_lens = pt->seq_lens;
     p.batch = pt->batch;
@@ -220,6 +222,7 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
     p.mu = out->mu;
     p.basis = out->basis;
     p.coef = out->coef;
+    p.out_bf16 = out->dtype == LOCKS_BF16;
     const hipError_t e = locks::launch_build(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LOCKS_OK : hip_fail(e);
 }
@@ -387,6 +390,6 @@ const char* locks_status_string(int32_t status) {
 
 int32_t locks_last_hip_error(void) { return g_last_hip_error; }
 
-int32_t locks_version(void) { return 101; }
+int32_t locks_version(void) { return 102; }
 
 }  // extern "C"

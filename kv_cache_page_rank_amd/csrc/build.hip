@@ -250,17 +250,22 @@ __global__ __launch_bounds__(256) void build_kernel(const BuildParams a) {
         }
     }
     __syncthreads();
-    // outputs: centroid, basis, coefficients = coordinates Kc V^T
-    float* mu_out = a.mu + unit * D;
-    float* basis_out = a.basis + unit * (size_t)r * D;
-    float* coef_out = a.coef + unit * (size_t)P * r;
-    for (int d = t; d < D; d += 256) mu_out[d] = mu_s[d];
-    for (int i = t; i < r * D; i += 256) basis_out[i] = vs[i / D][i % D];
+    // outputs: centroid, basis, coefficients = coordinates Kc V^T, stored as
+    // fp32 or rounded to bf16 (nearest even)
+    auto put = [&](void* base, size_t idx, float v) {
+        if (a.out_bf16)
+            static_cast<uint16_t*>(base)[idx] = f32_to_bf16_bits(v);
+        else
+            static_cast<float*>(base)[idx] = v;
+    };
+    const size_t mu0 = unit * D, basis0 = unit * (size_t)r * D, coef0 = unit * (size_t)P * r;
+    for (int d = t; d < D; d += 256) put(a.mu, mu0 + d, mu_s[d]);
+    for (int i = t; i < r * D; i += 256) put(a.basis, basis0 + i, vs[i / D][i % D]);
     for (int i = t; i < P * r; i += 256) {
         const int tok = i / r, k = i % r;
         float s = 0.f;
         for (int d = 0; d < D; ++d) s += kc[tok][d] * vs[k][d];
-        coef_out[i] = s;
+        put(a.coef, coef0 + i, s);
     }
 }
 

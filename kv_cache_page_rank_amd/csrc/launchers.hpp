@@ -15,9 +15,10 @@ constexpr int kRunPages = 16;
 
 struct ScanParams {
     const float* q;        // [B][Hq][D]
-    const float* mu;       // [NB][Hkv][D]
-    const float* basis;    // [NB][Hkv][r][D]
-    const float* coef;     // [NB][Hkv][P][r]
+    const void* mu;        // [NB][Hkv][D]       fp32 or bf16 (summ_bf16)
+    const void* basis;     // [NB][Hkv][r][D]
+    const void* coef;      // [NB][Hkv][P][r]
+    int32_t summ_bf16;
     const int32_t* block_table;
     const int32_t* seq_lens;
     int32_t batch, num_q_heads, num_kv_heads, max_pages, num_blocks;
@@ -71,9 +72,10 @@ struct BuildParams {
     const int32_t* page_begin; // [B] or null
     int32_t batch, num_kv_heads, max_pages, num_blocks;
     int32_t page_size, head_dim, rank;
-    float* mu;
-    float* basis;
-    float* coef;
+    void* mu;              // fp32 or bf16 (out_bf16)
+    void* basis;
+    void* coef;
+    int32_t out_bf16;
 };
 hipError_t launch_build(const BuildParams& p, hipStream_t s);
 bool build_supported(int page_size, int head_dim, int rank);

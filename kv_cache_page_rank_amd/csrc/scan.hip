@@ -45,29 +45,83 @@ struct WaveCtx {
     float qf[D / 4];
 };
 
-// Load of T at element offset `off` of `base`.  kOff32: every summary array
-// is below 4 GiB, so the byte offset is a 32-bit value added to the uniform
-// base (one VALU op per address instead of 64-bit arithmetic).
-template <typename T, bool kOff32>
-__device__ __forceinline__ T load_at(const float* base, size_t off) {
+// Summary element types: fp32, or bf16 bit patterns (uint16_t) widened to
+// fp32 on load.  E = elements per 16-byte load.
+template <typename TS>
+struct Summ {
+    static constexpr int E = 16 / (int)sizeof(TS);
+};
+
+// Address of element `off` of `base`.  kOff32: every summary array is below
+// 4 GiB, so the byte offset is a 32-bit value added to the uniform base (one
+// VALU op per address instead of 64-bit arithmetic).
+template <typename TS, bool kOff32>
+__device__ __forceinline__ const char* elem_addr(const void* base, size_t off) {
     if constexpr (kOff32)
-        return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) +
-                                           (uint32_t)((uint32_t)off * 4u));
+        return static_cast<const char*>(base) + (uint32_t)((uint32_t)off * (uint32_t)sizeof(TS));
     else
-        return *reinterpret_cast<const T*>(base + off);
+        return static_cast<const char*>(base) + off * sizeof(TS);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// N (1, 2, 4, or E for a full 16-byte load) consecutive summary elements
+// starting at element `off`, widened to fp32.
+template <typename TS, bool kOff32, int N>
+__device__ __forceinline__ void load_elems(const void* base, size_t off, float* out) {
+    const char* ptr = elem_addr<TS, kOff32>(base, off);
+    if constexpr (sizeof(TS) == 4) {
+        if constexpr (N == 1) {
+            out[0] = *reinterpret_cast<const float*>(ptr);
+        } else if constexpr (N == 2) {
+            const f32x2 v = *reinterpret_cast<const f32x2*>(ptr);
+            out[0] = v[0];
+            out[1] = v[1];
+        } else {
+            static_assert(N == 4, "fp32 loads of 1, 2 or 4 elements");
+            const f32x4 v = *reinterpret_cast<const f32x4*>(ptr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = v[e];
+        }
+    } else {
+        if constexpr (N == 1) {
+            out[0] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(ptr) << 16);
+        } else if constexpr (N == 2) {
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(ptr);
+            out[0] = bf16_lo(v);
+            out[1] = bf16_hi(v);
+        } else if constexpr (N == 4) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(ptr);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                out[2 * e] = bf16_lo(v[e]);
+                out[2 * e + 1] = bf16_hi(v[e]);
+            }
+        } else {
+            static_assert(N == 8, "bf16 loads of 1, 2, 4 or 8 elements");
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ptr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                out[2 * e] = bf16_lo(v[e]);
+                out[2 * e + 1] = bf16_hi(v[e]);
+            }
+        }
+    }
 }
 
 // One wave's batch of kBatch pages.  kMasked: some page of the batch is
 // absent or the rank is padded, so loads are zeroed per row; otherwise no
 // masking code is emitted.  kHeads: per-head masses are written too.
-template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
+template <typename TS, int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
 __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>& x) {
     constexpr int PPT = 16 / RR;          // pages per basis tile (16 rows = PPT pages x RR rows)
     constexpr int NTILE = kBatch / PPT;   // basis tiles per batch
     constexpr int KS2 = RR / 4;           // K-steps of the coefficient product
     constexpr int MT = P / 16;            // token tiles per page
     constexpr int DS = D / 4;             // K-steps of the d contraction
-    constexpr int DT = D / 16;            // 16-byte loads per row slice
+    constexpr int E = Summ<TS>::E;        // elements per 16-byte load
+    constexpr int NCH = D / (4 * E);      // 16-byte loads per row and lane
     constexpr int PF = kPrefetch, NACC = kChains;
     using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
     const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
@@ -82,9 +136,20 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
     const int a_pin = (c & 3) / KS2;
     const int a_kk = KS2 * (c >> 2) + ((c & 3) % KS2);
 
+    // A tile keeps the loaded words as they are (fp32 bits or bf16 pairs) and
+    // widens them only where the MFMAs consume them, so the waits for a
+    // tile's loads fall at its use, not at its load.
+    constexpr int VW = DS * (int)sizeof(TS) / 4;                  // words of the basis slice
+    constexpr int CFW = sizeof(TS) == 4 ? KS2 : (KS2 + 1) / 2;     // words per coefficient chunk
     struct Tile {
-        float v[DS];
-        float cf[PPT][MT][KS2];
+        uint32_t v[VW];
+        uint32_t cf[PPT][MT][CFW];
+    };
+    auto widen = [](const uint32_t* words, int i) -> float {  // element i of a word array
+        if constexpr (sizeof(TS) == 4)
+            return __uint_as_float(words[i]);
+        else
+            return (i & 1) ? bf16_hi(words[i >> 1]) : bf16_lo(words[i >> 1]);
     };
     // Loads are unconditional (absent rows read a clamped, valid address and
     // are zeroed afterwards) so that the next tile's loads stay in flight
@@ -93,12 +158,12 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
         const int pj = phys_at(tt * PPT + a_pin);
         const bool row_ok = !kMasked || (pj >= 0 && a_kk < r);
         const Off src = (((Off)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
-                         (kMasked && a_kk >= r ? r - 1 : a_kk)) * D + 4 * w;
+                         (kMasked && a_kk >= r ? r - 1 : a_kk)) * D + E * w;
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            const f32x4 v = load_at<f32x4, kOff32>(a.basis, src + 16 * t);
+        for (int t = 0; t < NCH; ++t) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(elem_addr<TS, kOff32>(a.basis, src + 4 * E * t));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) T.v[4 * t + e] = row_ok ? v[e] : 0.0f;
+            for (int e = 0; e < 4; ++e) T.v[4 * t + e] = row_ok ? v[e] : 0u;
         }
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
@@ -108,29 +173,55 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const Off row = csrc + (Off)(16 * mt + c) * r;
-                if constexpr (kExact) {
-                    if constexpr (KS2 == 1) {
-                        const float v = load_at<float, kOff32>(a.coef, row + w);
-                        T.cf[p][mt][0] = ok ? v : 0.0f;
-                    } else if constexpr (KS2 == 2) {
-                        const f32x2 v = load_at<f32x2, kOff32>(a.coef, row + 2 * w);
-                        T.cf[p][mt][0] = ok ? v[0] : 0.0f;
-                        T.cf[p][mt][1] = ok ? v[1] : 0.0f;
+                if (kExact || KS2 == 1) {
+                    // KS2 consecutive elements k = KS2 w .. (rank not padded), or the
+                    // single element k = w clamped to the rank and zeroed past it
+                    const int k0 = kExact ? KS2 * w : (w < r ? w : r - 1);
+                    const bool kok = kExact || w < r;
+                    const char* ptr = elem_addr<TS, kOff32>(a.coef, row + k0);
+                    if constexpr (CFW == 1) {
+                        uint32_t word;
+                        if constexpr (sizeof(TS) == 2 && KS2 == 1)
+                            word = *reinterpret_cast<const uint16_t*>(ptr);
+                        else
+                            word = *reinterpret_cast<const uint32_t*>(ptr);
+                        T.cf[p][mt][0] = (ok && kok) ? word : 0u;
+                    } else if constexpr (CFW == 2) {
+                        const u32x2 v = *reinterpret_cast<const u32x2*>(ptr);
+                        T.cf[p][mt][0] = ok ? v[0] : 0u;
+                        T.cf[p][mt][1] = ok ? v[1] : 0u;
                     } else {
-                        const f32x4 v = load_at<f32x4, kOff32>(a.coef, row + 4 * w);
+                        const u32x4 v = *reinterpret_cast<const u32x4*>(ptr);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) T.cf[p][mt][e] = ok ? v[e] : 0.0f;
+                        for (int e = 0; e < 4; ++e) T.cf[p][mt][e] = ok ? v[e] : 0u;
                     }
                 } else {
+                    // padded rank with KS2 > 1: element by element, clamped and
+                    // zeroed past the rank
+#pragma unroll
+                    for (int e = 0; e < CFW; ++e) T.cf[p][mt][e] = 0u;
 #pragma unroll
                     for (int ks = 0; ks < KS2; ++ks) {
                         const int kk = KS2 * w + ks;
-                        const float v = load_at<float, kOff32>(a.coef, row + (kk < r ? kk : r - 1));
-                        T.cf[p][mt][ks] = (ok && kk < r) ? v : 0.0f;
+                        const char* ptr = elem_addr<TS, kOff32>(a.coef, row + (kk < r ? kk : r - 1));
+                        if constexpr (sizeof(TS) == 4) {
+                            const uint32_t word = *reinterpret_cast<const uint32_t*>(ptr);
+                            T.cf[p][mt][ks] = (ok && kk < r) ? word : 0u;
+                        } else {
+                            const uint32_t half = *reinterpret_cast<const uint16_t*>(ptr);
+                            T.cf[p][mt][ks >> 1] |= ((ok && kk < r) ? half : 0u) << (16 * (ks & 1));
+                        }
                     }
                 }
             }
         }
+    };
+    // coefficient element ks of chunk (p, mt)
+    auto coef_el = [&](const Tile& tl, int p, int mt, int ks) -> float {
+        if constexpr (sizeof(TS) == 2 && KS2 == 1)
+            return bf16_lo(tl.cf[p][mt][0]);
+        else
+            return widen(tl.cf[p][mt], ks);
     };
     auto basis_product = [&](const Tile& tl) {
         f32x4 tacc[NACC];
@@ -138,7 +229,7 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
         for (int i = 0; i < NACC; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < DS; ++s)
-            tacc[s % NACC] = mfma_16x16x4_f32(tl.v[s], x.qf[s], tacc[s % NACC]);
+            tacc[s % NACC] = mfma_16x16x4_f32(widen(tl.v, s), x.qf[s], tacc[s % NACC]);
         f32x4 T = tacc[0];
 #pragma unroll
         for (int i = 1; i < NACC; ++i) T += tacc[i];
@@ -154,13 +245,14 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
     // beta tile: A row m = page j0 + m (lane column c supplies row c).
     f32x4 beta;
     {
-        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + 4 * w;
+        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + E * w;
         float mv[DS];
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            const f32x4 v = load_at<f32x4, kOff32>(a.mu, src + 16 * t);
+        for (int t = 0; t < NCH; ++t) {
+            float v[E];
+            load_elems<TS, kOff32, E>(a.mu, src + 4 * E * t, v);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mv[4 * t + e] = (!kMasked || my_phys >= 0) ? v[e] : 0.0f;
+            for (int e = 0; e < E; ++e) mv[E * t + e] = (!kMasked || my_phys >= 0) ? v[e] : 0.0f;
         }
         f32x4 bacc[NACC];
 #pragma unroll
@@ -188,7 +280,7 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
                 L[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS2; ++ks)
-                    L[p][mt] = mfma_16x16x4_f32(cur.cf[p][mt][ks], Tcur[p * KS2 + ks], L[p][mt]);
+                    L[p][mt] = mfma_16x16x4_f32(coef_el(cur, p, mt, ks), Tcur[p * KS2 + ks], L[p][mt]);
             }
 
 #pragma unroll
@@ -241,11 +333,12 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
     }
 }
 
-template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32>
+template <typename TS, int P, int D, int RR, bool kExact, bool kHeads, bool kOff32>
 __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
-    static_assert(P % 16 == 0 && D % 16 == 0, "P and d must be multiples of 16");
+    static_assert(P % 16 == 0 && D % 32 == 0, "P a multiple of 16, d of 32");
     static_assert(RR == 4 || RR == 8 || RR == 16, "padded rank");
-    constexpr int DT = D / 16;
+    constexpr int E = Summ<TS>::E;
+    constexpr int NCH = D / (4 * E);
 
     WaveCtx<D> x;
     x.lane = threadIdx.x & 63;
@@ -288,38 +381,54 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     x.my_phys =
         (c < kBatch && x.j0 + c < full && p_spec >= 0 && p_spec < a.num_blocks) ? p_spec : -1;
 
-    // Query fragment: q[h][16t + 4w + e] for head h = c, scaled to log2 units.
+    // Query fragment, in the contraction order of the summary loads:
+    // qf[E t + e] = q[h][4E t + E w + e] for head h = c, scaled to log2 units.
     const float qscale = kLog2e / sqrtf((float)D);
     {
         const float* qp =
             a.q + ((size_t)x.b * a.num_q_heads + x.g * x.G + (x.head_ok ? c : 0)) * D;
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            f32x4 v = *reinterpret_cast<const f32x4*>(qp + 16 * t + 4 * w);
+        for (int t = 0; t < NCH; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x.qf[4 * t + e] = x.head_ok ? v[e] * qscale : 0.0f;
-        }
+            for (int h4 = 0; h4 < E / 4; ++h4) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(qp + 4 * E * t + E * w + 4 * h4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x.qf[E * t + 4 * h4 + e] = x.head_ok ? v[e] * qscale : 0.0f;
+            }
     }
 
     // every page of the batch present and the rank not padded: no masking
     if constexpr (kExact) {
         if (x.j0 + kBatch <= full && __ballot(c < kBatch && x.my_phys < 0) == 0ull) {
-            scan_batch<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
+            scan_batch<TS, P, D, RR, kExact, kHeads, kOff32, false>(a, x);
             return;
         }
     }
-    scan_batch<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
+    scan_batch<TS, P, D, RR, kExact, kHeads, kOff32, true>(a, x);
 }
 
-template <int P, int D, int RR, bool kHeads, bool kOff32>
+template <typename TS, int P, int D, int RR, bool kHeads, bool kOff32>
 hipError_t launch4(const ScanParams& p, hipStream_t s, unsigned blocks) {
     if (p.rank == RR)
-        hipLaunchKernelGGL((scan_kernel<P, D, RR, true, kHeads, kOff32>), dim3(blocks), dim3(256),
-                           0, s, p);
+        hipLaunchKernelGGL((scan_kernel<TS, P, D, RR, true, kHeads, kOff32>), dim3(blocks),
+                           dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((scan_kernel<P, D, RR, false, kHeads, kOff32>), dim3(blocks), dim3(256),
-                           0, s, p);
+        hipLaunchKernelGGL((scan_kernel<TS, P, D, RR, false, kHeads, kOff32>), dim3(blocks),
+                           dim3(256), 0, s, p);
     return hipGetLastError();
+}
+
+template <typename TS, int P, int D, int RR>
+hipError_t launch_ts(const ScanParams& p, hipStream_t s, unsigned blocks) {
+    // largest summary array (basis or coefficients) in bytes
+    const size_t per_unit = (size_t)p.rank * (D > P ? D : P) * sizeof(TS);
+    const bool off32 = (size_t)p.num_blocks * p.num_kv_heads * per_unit < (size_t(1) << 32);
+    if (p.head_logmass != nullptr)
+        return off32 ? launch4<TS, P, D, RR, true, true>(p, s, blocks)
+                     : launch4<TS, P, D, RR, true, false>(p, s, blocks);
+    return off32 ? launch4<TS, P, D, RR, false, true>(p, s, blocks)
+                 : launch4<TS, P, D, RR, false, false>(p, s, blocks);
 }
 
 template <int P, int D, int RR>
@@ -327,15 +436,8 @@ hipError_t launch(const ScanParams& p, hipStream_t s) {
     const long waves = (long)p.batch * p.num_kv_heads * ((p.max_pages + kBatch - 1) / kBatch);
     const unsigned blocks = (unsigned)((waves + 3) / 4);
     if (blocks == 0) return hipSuccess;
-    // largest summary array (basis or coefficients) in bytes
-    const size_t per_unit = (size_t)p.rank * (D > P ? D : P) * sizeof(float);
-    const bool off32 = (size_t)p.num_blocks * p.num_kv_heads * per_unit < (size_t(1) << 32);
-    const bool heads = p.head_logmass != nullptr;
-    if (heads)
-        return off32 ? launch4<P, D, RR, true, true>(p, s, blocks)
-                     : launch4<P, D, RR, true, false>(p, s, blocks);
-    return off32 ? launch4<P, D, RR, false, true>(p, s, blocks)
-                 : launch4<P, D, RR, false, false>(p, s, blocks);
+    return p.summ_bf16 ? launch_ts<uint16_t, P, D, RR>(p, s, blocks)
+                       : launch_ts<float, P, D, RR>(p, s, blocks);
 }
 
 template <int P, int D>

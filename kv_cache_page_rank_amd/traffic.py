@@ -21,17 +21,19 @@ def summary_to_cache_ratio(d: int, P: int, r: int, summary_elem: int = 4, kv_ele
     return summary_unit_bytes(d, P, r, summary_elem) / kv_unit_bytes(d, P, kv_elem)
 
 
-def scan_bytes(batch, num_q_heads, num_kv_heads, max_pages, full_pages, d, P, r) -> int:
+def scan_bytes(batch, num_q_heads, num_kv_heads, max_pages, full_pages, d, P, r,
+               summary_elem: int = 4) -> int:
     """Bytes one scan launch must move: every full page's summary, the
     queries, and the page-mass output row."""
-    return (full_pages * num_kv_heads * summary_unit_bytes(d, P, r) + batch * num_q_heads * d * 4
-            + batch * num_kv_heads * max_pages * 4)
+    return (full_pages * num_kv_heads * summary_unit_bytes(d, P, r, summary_elem)
+            + batch * num_q_heads * d * 4 + batch * num_kv_heads * max_pages * 4)
 
 
-def step_bytes(full_pages, partial_pages, num_kv_heads, d, P, r, k_pages_total) -> int:
+def step_bytes(full_pages, partial_pages, num_kv_heads, d, P, r, k_pages_total,
+               summary_elem: int = 4) -> int:
     """Bytes of one decode step: all summaries + the K/V of the selected pages
     and of each sequence's partial last page."""
-    return (full_pages * num_kv_heads * summary_unit_bytes(d, P, r)
+    return (full_pages * num_kv_heads * summary_unit_bytes(d, P, r, summary_elem)
             + (k_pages_total + partial_pages * num_kv_heads) * kv_unit_bytes(d, P))
 
 

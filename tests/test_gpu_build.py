@@ -23,11 +23,12 @@ from gpu_cases import DEV, Case, bf16_small, masses_close, say, tiny, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _build_gpu(case, rank=None, page_begin=None):
+def _build_gpu(case, rank=None, page_begin=None, dtype=torch.float32):
     import kv_cache_page_rank_amd as lk
     s = case.spec
     r = s.rank if rank is None else rank
-    summ = lk.Summaries.empty(s.num_blocks, s.num_kv_heads, s.page_size, s.head_dim, r)
+    summ = lk.Summaries.empty(s.num_blocks, s.num_kv_heads, s.page_size, s.head_dim, r,
+                              dtype=dtype)
     for t in (summ.mu, summ.basis, summ.coef):
         t.fill_(np.nan)
     lk.locks_build_summaries(case.kv, case.pages, summ, page_begin=page_begin)
@@ -132,3 +133,21 @@ def test_build_deterministic():
     for x, y in ((a.mu, b.mu), (a.basis, b.basis), (a.coef, b.coef)):
         # bitwise (blocks of partial pages keep their NaN fill in both runs)
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+@pytest.mark.parametrize("mk", [lambda: bf16_small(), lambda: bf16_small(rank=2),
+                                lambda: tiny(rank=3)], ids=["r8", "r2", "tiny-r3"])
+def test_build_bf16_is_rounded_fp32_build(mk):
+    """bf16 summaries are the fp32 summaries rounded to nearest even (the
+    rounding done here by torch on the host), bit for bit; blocks that hold
+    no full page stay untouched in both."""
+    case = Case(mk())
+    say("build bf16 vs fp32", case.spec.name)
+    f = _build_gpu(case)
+    h = _build_gpu(case, dtype=torch.bfloat16)
+    for x32, x16 in ((f.mu, h.mu), (f.basis, h.basis), (f.coef, h.coef)):
+        ref = x32.cpu().to(torch.bfloat16)
+        got = x16.cpu()
+        fin = torch.isfinite(ref)
+        assert torch.equal(fin, torch.isfinite(got))
+        assert torch.equal(ref[fin].view(torch.int16), got[fin].view(torch.int16))

@@ -10,12 +10,15 @@ from workload.device import summaries_to_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("mk", [lambda: tiny(), lambda: bf16_small()], ids=["tiny", "bf16"])
-def test_graph_replay_equals_eager(mk):
+@pytest.mark.parametrize("mk,sdt", [(lambda: tiny(), torch.float32),
+                                    (lambda: bf16_small(), torch.float32),
+                                    (lambda: bf16_small(), torch.bfloat16)],
+                         ids=["tiny", "bf16", "bf16-summaries"])
+def test_graph_replay_equals_eager(mk, sdt):
     import kv_cache_page_rank_amd as lk
     case = Case(mk())
     s = case.spec
-    summ = summaries_to_device(*case.oracle_summaries())
+    summ = summaries_to_device(*case.oracle_summaries(), dtype=sdt)
     k = s.k_pages
     ws_b = lk.workspace_bytes(lk.OP_STEP, s.batch, s.max_pages, s.num_q_heads, s.num_kv_heads,
                               s.page_size, s.head_dim, s.rank, k)

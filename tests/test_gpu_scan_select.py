@@ -60,6 +60,60 @@ def test_scan_matches_oracle(name, mk):
     np.testing.assert_array_equal(to_np(rm), host_run_max(to_np(pm), s.seq_lens, s.page_size))
 
 
+@pytest.mark.parametrize("name,mk", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
+def test_scan_bf16_summaries_match_oracle(name, mk):
+    """Scan of bf16 summaries: the oracle reads the same rounded values
+    (widened exactly), so the bar is the fp32 one: log-masses within 1e-4."""
+    case = Case(mk())
+    s = case.spec
+    mu, basis, coef = (torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+                       for x in case.oracle_summaries())
+    wide = [x.float().numpy() for x in (mu, basis, coef)]
+    head_o, page_o = oracle.scan_pool(case.lay, s.rank, case.layer.q, *wide)
+    import kv_cache_page_rank_amd as lk
+    summ = lk.Summaries(mu.to(DEV), basis.to(DEV), coef.to(DEV))
+    pm = torch.full((s.batch, s.num_kv_heads, s.max_pages), 7.0, device=DEV)
+    hm = torch.full((s.batch, s.num_q_heads, s.max_pages), 7.0, device=DEV)
+    rm = torch.full((s.batch, s.num_kv_heads, -(-s.max_pages // RUN)), 7.0, device=DEV)
+    say("scan bf16 summaries", name, s)
+    lk.locks_scan(case.q, summ, case.pages, pm, hm, run_max=rm)
+    pm2 = torch.full_like(pm, 7.0)
+    lk.locks_scan(case.q, summ, case.pages, pm2)  # the path without per-head output
+    torch.cuda.synchronize()
+    assert masses_close(to_np(pm), page_o) <= 1e-4
+    assert masses_close(to_np(pm2), page_o) <= 1e-4
+    assert masses_close(to_np(hm), head_o) <= 1e-4
+    np.testing.assert_array_equal(to_np(rm), host_run_max(to_np(pm), s.seq_lens, s.page_size))
+
+
+def test_select_bf16_summaries_band():
+    """locks_select over GPU-built bf16 summaries against the oracle's
+    selection from the same (downloaded) summaries."""
+    case = Case(bf16_small())
+    s = case.spec
+    import kv_cache_page_rank_amd as lk
+    summ = lk.Summaries.empty(s.num_blocks, s.num_kv_heads, s.page_size, s.head_dim, s.rank,
+                              dtype=torch.bfloat16)
+    say("select bf16 summaries")
+    lk.locks_build_summaries(case.kv, case.pages, summ)
+    torch.cuda.synchronize()
+    wide = [x.float().cpu().numpy() for x in (summ.mu, summ.basis, summ.coef)]
+    _, page_o = oracle.scan_pool(case.lay, s.rank, case.layer.q, *wide, heads=False)
+    k = s.k_pages
+    sel_o, _ = oracle.select_pool(case.lay, s.budget_tokens, page_o.astype(np.float32), k)
+    sel = torch.empty((s.batch, s.num_kv_heads, k), dtype=torch.int32, device=DEV)
+    mass = torch.empty((s.batch, s.num_kv_heads, k), device=DEV)
+    ws = lk.workspace(lk.workspace_bytes(lk.OP_SELECT, s.batch, s.max_pages, s.num_q_heads,
+                                         s.num_kv_heads, s.page_size, s.head_dim, s.rank, k))
+    lk.locks_select(case.q, summ, case.pages, s.budget_tokens, sel, mass, ws=ws)
+    torch.cuda.synchronize()
+    sel_g = sel.cpu().numpy()
+    for b in range(s.batch):
+        f = s.seq_lens[b] // s.page_size
+        for g in range(s.num_kv_heads):
+            assert band_ok(sel_g[b, g], sel_o[b, g], page_o[b, g, :f], min(k, f)), (b, g)
+
+
 def test_scan_full_rank_is_exact_lse():
     """r = min(P, d): the GPU estimate from oracle summaries equals the exact
     page LSE (the selection that reads every key)."""

@@ -26,8 +26,9 @@ def upload(layer, device="cuda"):
     return q, lk.PagedKV(k, v), pages
 
 
-def summaries_to_device(mu, basis, coef, device="cuda"):
+def summaries_to_device(mu, basis, coef, device="cuda", dtype=torch.float32):
+    """Host summaries (float arrays) as device tensors of the given dtype
+    (bf16: torch's round-to-nearest-even of the fp32 values)."""
     import kv_cache_page_rank_amd as lk
-    return lk.Summaries(torch.from_numpy(np.ascontiguousarray(mu, np.float32)).to(device),
-                        torch.from_numpy(np.ascontiguousarray(basis, np.float32)).to(device),
-                        torch.from_numpy(np.ascontiguousarray(coef, np.float32)).to(device))
+    return lk.Summaries(*(torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device).to(dtype)
+                          for x in (mu, basis, coef)))
