@@ -45,8 +45,8 @@ struct WaveCtx {
     float qf[D / 4];
 };
 
-// Summary element types: fp32, or bf16 bit patterns (uint16_t) widened to
-// fp32 on load.  E = elements per 16-byte load.
+// Summary element types: fp32, or bf16 bit patterns (uint16_t).  E =
+// elements per 16-byte load.
 template <typename TS>
 struct Summ {
     static constexpr int E = 16 / (int)sizeof(TS);
@@ -63,49 +63,68 @@ __device__ __forceinline__ const char* elem_addr(const void* base, size_t off) {
         return static_cast<const char*>(base) + off * sizeof(TS);
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
-
-// N (1, 2, 4, or E for a full 16-byte load) consecutive summary elements
-// starting at element `off`, widened to fp32.
-template <typename TS, bool kOff32, int N>
-__device__ __forceinline__ void load_elems(const void* base, size_t off, float* out) {
-    const char* ptr = elem_addr<TS, kOff32>(base, off);
-    if constexpr (sizeof(TS) == 4) {
-        if constexpr (N == 1) {
-            out[0] = *reinterpret_cast<const float*>(ptr);
-        } else if constexpr (N == 2) {
-            const f32x2 v = *reinterpret_cast<const f32x2*>(ptr);
-            out[0] = v[0];
-            out[1] = v[1];
-        } else {
-            static_assert(N == 4, "fp32 loads of 1, 2 or 4 elements");
-            const f32x4 v = *reinterpret_cast<const f32x4*>(ptr);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = v[e];
-        }
+// N (1, 2 or 4) consecutive fp32 summary elements starting at element `off`.
+template <bool kOff32, int N>
+__device__ __forceinline__ void load_f32(const void* base, size_t off, float* out) {
+    const char* ptr = elem_addr<float, kOff32>(base, off);
+    if constexpr (N == 1) {
+        out[0] = *reinterpret_cast<const float*>(ptr);
+    } else if constexpr (N == 2) {
+        const f32x2 v = *reinterpret_cast<const f32x2*>(ptr);
+        out[0] = v[0];
+        out[1] = v[1];
     } else {
-        if constexpr (N == 1) {
-            out[0] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(ptr) << 16);
-        } else if constexpr (N == 2) {
-            const uint32_t v = *reinterpret_cast<const uint32_t*>(ptr);
-            out[0] = bf16_lo(v);
-            out[1] = bf16_hi(v);
-        } else if constexpr (N == 4) {
-            const u32x2 v = *reinterpret_cast<const u32x2*>(ptr);
+        static_assert(N == 4, "loads of 1, 2 or 4 elements");
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ptr);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                out[2 * e] = bf16_lo(v[e]);
-                out[2 * e + 1] = bf16_hi(v[e]);
-            }
-        } else {
-            static_assert(N == 8, "bf16 loads of 1, 2, 4 or 8 elements");
-            const u32x4 v = *reinterpret_cast<const u32x4*>(ptr);
+        for (int e = 0; e < 4; ++e) out[e] = v[e];
+    }
+}
+
+// Per-page tail shared by both summary types: lane (w, c) holds the logits of
+// tokens 16 mt + 4w + v for head c (log2 units, beta not yet added) in
+// L[mt][v].  Forms the head's LSE, adds beta, aggregates the group and
+// writes page pb of the batch (row w = pb / 4 holds the right beta).
+template <int D, int MT, bool kHeads, bool kMasked>
+__device__ __forceinline__ void page_mass(const ScanParams& a, const WaveCtx<D>& x,
+                                          const f32x4* L, int pb, const f32x4& beta,
+                                          float& run_mx) {
+    const int w = x.w, c = x.c, g = x.g;
+    const int j = x.j0 + pb;
+    float mx = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                out[2 * e] = bf16_lo(v[e]);
-                out[2 * e + 1] = bf16_hi(v[e]);
-            }
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, L[mt][v]);
+    mx = max_over_rows(mx);
+    float sum = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sum += fast_exp2(L[mt][v] - mx);
+    sum = sum_over_rows(sum);
+    // head h's mass is sum * 2^(mx + beta); beta of page pb sits in row
+    // pb/4, element pb%4, so only that row's values are right
+    const float top = mx + beta[pb & 3];
+    float a2, s2 = 0.0f;
+    if constexpr (kHeads) {
+        s2 = top + fast_log2(sum);
+        const float xv = x.head_ok ? s2 : -INFINITY;
+        const float gm = max_in_row(xv);
+        a2 = gm + fast_log2(sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f));
+    } else {  // the group sum without each head's log: sum_h sum_h 2^(top_h - max top)
+        const float gm = max_in_row(x.head_ok ? top : -INFINITY);
+        a2 = gm + fast_log2(sum_in_row(x.head_ok ? sum * fast_exp2(top - gm) : 0.0f));
+    }
+    if (w == (pb >> 2) && j < a.max_pages) {
+        const bool ok = !kMasked || __builtin_amdgcn_readlane(x.my_phys, pb) >= 0;
+        const float mass = ok ? a2 * kLn2 : -INFINITY;
+        run_mx = fmaxf(run_mx, mass);
+        if (c == 0) x.out_page[j] = mass;
+        if constexpr (kHeads) {
+            if (x.head_ok)
+                a.head_logmass[((size_t)x.b * a.num_q_heads + g * x.G + c) * a.max_pages + j] =
+                    ok ? s2 * kLn2 : -INFINITY;
         }
     }
 }
@@ -113,8 +132,9 @@ __device__ __forceinline__ void load_elems(const void* base, size_t off, float* 
 // One wave's batch of kBatch pages.  kMasked: some page of the batch is
 // absent or the rank is padded, so loads are zeroed per row; otherwise no
 // masking code is emitted.  kHeads: per-head masses are written too.
-template <typename TS, int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
-__device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>& x) {
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
+__device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCtx<D>& x) {
+    using TS = float;
     constexpr int PPT = 16 / RR;          // pages per basis tile (16 rows = PPT pages x RR rows)
     constexpr int NTILE = kBatch / PPT;   // basis tiles per batch
     constexpr int KS2 = RR / 4;           // K-steps of the coefficient product
@@ -136,21 +156,14 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
     const int a_pin = (c & 3) / KS2;
     const int a_kk = KS2 * (c >> 2) + ((c & 3) % KS2);
 
-    // A tile keeps the loaded words as they are (fp32 bits or bf16 pairs) and
-    // widens them only where the MFMAs consume them, so the waits for a
-    // tile's loads fall at its use, not at its load.
-    constexpr int VW = DS * (int)sizeof(TS) / 4;                  // words of the basis slice
-    constexpr int CFW = sizeof(TS) == 4 ? KS2 : (KS2 + 1) / 2;     // words per coefficient chunk
+    // A tile keeps the loaded words as they are and reinterprets them where
+    // the MFMAs consume them, so the waits for a tile's loads fall at its use.
+    constexpr int CFW = KS2;  // words per coefficient chunk
     struct Tile {
-        uint32_t v[VW];
+        uint32_t v[DS];
         uint32_t cf[PPT][MT][CFW];
     };
-    auto widen = [](const uint32_t* words, int i) -> float {  // element i of a word array
-        if constexpr (sizeof(TS) == 4)
-            return __uint_as_float(words[i]);
-        else
-            return (i & 1) ? bf16_hi(words[i >> 1]) : bf16_lo(words[i >> 1]);
-    };
+    auto widen = [](const uint32_t* words, int i) -> float { return __uint_as_float(words[i]); };
     // Loads are unconditional (absent rows read a clamped, valid address and
     // are zeroed afterwards) so that the next tile's loads stay in flight
     // while the current tile is computed.
@@ -180,11 +193,7 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
                     const bool kok = kExact || w < r;
                     const char* ptr = elem_addr<TS, kOff32>(a.coef, row + k0);
                     if constexpr (CFW == 1) {
-                        uint32_t word;
-                        if constexpr (sizeof(TS) == 2 && KS2 == 1)
-                            word = *reinterpret_cast<const uint16_t*>(ptr);
-                        else
-                            word = *reinterpret_cast<const uint32_t*>(ptr);
+                        const uint32_t word = *reinterpret_cast<const uint32_t*>(ptr);
                         T.cf[p][mt][0] = (ok && kok) ? word : 0u;
                     } else if constexpr (CFW == 2) {
                         const u32x2 v = *reinterpret_cast<const u32x2*>(ptr);
@@ -204,13 +213,8 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
                     for (int ks = 0; ks < KS2; ++ks) {
                         const int kk = KS2 * w + ks;
                         const char* ptr = elem_addr<TS, kOff32>(a.coef, row + (kk < r ? kk : r - 1));
-                        if constexpr (sizeof(TS) == 4) {
-                            const uint32_t word = *reinterpret_cast<const uint32_t*>(ptr);
-                            T.cf[p][mt][ks] = (ok && kk < r) ? word : 0u;
-                        } else {
-                            const uint32_t half = *reinterpret_cast<const uint16_t*>(ptr);
-                            T.cf[p][mt][ks >> 1] |= ((ok && kk < r) ? half : 0u) << (16 * (ks & 1));
-                        }
+                        const uint32_t word = *reinterpret_cast<const uint32_t*>(ptr);
+                        T.cf[p][mt][ks] = (ok && kk < r) ? word : 0u;
                     }
                 }
             }
@@ -218,10 +222,7 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
     };
     // coefficient element ks of chunk (p, mt)
     auto coef_el = [&](const Tile& tl, int p, int mt, int ks) -> float {
-        if constexpr (sizeof(TS) == 2 && KS2 == 1)
-            return bf16_lo(tl.cf[p][mt][0]);
-        else
-            return widen(tl.cf[p][mt], ks);
+        return widen(tl.cf[p][mt], ks);
     };
     auto basis_product = [&](const Tile& tl) {
         f32x4 tacc[NACC];
@@ -250,7 +251,7 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
 #pragma unroll
         for (int t = 0; t < NCH; ++t) {
             float v[E];
-            load_elems<TS, kOff32, E>(a.mu, src + 4 * E * t, v);
+            load_f32<kOff32, E>(a.mu, src + 4 * E * t, v);
 #pragma unroll
             for (int e = 0; e < E; ++e) mv[E * t + e] = (!kMasked || my_phys >= 0) ? v[e] : 0.0f;
         }
@@ -284,47 +285,163 @@ __device__ __forceinline__ void scan_batch(const ScanParams& a, const WaveCtx<D>
             }
 
 #pragma unroll
-        for (int p = 0; p < PPT; ++p) {
-            const int pb = tt * PPT + p;  // page index within the batch
-            const int j = x.j0 + pb;
-            // lane (w, c) holds logits of tokens 16*mt + 4w + v for head c.
-            float mx = -INFINITY;
+        for (int p = 0; p < PPT; ++p)
+            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], tt * PPT + p, beta, run_mx);
+    }
+    if (a.run_max) {
+        run_mx = max_over_rows(run_mx);
+        const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
+        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
+    }
+}
+
+// bf16 summaries on the bf16 matrix cores, to fp32 accuracy: the stored
+// values are bf16 already, and each fp32 multiplicand (q, and the basis
+// product T) is split into three bf16 parts hi + mid + lo whose sum is the
+// value (24 significant bits); every product is exact and accumulates in
+// fp32.  Per tile of 16 basis rows (row m = basis row m % RR of page m / RR):
+//   T (16 rows x 16 heads)   = basis rows . q^T   v_mfma_f32_16x16x32_bf16 x 3 parts per 32 d
+//   L (16 tokens x 16 heads) = coef . T           v_mfma_f32_16x16x16_bf16 x 3 parts
+// The coefficient operand of page p is zero outside p's rows of the tile.
+__device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
+    h = (__bf16)x;
+    float rest = x - (float)h;
+    m = (__bf16)rest;
+    rest -= (float)m;
+    l = (__bf16)rest;
+}
+
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
+__device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveCtx<D>& x) {
+    using TS = uint16_t;
+    constexpr int PPT = 16 / RR;          // pages per tile
+    constexpr int NTILE = kBatch / PPT;
+    constexpr int MT = P / 16;            // token tiles per page
+    constexpr int NCH = D / 32;           // 32-wide d chunks (one 16-byte load per lane each)
+    constexpr int WPP = RR / 4;           // lane groups per page in the coefficient operand
+    constexpr int PF = kPrefetch;
+    using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
+    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
+    const int my_phys = x.my_phys;
+
+    // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e
+    bf16x8 qp[3][NCH];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < NCH; ++t)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) mx = fmaxf(mx, L[p][mt][v]);
-            mx = max_over_rows(mx);
-            float sum = 0.0f;
+        for (int e = 0; e < 8; ++e) {
+            __bf16 h, m, l;
+            split3(x.qf[8 * t + e], h, m, l);
+            qp[0][t][e] = h;
+            qp[1][t][e] = m;
+            qp[2][t][e] = l;
+        }
+
+    const int a_pin = c / RR, a_k = c % RR;   // basis row loaded by this lane
+    const int c_pin = w / WPP;                // page whose coefficients this lane supplies
+    const int c_k0 = 4 * (w % WPP);           // its first coefficient index
+    struct Tile {
+        u32x4 v[NCH];
+        u32x2 cf[MT];
+    };
+    auto load_tile = [&](int tt, Tile& T) {
+        const int pj = __shfl(my_phys, tt * PPT + a_pin, kWave);
+        const bool row_ok = !kMasked || (pj >= 0 && a_k < r);
+        const Off src = (((Off)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
+                         (kMasked && a_k >= r ? r - 1 : a_k)) * D + 8 * w;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int t = 0; t < NCH; ++t) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(elem_addr<TS, kOff32>(a.basis, src + 32 * t));
 #pragma unroll
-                for (int v = 0; v < 4; ++v) sum += fast_exp2(L[p][mt][v] - mx);
-            sum = sum_over_rows(sum);
-            // head h's mass is sum * 2^(mx + beta); beta of page pb sits in row
-            // pb/4, element pb%4, so only that row's values are right
-            const float top = mx + beta[pb & 3];
-            float a2, s2 = 0.0f;
-            if constexpr (kHeads) {
-                s2 = top + fast_log2(sum);
-                const float xv = x.head_ok ? s2 : -INFINITY;
-                const float gm = max_in_row(xv);
-                a2 = gm + fast_log2(sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f));
-            } else {  // the group sum without each head's log: sum_h sum_h 2^(top_h - max top)
-                const float gm = max_in_row(x.head_ok ? top : -INFINITY);
-                a2 = gm + fast_log2(sum_in_row(x.head_ok ? sum * fast_exp2(top - gm) : 0.0f));
-            }
-            if (w == (pb >> 2) && j < a.max_pages) {
-                const bool ok = !kMasked || phys_uniform(pb) >= 0;
-                const float mass = ok ? a2 * kLn2 : -INFINITY;
-                run_mx = fmaxf(run_mx, mass);
-                if (c == 0) x.out_page[j] = mass;
-                if constexpr (kHeads) {
-                    if (x.head_ok)
-                        a.head_logmass[((size_t)x.b * a.num_q_heads + g * x.G + c) * a.max_pages +
-                                       j] = ok ? s2 * kLn2 : -INFINITY;
+            for (int e = 0; e < 4; ++e) T.v[t][e] = row_ok ? v[e] : 0u;
+        }
+        const int pp = __shfl(my_phys, tt * PPT + c_pin, kWave);
+        const bool ok = !kMasked || pp >= 0;
+        const Off csrc = ((Off)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const Off row = csrc + (Off)(16 * mt + c) * r;
+            if constexpr (kExact) {
+                const u32x2 v = *reinterpret_cast<const u32x2*>(elem_addr<TS, kOff32>(a.coef, row + c_k0));
+                T.cf[mt][0] = ok ? v[0] : 0u;
+                T.cf[mt][1] = ok ? v[1] : 0u;
+            } else {  // padded rank: element by element, clamped and zeroed past it
+                uint32_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kk = c_k0 + e;
+                    const uint32_t h = *reinterpret_cast<const uint16_t*>(
+                        elem_addr<TS, kOff32>(a.coef, row + (kk < r ? kk : r - 1)));
+                    hv[e] = (ok && kk < r) ? h : 0u;
                 }
+                T.cf[mt][0] = hv[0] | (hv[1] << 16);
+                T.cf[mt][1] = hv[2] | (hv[3] << 16);
             }
         }
+    };
+
+    Tile ring[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF && i < NTILE; ++i) load_tile(i, ring[i]);
+
+    // beta tile: A row m = page j0 + m (lane column c supplies row c).
+    f32x4 beta;
+    {
+        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + 8 * w;
+        f32x4 bacc[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) bacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            u32x4 v = *reinterpret_cast<const u32x4*>(elem_addr<TS, kOff32>(a.mu, src + 32 * t));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (!kMasked || my_phys >= 0) ? v[e] : 0u;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) bacc[i] = mfma_16x16x32_bf16(as_bf16x8(v), qp[i][t], bacc[i]);
+        }
+        beta = bacc[0] + bacc[1] + bacc[2];
+    }
+
+    float run_mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) {
+        if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
+        const Tile& cur = ring[tt % (PF + 1)];
+        f32x4 tacc[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) tacc[i] = mfma_16x16x32_bf16(as_bf16x8(cur.v[t]), qp[i][t], tacc[i]);
+        const f32x4 T = tacc[0] + tacc[1] + tacc[2];
+        // lane (w, c) holds T[tile row 4w + v][head c]: its B operand rows of the
+        // coefficient product, split into three bf16 parts
+        bf16x4 tp[3];
+        {
+            __bf16 hv[4], mv[4], lv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) split3(T[v], hv[v], mv[v], lv[v]);
+            typedef __bf16 bf16v4 __attribute__((ext_vector_type(4)));
+            tp[0] = __builtin_bit_cast(bf16x4, bf16v4{hv[0], hv[1], hv[2], hv[3]});
+            tp[1] = __builtin_bit_cast(bf16x4, bf16v4{mv[0], mv[1], mv[2], mv[3]});
+            tp[2] = __builtin_bit_cast(bf16x4, bf16v4{lv[0], lv[1], lv[2], lv[3]});
+        }
+        f32x4 L[PPT][MT];
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const bool mine = c_pin == p;
+                const u32x2 av = {mine ? cur.cf[mt][0] : 0u, mine ? cur.cf[mt][1] : 0u};
+                const bf16x4 A = as_bf16x4(av);
+                f32x4 acc = mfma_16x16x16_bf16(A, tp[0], f32x4{0.f, 0.f, 0.f, 0.f});
+                acc = mfma_16x16x16_bf16(A, tp[1], acc);
+                L[p][mt] = mfma_16x16x16_bf16(A, tp[2], acc);
+            }
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], tt * PPT + p, beta, run_mx);
     }
     if (a.run_max) {
         run_mx = max_over_rows(run_mx);
@@ -401,11 +518,17 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     // every page of the batch present and the rank not padded: no masking
     if constexpr (kExact) {
         if (x.j0 + kBatch <= full && __ballot(c < kBatch && x.my_phys < 0) == 0ull) {
-            scan_batch<TS, P, D, RR, kExact, kHeads, kOff32, false>(a, x);
+            if constexpr (sizeof(TS) == 2)
+                scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
+            else
+                scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
             return;
         }
     }
-    scan_batch<TS, P, D, RR, kExact, kHeads, kOff32, true>(a, x);
+    if constexpr (sizeof(TS) == 2)
+        scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
+    else
+        scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
 }
 
 template <typename TS, int P, int D, int RR, bool kHeads, bool kOff32>
