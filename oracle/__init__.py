@@ -69,6 +69,7 @@ def lib():
         L.orc_scan_units.argtypes = [lay, c_int, _f32p, _f32p, _f32p, _f32p, c_int, _i32p,
                                      _i32p, _i32p, _f64p, _f64p]
         L.orc_exact_pool.argtypes = [lay, _f32p, _f32p, ctypes.c_void_p, ctypes.c_void_p, c_int]
+        L.orc_share_pool.argtypes = [lay, _f64p, _f64p]
         L.orc_select_pool.argtypes = [lay, c_int, _f32p, c_int, _i32p, ctypes.c_void_p]
         L.orc_attend_pool.argtypes = [lay, _f32p, _f32p, _f32p, ctypes.c_void_p, c_int, _f64p,
                                       ctypes.c_void_p, c_int]
@@ -257,6 +258,16 @@ def exact_pool(L: Layout, q, k_pool, threads: int = 0):
     _check(lib().orc_exact_pool(ref, _f32(q).reshape(-1), _f32(k_pool).reshape(-1),
                                 _ptr(head), _ptr(page), threads), "exact_pool")
     return head, page
+
+
+def share_pool(L: Layout, head_mass):
+    """Mean-of-share group scores [B][Hkv][max_pages] (log of the group's mean
+    share) from per-head estimates [B][Hq][max_pages]."""
+    hm = np.ascontiguousarray(head_mass, np.float64)
+    out = np.zeros((L.batch, L.num_kv_heads, L.max_pages))
+    ref, _keep = L.c()
+    _check(lib().orc_share_pool(ref, hm.reshape(-1), out.reshape(-1)), "share_pool")
+    return out
 
 
 def select_pool(L: Layout, budget_tokens: int, page_mass_f32, width: int):

@@ -386,6 +386,38 @@ int orc_scan_pool(const orc_layout* L, int r, const float* q, const float* mu,
     return 0;
 }
 
+int orc_share_pool(const orc_layout* L, const double* head_mass, double* page_share) {
+    if (!layout_ok(L)) return -1;
+    const int H = L->num_kv_heads, Hq = L->num_q_heads, G = Hq / H, MP = L->max_pages;
+    double* z = (double*)malloc(sizeof(double) * (size_t)Hq);
+    double* terms = (double*)malloc(sizeof(double) * (size_t)G);
+    if (!z || !terms) {
+        free(z);
+        free(terms);
+        return -1;
+    }
+    for (int b = 0; b < L->batch; ++b) {
+        const int full = full_pages(L, b);
+        /* each head's total estimated mass over the sequence's full pages */
+        for (int h = 0; h < Hq; ++h) z[h] = orc_lse(full, head_mass + ((size_t)b * Hq + h) * MP);
+        for (int g = 0; g < H; ++g)
+            for (int j = 0; j < MP; ++j) {
+                double v = -INFINITY;
+                if (j < full) {
+                    for (int hh = 0; hh < G; ++hh) {
+                        const int h = g * G + hh;
+                        terms[hh] = head_mass[((size_t)b * Hq + h) * MP + j] - z[h];
+                    }
+                    v = orc_lse(G, terms) - log((double)G); /* log of the mean share */
+                }
+                page_share[((size_t)b * H + g) * MP + j] = v;
+            }
+    }
+    free(z);
+    free(terms);
+    return 0;
+}
+
 int orc_exact_pool(const orc_layout* L, const float* q, const float* k_pool, double* head_lse,
                    double* page_lse, int nthreads) {
     if (!layout_ok(L)) return -1;

@@ -117,6 +117,15 @@ int orc_scan_units(const orc_layout* L, int r, const float* q, const float* mu,
                    const float* basis, const float* coef, int n, const int32_t* ub,
                    const int32_t* ug, const int32_t* uj, double* head_mass, double* page_mass);
 
+/* Mean-of-share group score (technical summary, section 2, Group-Shared
+ * Selection: the heads' estimated mass shares are averaged over the group
+ * into one table).  For every (b, g) and full page j:
+ *   share_{j,h} = exp(s_{j,h} - Z_h),  Z_h = LSE over the full pages j' of s_{j',h},
+ *   page_share[b][g][j] = log( (1/G) sum_{h in g} share_{j,h} ),
+ * from per-head estimates head_mass [B][Hq][max_pages] (as orc_scan_pool
+ * writes them).  Entries of pages that are not full are -inf. */
+int orc_share_pool(const orc_layout* L, const double* head_mass, double* page_share);
+
 /* Exact ("read every key") page masses: head_lse [B][Hq][max_pages] over every
  * page including a partial last one, page_lse [B][Hkv][max_pages] = LSE over
  * the group's heads; -inf past the last page.  Either output may be NULL. */

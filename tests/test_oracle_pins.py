@@ -234,6 +234,60 @@ def test_scan_group_aggregation(wl, orc):
     np.testing.assert_array_equal(h1, p1)
 
 
+def _share_layout(orc, B, Hq, Hkv, P, lens, MP):
+    bt = np.arange(B * MP, dtype=np.int32).reshape(B, MP)
+    return orc.Layout(Hq, Hkv, 8, P, bt, np.asarray(lens, np.int32))
+
+
+def _random_heads(B, Hq, MP, lens, P, seed):
+    g = np.random.default_rng(seed)
+    hm = g.normal(3.0, 2.0, (B, Hq, MP))
+    for b in range(B):
+        hm[b, :, lens[b] // P:] = -np.inf
+    return hm
+
+
+def test_mean_share_sums_to_one_and_ignores_head_shifts(orc):
+    """Mean-of-share scores (technical summary, section 2, Group-Shared
+    Selection): every head's shares over the full pages sum to 1, so their
+    mean does too; a per-head shift of the estimates cancels in the share
+    (while the LSE aggregation would move); non-full pages are -inf."""
+    B, Hq, Hkv, P, MP = 2, 8, 2, 16, 50
+    lens = [16 * 50, 16 * 31 + 5]
+    lay = _share_layout(orc, B, Hq, Hkv, P, lens, MP)
+    hm = _random_heads(B, Hq, MP, lens, P, 7)
+    sh = orc.share_pool(lay, hm)
+    for b in range(B):
+        f = lens[b] // P
+        np.testing.assert_allclose(np.exp(sh[b, :, :f]).sum(axis=-1), 1.0, atol=1e-12)
+        assert np.all(sh[b, :, f:] == -np.inf)
+    shift = np.random.default_rng(8).normal(0, 5, (1, Hq, 1))
+    sh2 = orc.share_pool(lay, hm + shift)
+    fin = np.isfinite(sh)
+    np.testing.assert_allclose(sh2[fin], sh[fin], atol=1e-12)
+
+
+def test_mean_share_special_cases(orc):
+    """G = 1: the share is the head's estimate minus its total (a shift), so
+    the selection equals the LSE-aggregation selection.  Identical heads: the
+    mean share is each head's share."""
+    B, P, MP = 1, 16, 40
+    lens = [16 * 40]
+    lay1 = _share_layout(orc, B, 2, 2, P, lens, MP)
+    hm = _random_heads(B, 2, MP, lens, P, 9)
+    sh = orc.share_pool(lay1, hm)
+    for h in range(2):
+        np.testing.assert_allclose(sh[0, h], hm[0, h] - logsumexp(hm[0, h]), atol=1e-12)
+    sel_share, _ = orc.select_pool(lay1, 16 * 8, sh.astype(np.float32), 8)
+    sel_lse, _ = orc.select_pool(lay1, 16 * 8, (hm - logsumexp(hm, axis=-1, keepdims=True))
+                                 .astype(np.float32), 8)
+    np.testing.assert_array_equal(sel_share, sel_lse)
+    lay4 = _share_layout(orc, B, 4, 1, P, lens, MP)
+    one = _random_heads(B, 1, MP, lens, P, 10)
+    sh4 = orc.share_pool(lay4, np.repeat(one, 4, axis=1))
+    np.testing.assert_allclose(sh4[0, 0], one[0, 0] - logsumexp(one[0, 0]), atol=1e-12)
+
+
 def test_scan_full_rank_equals_exact(wl, orc):
     """Pool-level P1 on the tiny workload at r = min(P, d) = 16, with the
     summaries kept in double (build_units) so only rounding remains."""
