@@ -273,6 +273,22 @@ def main():
             g.close()
         log(f"bf16 summaries: step {step16:.2f} us, scan {scan16:.2f} us, {gbs16:.0f} GB/s")
 
+    # --- the same step with the mean-of-share group aggregation (fp32 summaries)
+    gm = [lk.StepGraph(q, summs[i], kvs[i], pages, spec.budget_tokens, *bufs[i][:4], ws=bufs[i][4],
+                       agg=lk.AGG_MEAN_SHARE) for i in range(L)]
+    for i in range(args.warmup):
+        gm[i % L].launch()
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        gm[i % L].launch()
+    e1.record()
+    torch.cuda.synchronize()
+    share_step = e0.elapsed_time(e1) * 1e3 / args.steps
+    for g_ in gm:
+        g_.close()
+    log(f"mean-of-share aggregation: step {share_step:.2f} us")
+
     # --- dense baseline
     dense_mean = None
     dense_b = traffic.dense_bytes(sum(-(-n // P) for n in spec.seq_lens), Hkv, d, P)
@@ -334,6 +350,7 @@ def main():
             "build_ms": round(build_ms, 3),
             "build_pages_per_s": round(full_total * Hkv / (build_ms * 1e-3), 1),
             "bf16_summaries": bf16_summ,
+            "mean_share_step_us": round(share_step, 3),
         },
     }
     for g in graphs:

@@ -82,6 +82,12 @@ typedef enum {
 
 typedef enum { LOCKS_F32 = 0, LOCKS_BF16 = 1 } locks_dtype;
 
+/* How the heads of a GQA group are combined into one page score
+ * (technical summary, section 2, Group-Shared Selection).  LSE: the log of
+ * the sum of the heads' estimated masses.  MEAN_SHARE: the log of the mean
+ * over the heads of each head's share of its own total estimated mass. */
+typedef enum { LOCKS_AGG_LSE = 0, LOCKS_AGG_MEAN_SHARE = 1 } locks_agg;
+
 /* Operations for locks_workspace_bytes(). */
 typedef enum {
     LOCKS_OP_BUILD = 0,
@@ -159,9 +165,11 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
  *   s_hat_{j,h} = log sum_i exp((beta + t . c_i) / sqrt(d))
  * (technical summary, section 2, Reconstructie en Selectie, the displayed
  * estimator; the LSE of the reconstructed logits is the page's mass).
- * Group score a_{j,g} = log sum_{h in g} exp(s_hat_{j,h}): one shared
- * selection per GQA group (section 2, Group-Shared Selection; the group
- * score is read here as the sum of the heads' unnormalised masses).
+ * Group score, one shared selection per GQA group (section 2, Group-Shared
+ * Selection), by agg: LOCKS_AGG_LSE a_{j,g} = log sum_{h in g} exp(s_hat_{j,h})
+ * (the sum of the heads' unnormalised masses); LOCKS_AGG_MEAN_SHARE
+ * a_{j,g} = log (1/G) sum_{h in g} exp(s_hat_{j,h} - Z_h), Z_h = log sum over
+ * the full pages j' of exp(s_hat_{j',h}) (the heads' mean mass share).
  * Selection: k_b = min(floor(budget_tokens / P), full pages of b) pages
  * with the largest a (equal fp32 values: lowest j first), written in
  * ascending j to sel_pages / sel_logmass rows of width floor(budget/P),
@@ -174,7 +182,7 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
  * page_logmass is given (then, without one, the top-k reads every mass).
  */
 locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
-                          const locks_page_table* pages, int32_t budget_tokens,
+                          const locks_page_table* pages, int32_t budget_tokens, int32_t agg,
                           int32_t* sel_pages, float* sel_logmass, float* page_logmass, void* ws,
                           size_t ws_bytes, void* stream);
 
@@ -208,6 +216,20 @@ locks_status locks_topk(const float* page_logmass, const locks_page_table* pages
                         const float* run_max, void* stream);
 
 /*
+ * The LOCKS_AGG_MEAN_SHARE group score alone, from per-head estimates
+ * head_logmass [B][H_q][max_pages] (as locks_scan writes them; entries of
+ * pages that are not full are ignored): page_logmass [B][H_kv][max_pages]
+ * gets a_{j,g} of locks_select's MEAN_SHARE rule (-inf for pages that are
+ * not full); run_max (optional) the run maxima of those scores as
+ * locks_scan defines them.  Workspace: B * H_q floats (the totals Z_h),
+ * locks_workspace_bytes(LOCKS_OP_SELECT, ...) suffices.
+ */
+locks_status locks_mean_share(const float* head_logmass, int32_t num_q_heads,
+                              int32_t num_kv_heads, const locks_page_table* pages,
+                              int32_t page_size, float* page_logmass, float* run_max, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
  * Step 3 - attention of every query head over the tokens of its group's
  * selected pages plus the sequence's partial last page (abstract: only the
  * top pages are attended).  The softmax is renormalised over exactly these
@@ -236,6 +258,7 @@ typedef struct {
     const float* q;
     int32_t num_q_heads;
     int32_t budget_tokens;
+    int32_t agg;          /* locks_agg */
     locks_summaries summaries;
     locks_kv_cache cache;
     locks_page_table pages;

@@ -21,9 +21,10 @@ LOCKS_OK, LOCKS_ERR_INVALID_ARG, LOCKS_ERR_UNSUPPORTED, LOCKS_ERR_WORKSPACE, LOC
 LOCKS_F32, LOCKS_BF16 = 0, 1
 OP_BUILD, OP_SELECT, OP_SPARSE_ATTEND, OP_DENSE_ATTEND, OP_STEP = range(5)
 RUN_PAGES = 16  # pages per run maximum (LOCKS_RUN_PAGES)
+AGG_LSE, AGG_MEAN_SHARE = 0, 1  # locks_agg
 
 EXPORTED = ("locks_workspace_bytes", "locks_build_summaries", "locks_select", "locks_scan",
-            "locks_topk", "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
+            "locks_topk", "locks_mean_share", "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
             "locks_step_graph_launch", "locks_step_graph_destroy", "locks_status_string",
             "locks_last_hip_error", "locks_version")
 
@@ -58,7 +59,8 @@ class CPageTable(ctypes.Structure):
 
 class CStepArgs(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("num_q_heads", ctypes.c_int32),
-                ("budget_tokens", ctypes.c_int32), ("summaries", CSummaries),
+                ("budget_tokens", ctypes.c_int32), ("agg", ctypes.c_int32),
+                ("summaries", CSummaries),
                 ("cache", CKVCache), ("pages", CPageTable), ("sel_pages", ctypes.c_void_p),
                 ("sel_logmass", ctypes.c_void_p), ("page_logmass", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("out_lse", ctypes.c_void_p), ("ws", ctypes.c_void_p),
@@ -81,8 +83,9 @@ def lib() -> ctypes.CDLL:
         L.locks_workspace_bytes.restype = sz
         L.locks_build_summaries.argtypes = [P(CKVCache), P(CPageTable), vp, P(CSummaries), vp, sz,
                                             vp]
-        L.locks_select.argtypes = [vp, i32, P(CSummaries), P(CPageTable), i32, vp, vp, vp, vp, sz,
-                                   vp]
+        L.locks_select.argtypes = [vp, i32, P(CSummaries), P(CPageTable), i32, i32, vp, vp, vp,
+                                   vp, sz, vp]
+        L.locks_mean_share.argtypes = [vp, i32, i32, P(CPageTable), i32, vp, vp, vp, sz, vp]
         L.locks_scan.argtypes = [vp, i32, P(CSummaries), P(CPageTable), vp, vp, vp, vp]
         L.locks_topk.argtypes = [vp, P(CPageTable), i32, i32, i32, i32, vp, vp, vp, vp]
         L.locks_sparse_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, i32, vp, vp,
@@ -97,6 +100,7 @@ def lib() -> ctypes.CDLL:
         L.locks_last_hip_error.restype = i32
         L.locks_version.restype = i32
         for fn in ("locks_build_summaries", "locks_select", "locks_scan", "locks_topk",
+                   "locks_mean_share",
                    "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
                    "locks_step_graph_launch"):
             getattr(L, fn).restype = i32
@@ -211,12 +215,21 @@ def locks_topk(page_logmass, pages: PageTable, page_size, budget_tokens, sel_pag
 
 
 def locks_select(q, summaries: Summaries, pages: PageTable, budget_tokens, sel_pages, sel_logmass,
-                 page_logmass=None, ws=None, stream=None):
+                 page_logmass=None, ws=None, stream=None, agg=AGG_LSE):
     sc, pc = summaries.c(), pages.c()
     _check(lib().locks_select(_ptr(q), q.shape[1], ctypes.byref(sc), ctypes.byref(pc),
-                              budget_tokens, _ptr(sel_pages), _ptr(sel_logmass),
+                              budget_tokens, agg, _ptr(sel_pages), _ptr(sel_logmass),
                               _ptr(page_logmass), _ptr(ws), 0 if ws is None else ws.numel(),
                               _stream(stream)), "locks_select")
+
+
+def locks_mean_share(head_logmass, num_kv_heads, pages: PageTable, page_size, page_logmass,
+                     run_max=None, ws=None, stream=None):
+    pc = pages.c()
+    _check(lib().locks_mean_share(_ptr(head_logmass), head_logmass.shape[1], num_kv_heads,
+                                  ctypes.byref(pc), page_size, _ptr(page_logmass), _ptr(run_max),
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "locks_mean_share")
 
 
 def locks_sparse_attend(q, cache: PagedKV, pages: PageTable, sel_pages, out, out_lse=None, ws=None,
@@ -242,10 +255,11 @@ class StepGraph:
     """One decode step (select + sparse attend) captured as a HIP graph."""
 
     def __init__(self, q, summaries: Summaries, cache: PagedKV, pages: PageTable, budget_tokens,
-                 sel_pages, sel_logmass, out, out_lse=None, page_logmass=None, ws=None):
+                 sel_pages, sel_logmass, out, out_lse=None, page_logmass=None, ws=None,
+                 agg=AGG_LSE):
         self._keep = (q, summaries, cache, pages, sel_pages, sel_logmass, out, out_lse,
                       page_logmass, ws)
-        a = CStepArgs(q.data_ptr(), q.shape[1], budget_tokens, summaries.c(), cache.c(),
+        a = CStepArgs(q.data_ptr(), q.shape[1], budget_tokens, agg, summaries.c(), cache.c(),
                       pages.c(), sel_pages.data_ptr(), sel_logmass.data_ptr(),
                       None if page_logmass is None else page_logmass.data_ptr(), out.data_ptr(),
                       None if out_lse is None else out_lse.data_ptr(),

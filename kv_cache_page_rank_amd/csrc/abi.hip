@@ -52,13 +52,21 @@ locks_status check_cache(const locks_kv_cache* kv, bool need_v) {
 
 int32_t num_runs(int32_t max_pages) { return (max_pages + locks::kRunPages - 1) / locks::kRunPages; }
 
-// Selection workspace: page masses, then the run maxima.
+// Selection workspace: page masses, run maxima, per-head estimates and
+// per-head totals (the last two for the mean-of-share aggregation).
 size_t select_mass_bytes(int32_t batch, int32_t max_pages, int32_t hkv) {
     return align_up((size_t)batch * hkv * max_pages * sizeof(float));
 }
-size_t select_ws(int32_t batch, int32_t max_pages, int32_t hkv) {
-    return select_mass_bytes(batch, max_pages, hkv) +
-           align_up((size_t)batch * hkv * num_runs(max_pages) * sizeof(float));
+size_t select_run_bytes(int32_t batch, int32_t max_pages, int32_t hkv) {
+    return align_up((size_t)batch * hkv * num_runs(max_pages) * sizeof(float));
+}
+size_t select_head_bytes(int32_t batch, int32_t max_pages, int32_t hq) {
+    return align_up((size_t)batch * hq * max_pages * sizeof(float));
+}
+size_t total_bytes(int32_t batch, int32_t hq) { return align_up((size_t)batch * hq * sizeof(float)); }
+size_t select_ws(int32_t batch, int32_t max_pages, int32_t hq, int32_t hkv) {
+    return select_mass_bytes(batch, max_pages, hkv) + select_run_bytes(batch, max_pages, hkv) +
+           select_head_bytes(batch, max_pages, hq) + total_bytes(batch, hq);
 }
 
 size_t attend_ws(int32_t batch, int32_t hq, int32_t d, int32_t splits) {
@@ -160,6 +168,24 @@ locks_status topk_common(const float* page_logmass, const locks_page_table* pt, 
     return e == hipSuccess ? LOCKS_OK : hip_fail(e);
 }
 
+locks_status share_common(const float* head_logmass, int32_t hq, int32_t hkv,
+                          const locks_page_table* pt, int32_t page_size, float* head_total,
+                          float* page_logmass, float* run_max, hipStream_t stream) {
+    locks::ShareParams p{};
+    p.head_logmass = head_logmass;
+    p.seq_lens = pt->seq_lens;
+    p.batch = pt->batch;
+    p.num_q_heads = hq;
+    p.num_kv_heads = hkv;
+    p.max_pages = pt->max_pages;
+    p.page_size = page_size;
+    p.head_total = head_total;
+    p.page_logmass = page_logmass;
+    p.run_max = run_max;
+    const hipError_t e = locks::launch_share(p, stream);
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
 }  // namespace
 
 struct locks_step_graph {
@@ -179,13 +205,13 @@ size_t locks_workspace_bytes(int32_t op, int32_t batch, int32_t max_pages, int32
         case LOCKS_OP_BUILD:
             return 0;
         case LOCKS_OP_SELECT:
-            return select_ws(batch, max_pages, num_kv_heads);
+            return select_ws(batch, max_pages, num_q_heads, num_kv_heads);
         case LOCKS_OP_SPARSE_ATTEND:
             return attend_ws(batch, num_q_heads, head_dim, (k_pages < 0 ? 0 : k_pages) + 1);
         case LOCKS_OP_DENSE_ATTEND:
             return attend_ws(batch, num_q_heads, head_dim, dense_splits(batch, num_kv_heads, max_pages));
         case LOCKS_OP_STEP:
-            return select_ws(batch, max_pages, num_kv_heads) +
+            return select_ws(batch, max_pages, num_q_heads, num_kv_heads) +
                    attend_ws(batch, num_q_heads, head_dim, (k_pages < 0 ? 0 : k_pages) + 1);
         default:
             return 0;
@@ -254,7 +280,7 @@ locks_status locks_topk(const float* page_logmass, const locks_page_table* pages
 }
 
 locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
-                          const locks_page_table* pages, int32_t budget_tokens,
+                          const locks_page_table* pages, int32_t budget_tokens, int32_t agg,
                           int32_t* sel_pages, float* sel_logmass, float* page_logmass, void* ws,
                           size_t ws_bytes, void* stream) {
     locks_status st = check_summaries(summaries, true);
@@ -262,29 +288,57 @@ locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summa
     if ((st = check_page_table(pages)) != LOCKS_OK) return st;
     if (!q || budget_tokens < 0 || !head_dims_ok(num_q_heads, summaries->num_kv_heads))
         return LOCKS_ERR_INVALID_ARG;
+    if (agg != LOCKS_AGG_LSE && agg != LOCKS_AGG_MEAN_SHARE) return LOCKS_ERR_INVALID_ARG;
     const int32_t width = budget_tokens / summaries->page_size;
     if (width > 0 && !sel_pages) return LOCKS_ERR_INVALID_ARG;
-    // The workspace holds the page masses (unless the caller takes them) and
-    // the run maxima; without a workspace the top-k reads every mass.
-    const bool have_ws =
-        ws && ws_bytes >= select_ws(pages->batch, pages->max_pages, summaries->num_kv_heads);
+    // The workspace holds the page masses (unless the caller takes them), the
+    // run maxima and, for the mean-of-share aggregation, the per-head
+    // estimates and totals; without a workspace (LSE only) the top-k reads
+    // every mass.
+    const int32_t B = pages->batch, MP = pages->max_pages, hkv = summaries->num_kv_heads;
+    const bool have_ws = ws && ws_bytes >= select_ws(B, MP, num_q_heads, hkv);
+    if (agg == LOCKS_AGG_MEAN_SHARE && !have_ws) return LOCKS_ERR_WORKSPACE;
     float* masses = page_logmass;
     if (!masses) {
         if (!have_ws) return LOCKS_ERR_WORKSPACE;
         masses = static_cast<float*>(ws);
     }
-    float* run_max = nullptr;
-    if (have_ws)
-        run_max = reinterpret_cast<float*>(
-            static_cast<char*>(ws) +
-            select_mass_bytes(pages->batch, pages->max_pages, summaries->num_kv_heads));
+    char* wsb = static_cast<char*>(ws);
+    float* run_max =
+        have_ws ? reinterpret_cast<float*>(wsb + select_mass_bytes(B, MP, hkv)) : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = scan_common(q, num_q_heads, summaries, pages, masses, nullptr, run_max, s)) !=
-        LOCKS_OK)
+    if (agg == LOCKS_AGG_MEAN_SHARE) {
+        const size_t heads_off = select_mass_bytes(B, MP, hkv) + select_run_bytes(B, MP, hkv);
+        float* heads = reinterpret_cast<float*>(wsb + heads_off);
+        float* totals =
+            reinterpret_cast<float*>(wsb + heads_off + select_head_bytes(B, MP, num_q_heads));
+        if ((st = scan_common(q, num_q_heads, summaries, pages, masses, heads, nullptr, s)) !=
+            LOCKS_OK)
+            return st;
+        if ((st = share_common(heads, num_q_heads, hkv, pages, summaries->page_size, totals,
+                               masses, run_max, s)) != LOCKS_OK)
+            return st;
+    } else if ((st = scan_common(q, num_q_heads, summaries, pages, masses, nullptr, run_max, s)) !=
+               LOCKS_OK) {
         return st;
+    }
     if (width == 0) return LOCKS_OK;
     return topk_common(masses, pages, summaries->num_kv_heads, summaries->page_size, budget_tokens,
                        width, sel_pages, sel_logmass, run_max, s);
+}
+
+locks_status locks_mean_share(const float* head_logmass, int32_t num_q_heads,
+                              int32_t num_kv_heads, const locks_page_table* pages,
+                              int32_t page_size, float* page_logmass, float* run_max, void* ws,
+                              size_t ws_bytes, void* stream) {
+    locks_status st = check_page_table(pages);
+    if (st != LOCKS_OK) return st;
+    if (!head_logmass || !page_logmass || page_size <= 0 || !head_dims_ok(num_q_heads, num_kv_heads))
+        return LOCKS_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < total_bytes(pages->batch, num_q_heads)) return LOCKS_ERR_WORKSPACE;
+    return share_common(head_logmass, num_q_heads, num_kv_heads, pages, page_size,
+                        static_cast<float*>(ws), page_logmass, run_max,
+                        static_cast<hipStream_t>(stream));
 }
 
 locks_status locks_sparse_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,
@@ -312,7 +366,7 @@ locks_status locks_step_graph_create(const locks_step_args* a, locks_step_graph*
     *graph = nullptr;
     const int32_t k = a->summaries.page_size > 0 ? a->budget_tokens / a->summaries.page_size : 0;
     const size_t sel_bytes =
-        select_ws(a->pages.batch, a->pages.max_pages, a->summaries.num_kv_heads);
+        select_ws(a->pages.batch, a->pages.max_pages, a->num_q_heads, a->summaries.num_kv_heads);
     const size_t need = locks_workspace_bytes(LOCKS_OP_STEP, a->pages.batch, a->pages.max_pages,
                                               a->num_q_heads, a->summaries.num_kv_heads,
                                               a->summaries.page_size, a->summaries.head_dim,
@@ -331,7 +385,7 @@ locks_status locks_step_graph_create(const locks_step_args* a, locks_step_graph*
         return hip_fail(e);
     }
     locks_status st = locks_select(a->q, a->num_q_heads, &a->summaries, &a->pages, a->budget_tokens,
-                                   a->sel_pages, a->sel_logmass, a->page_logmass, a->ws, a->ws_bytes,
+                                   a->agg, a->sel_pages, a->sel_logmass, a->page_logmass, a->ws, a->ws_bytes,
                                    s);
     if (st == LOCKS_OK) {
         void* attn_ws = static_cast<char*>(a->ws) + sel_bytes;
@@ -390,6 +444,6 @@ const char* locks_status_string(int32_t status) {
 
 int32_t locks_last_hip_error(void) { return g_last_hip_error; }
 
-int32_t locks_version(void) { return 102; }
+int32_t locks_version(void) { return 103; }
 
 }  // extern "C"

@@ -30,6 +30,17 @@ struct ScanParams {
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 bool scan_supported(int page_size, int head_dim, int rank);
 
+// Mean-of-share group scores from per-head estimates.
+struct ShareParams {
+    const float* head_logmass;  // [B][Hq][max_pages]
+    const int32_t* seq_lens;
+    int32_t batch, num_q_heads, num_kv_heads, max_pages, page_size;
+    float* head_total;          // [B][Hq] workspace
+    float* page_logmass;        // [B][Hkv][max_pages]
+    float* run_max;             // [B][Hkv][ceil(max_pages / kRunPages)] or null
+};
+hipError_t launch_share(const ShareParams& p, hipStream_t s);
+
 struct TopkParams {
     const float* page_logmass;  // [B][Hkv][max_pages]
     const int32_t* seq_lens;

@@ -39,7 +39,7 @@ def test_header_symbols_exported(lk):
 
 def test_version_and_status_strings(lk):
     lib = lk.lib()
-    assert lib.locks_version() == 102
+    assert lib.locks_version() == 103
     assert lib.locks_status_string(0) == b"ok"
     assert b"workspace" in lib.locks_status_string(3)
     assert lib.locks_status_string(99) == b"unknown status"
@@ -47,10 +47,12 @@ def test_version_and_status_strings(lk):
 
 def test_workspace_sizes(lk):
     ws = lk.workspace_bytes
-    # select: page masses [B][Hkv][max_pages] fp32, then run maxima
-    # [B][Hkv][ceil(max_pages / 16)], each 256-byte aligned
-    assert ws(lk.OP_SELECT, 1, 16384, 32, 2, 64, 128, 8, 32) == 2 * 16384 * 4 + 2 * 1024 * 4
-    assert ws(lk.OP_SELECT, 1, 100, 32, 2, 64, 128, 8, 32) == 1024 + 256
+    # select: page masses [B][Hkv][max_pages] fp32, run maxima
+    # [B][Hkv][ceil(max_pages / 16)], per-head estimates [B][Hq][max_pages] and
+    # per-head totals [B][Hq], each 256-byte aligned
+    assert ws(lk.OP_SELECT, 1, 16384, 32, 2, 64, 128, 8, 32) == \
+        2 * 16384 * 4 + 2 * 1024 * 4 + 32 * 16384 * 4 + 256
+    assert ws(lk.OP_SELECT, 1, 100, 32, 2, 64, 128, 8, 32) == 1024 + 256 + 12800 + 256
     # sparse attend: (k + 1) splits of (2 + d) floats per query head
     assert ws(lk.OP_SPARSE_ATTEND, 1, 16384, 32, 2, 64, 128, 8, 32) == \
         256 * ((32 * 33 * 2 * 4 + 255) // 256) + 32 * 33 * 128 * 4
@@ -76,7 +78,7 @@ def test_host_validation_rejects_without_launch(lk):
     by = ctypes.byref
     kv, sm, pt, p = _fake(lk)
     # null query
-    assert lib.locks_select(None, 32, by(sm), by(pt), 2048, p, p, p, p, 1 << 20, None) == \
+    assert lib.locks_select(None, 32, by(sm), by(pt), 2048, 0, p, p, p, p, 1 << 20, None) == \
         lk.LOCKS_ERR_INVALID_ARG
     # H_q not a multiple of H_kv
     assert lib.locks_scan(p, 31, by(sm), by(pt), p, None, None, None) == lk.LOCKS_ERR_INVALID_ARG
@@ -92,7 +94,7 @@ def test_host_validation_rejects_without_launch(lk):
     assert lib.locks_dense_attend(p, 32, by(kv_p), by(pt), p, None, p, 1 << 30, None) == \
         lk.LOCKS_ERR_UNSUPPORTED
     # workspace missing / too small
-    assert lib.locks_select(p, 32, by(sm), by(pt), 2048, p, p, None, None, 0, None) == \
+    assert lib.locks_select(p, 32, by(sm), by(pt), 2048, 0, p, p, None, None, 0, None) == \
         lk.LOCKS_ERR_WORKSPACE
     assert lib.locks_sparse_attend(p, 32, by(kv), by(pt), p, 32, p, None, p, 16, None) == \
         lk.LOCKS_ERR_WORKSPACE
@@ -100,10 +102,19 @@ def test_host_validation_rejects_without_launch(lk):
     _, _, pt_big, _ = _fake(lk, MP=40000)
     assert lib.locks_scan(p, 32, by(sm), by(pt_big), p, None, None, None) == lk.LOCKS_ERR_UNSUPPORTED
     # negative budget, bad dtype, mismatched build shapes
-    assert lib.locks_select(p, 32, by(sm), by(pt), -1, p, p, p, p, 1 << 20, None) == \
+    assert lib.locks_select(p, 32, by(sm), by(pt), -1, 0, p, p, p, p, 1 << 20, None) == \
         lk.LOCKS_ERR_INVALID_ARG
     kv_bad, _, _, _ = _fake(lk, dtype=7)
     assert lib.locks_dense_attend(p, 32, by(kv_bad), by(pt), p, None, p, 1 << 30, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    # unknown aggregation; mean-of-share without workspace
+    assert lib.locks_select(p, 32, by(sm), by(pt), 2048, 7, p, p, p, p, 1 << 20, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_select(p, 32, by(sm), by(pt), 2048, 1, p, p, p, None, 0, None) == \
+        lk.LOCKS_ERR_WORKSPACE
+    assert lib.locks_mean_share(p, 32, 2, by(pt), 64, p, None, None, 0, None) == \
+        lk.LOCKS_ERR_WORKSPACE
+    assert lib.locks_mean_share(None, 32, 2, by(pt), 64, p, None, p, 1024, None) == \
         lk.LOCKS_ERR_INVALID_ARG
     _, sm_dt, _, _ = _fake(lk, sdtype=5)  # summary dtype neither fp32 nor bf16
     assert lib.locks_scan(p, 32, by(sm_dt), by(pt), p, None, None, None) == lk.LOCKS_ERR_INVALID_ARG
@@ -118,7 +129,7 @@ def test_host_validation_rejects_without_launch(lk):
     # graph creation validates before capturing
     h = ctypes.c_void_p()
     assert lib.locks_step_graph_create(None, by(h)) == lk.LOCKS_ERR_INVALID_ARG
-    args = lk.CStepArgs(0x1000, 32, 2048, sm, kv, pt, 0x1000, 0x1000, None, 0x1000, None, None, 0)
+    args = lk.CStepArgs(0x1000, 32, 2048, 0, sm, kv, pt, 0x1000, 0x1000, None, 0x1000, None, None, 0)
     assert lib.locks_step_graph_create(by(args), by(h)) == lk.LOCKS_ERR_WORKSPACE
     assert lib.locks_step_graph_launch(None, None) == lk.LOCKS_ERR_INVALID_ARG
     lib.locks_step_graph_destroy(None)

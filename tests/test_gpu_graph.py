@@ -10,11 +10,12 @@ from workload.device import summaries_to_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("mk,sdt", [(lambda: tiny(), torch.float32),
-                                    (lambda: bf16_small(), torch.float32),
-                                    (lambda: bf16_small(), torch.bfloat16)],
-                         ids=["tiny", "bf16", "bf16-summaries"])
-def test_graph_replay_equals_eager(mk, sdt):
+@pytest.mark.parametrize("mk,sdt,agg", [(lambda: tiny(), torch.float32, 0),
+                                        (lambda: bf16_small(), torch.float32, 0),
+                                        (lambda: bf16_small(), torch.bfloat16, 0),
+                                        (lambda: bf16_small(), torch.float32, 1)],
+                         ids=["tiny", "bf16", "bf16-summaries", "mean-share"])
+def test_graph_replay_equals_eager(mk, sdt, agg):
     import kv_cache_page_rank_amd as lk
     case = Case(mk())
     s = case.spec
@@ -34,7 +35,8 @@ def test_graph_replay_equals_eager(mk, sdt):
 
     e = bufs()
     say("eager step")
-    lk.locks_select(case.q, summ, case.pages, s.budget_tokens, e["sel"], e["mass"], ws=e["ws"])
+    lk.locks_select(case.q, summ, case.pages, s.budget_tokens, e["sel"], e["mass"], ws=e["ws"],
+                    agg=agg)
     attn_ws = e["ws"][lk.workspace_bytes(lk.OP_SELECT, s.batch, s.max_pages, s.num_q_heads,
                                          s.num_kv_heads, s.page_size, s.head_dim, s.rank, k):]
     lk.locks_sparse_attend(case.q, case.kv, case.pages, e["sel"], e["out"], e["lse"], ws=attn_ws)
@@ -43,7 +45,7 @@ def test_graph_replay_equals_eager(mk, sdt):
     g = bufs()
     say("graph create")
     graph = lk.StepGraph(case.q, summ, case.kv, case.pages, s.budget_tokens, g["sel"], g["mass"],
-                         g["out"], g["lse"], ws=g["ws"])
+                         g["out"], g["lse"], ws=g["ws"], agg=agg)
     for rep in range(4):
         for t in (g["sel"], g["mass"], g["out"], g["lse"]):
             t.zero_()  # eager work between replays

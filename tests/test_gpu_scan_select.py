@@ -281,6 +281,78 @@ def test_select_equals_topk_of_its_masses(mk):
     assert torch.equal(mass, mass2)
 
 
+SHARE_CASES = [  # B, Hq, Hkv, max_pages, page_size, seq_lens
+    (2, 32, 2, 2000, 64, [64 * 2000, 64 * 1234 + 17]),
+    (3, 32, 8, 700, 64, [64 * 700, 64 * 3, 64 * 511 + 63]),
+    (1, 6, 2, 300, 16, [16 * 299 + 4]),
+    (2, 4, 4, 50, 64, [64 * 50, 0]),
+]
+
+
+@pytest.mark.parametrize("case", SHARE_CASES, ids=[f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}" for c in SHARE_CASES])
+def test_mean_share_matches_oracle(case):
+    """Mean-of-share scores from identical fp32 per-head estimates: within
+    2e-5 of the oracle (fp32 exp/log against fp64), -inf exactly where a page
+    is not full; the run maxima are exactly the maxima of the written scores."""
+    B, Hq, Hkv, MP, P, lens = case
+    rng = np.random.default_rng(Hq * 1000 + MP)
+    hm = rng.normal(2.0, 3.0, (B, Hq, MP)).astype(np.float32)
+    for b in range(B):
+        hm[b, :, lens[b] // P:] = np.nan  # never read: past the full pages
+    bt = np.zeros((B, MP), np.int32)
+    lay = oracle.Layout(Hq, Hkv, 8, P, bt, np.asarray(lens, np.int32))
+    ref = oracle.share_pool(lay, np.where(np.isnan(hm), -np.inf, hm).astype(np.float64))
+    import kv_cache_page_rank_amd as lk
+    pages = lk.PageTable(torch.from_numpy(bt).to(DEV), torch.from_numpy(np.asarray(lens, np.int32)).to(DEV))
+    out = torch.full((B, Hkv, MP), 7.0, device=DEV)
+    rm = torch.full((B, Hkv, -(-MP // RUN)), 7.0, device=DEV)
+    ws = lk.workspace(lk.workspace_bytes(lk.OP_SELECT, B, MP, Hq, Hkv, P, 128, 8, 1))
+    say("mean share", case)
+    lk.locks_mean_share(torch.from_numpy(hm).to(DEV), Hkv, pages, P, out, run_max=rm, ws=ws)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    assert np.abs(got[fin] - ref[fin]).max() <= 2e-5
+    np.testing.assert_array_equal(to_np(rm), host_run_max(got, lens, P))
+
+
+@pytest.mark.parametrize("mk", [lambda: tiny(num_q_heads=4, num_kv_heads=1, seq_lens=[1000]),
+                                lambda: bf16_small(), lambda: bf16_small(num_kv_heads=8)],
+                         ids=["tiny-G4", "bf16-G16", "bf16-G4"])
+def test_select_mean_share_band(mk):
+    """locks_select with the mean-of-share aggregation against the oracle on
+    the same summaries: scores within 1e-4, selections equal up to the 1e-3
+    band around the k-th score, and equal to the top-k of its own scores."""
+    case = Case(mk())
+    s = case.spec
+    mu, basis, coef = case.oracle_summaries()
+    head_o, _ = oracle.scan_pool(case.lay, s.rank, case.layer.q, mu, basis, coef)
+    share_o = oracle.share_pool(case.lay, head_o)
+    k = s.k_pages
+    sel_o, _ = oracle.select_pool(case.lay, s.budget_tokens, share_o.astype(np.float32), k)
+    import kv_cache_page_rank_amd as lk
+    sel = torch.empty((s.batch, s.num_kv_heads, k), dtype=torch.int32, device=DEV)
+    mass = torch.empty((s.batch, s.num_kv_heads, k), device=DEV)
+    pm = torch.empty((s.batch, s.num_kv_heads, s.max_pages), device=DEV)
+    ws = lk.workspace(lk.workspace_bytes(lk.OP_SELECT, s.batch, s.max_pages, s.num_q_heads,
+                                         s.num_kv_heads, s.page_size, s.head_dim, s.rank, k))
+    say("select mean share", s)
+    lk.locks_select(case.q, summaries_to_device(mu, basis, coef), case.pages, s.budget_tokens,
+                    sel, mass, page_logmass=pm, ws=ws, agg=lk.AGG_MEAN_SHARE)
+    sel2 = torch.empty_like(sel)
+    mass2 = torch.empty_like(mass)
+    lk.locks_topk(pm, case.pages, s.page_size, s.budget_tokens, sel2, mass2)
+    torch.cuda.synchronize()
+    assert masses_close(to_np(pm), share_o) <= 1e-4
+    assert torch.equal(sel, sel2) and torch.equal(mass, mass2)
+    sel_g = sel.cpu().numpy()
+    for b in range(s.batch):
+        f = s.seq_lens[b] // s.page_size
+        for g in range(s.num_kv_heads):
+            assert band_ok(sel_g[b, g], sel_o[b, g], share_o[b, g, :f], min(k, f)), (b, g)
+
+
 def test_select_deterministic():
     case = Case(bf16_small())
     s = case.spec
