@@ -159,6 +159,20 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Step 1 for pages that became final since the last step (technical summary,
+ * section 2: a page's summary is made when the page is final, off the
+ * attention's critical path): the same summaries as locks_build_summaries,
+ * for the pages page_begin[b] <= j < min(page_begin[b] + max_new_pages,
+ * seq_lens[b] / P) only, with a launch sized by max_new_pages (not by
+ * max_pages).  page_begin: device [B], required.  In a decode loop the
+ * caller sets page_begin[b] to the previous step's count of full pages, so a
+ * step whose new token completes a page refreshes exactly that page.
+ */
+locks_status locks_refresh_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
+                                     const int32_t* page_begin, int32_t max_new_pages,
+                                     const locks_summaries* out, void* stream);
+
+/*
  * Step 2 - score every full page from its summary alone and select the top
  * pages per (sequence, KV group).  For each head h of group g:
  *   t = V_j^T q_h, beta = q_h . mu_j,
@@ -269,13 +283,16 @@ typedef struct {
     float* out_lse;       /* optional [B][H_q] */
     void* ws;             /* locks_workspace_bytes(LOCKS_OP_STEP, ...) */
     size_t ws_bytes;
+    const int32_t* refresh_begin; /* optional device [B]: refresh node first (see */
+    int32_t refresh_pages;        /* locks_refresh_summaries); NULL / 0: none     */
 } locks_step_args;
 
 typedef struct locks_step_graph locks_step_graph;
 
 /*
- * Capture one decode step (locks_select then locks_sparse_attend, with the
- * argument pointers given) into an instantiated HIP graph (technical
+ * Capture one decode step (locks_refresh_summaries when refresh_begin is
+ * set, then locks_select and locks_sparse_attend, with the argument
+ * pointers given) into an instantiated HIP graph (technical
  * summary, section 2, Implementatie: scoring, selection and sparse attention
  * run inside full graphs).  The pointers are baked in: replay reads the
  * current contents of the same buffers.  *graph receives a handle owned by

@@ -24,7 +24,7 @@ RUN_PAGES = 16  # pages per run maximum (LOCKS_RUN_PAGES)
 AGG_LSE, AGG_MEAN_SHARE = 0, 1  # locks_agg
 
 EXPORTED = ("locks_workspace_bytes", "locks_build_summaries", "locks_select", "locks_scan",
-            "locks_topk", "locks_mean_share", "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
+            "locks_topk", "locks_mean_share", "locks_refresh_summaries", "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
             "locks_step_graph_launch", "locks_step_graph_destroy", "locks_status_string",
             "locks_last_hip_error", "locks_version")
 
@@ -64,7 +64,8 @@ class CStepArgs(ctypes.Structure):
                 ("cache", CKVCache), ("pages", CPageTable), ("sel_pages", ctypes.c_void_p),
                 ("sel_logmass", ctypes.c_void_p), ("page_logmass", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("out_lse", ctypes.c_void_p), ("ws", ctypes.c_void_p),
-                ("ws_bytes", ctypes.c_size_t)]
+                ("ws_bytes", ctypes.c_size_t), ("refresh_begin", ctypes.c_void_p),
+                ("refresh_pages", ctypes.c_int32)]
 
 
 _lib = None
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.locks_select.argtypes = [vp, i32, P(CSummaries), P(CPageTable), i32, i32, vp, vp, vp,
                                    vp, sz, vp]
         L.locks_mean_share.argtypes = [vp, i32, i32, P(CPageTable), i32, vp, vp, vp, sz, vp]
+        L.locks_refresh_summaries.argtypes = [P(CKVCache), P(CPageTable), vp, i32, P(CSummaries),
+                                              vp]
         L.locks_scan.argtypes = [vp, i32, P(CSummaries), P(CPageTable), vp, vp, vp, vp]
         L.locks_topk.argtypes = [vp, P(CPageTable), i32, i32, i32, i32, vp, vp, vp, vp]
         L.locks_sparse_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, i32, vp, vp,
@@ -100,7 +103,7 @@ def lib() -> ctypes.CDLL:
         L.locks_last_hip_error.restype = i32
         L.locks_version.restype = i32
         for fn in ("locks_build_summaries", "locks_select", "locks_scan", "locks_topk",
-                   "locks_mean_share",
+                   "locks_mean_share", "locks_refresh_summaries",
                    "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
                    "locks_step_graph_launch"):
             getattr(L, fn).restype = i32
@@ -223,6 +226,14 @@ def locks_select(q, summaries: Summaries, pages: PageTable, budget_tokens, sel_p
                               _stream(stream)), "locks_select")
 
 
+def locks_refresh_summaries(cache: PagedKV, pages: PageTable, page_begin, max_new_pages,
+                            out: Summaries, stream=None):
+    cc, pc, sc = cache.c(), pages.c(), out.c()
+    _check(lib().locks_refresh_summaries(ctypes.byref(cc), ctypes.byref(pc), _ptr(page_begin),
+                                         max_new_pages, ctypes.byref(sc), _stream(stream)),
+           "locks_refresh_summaries")
+
+
 def locks_mean_share(head_logmass, num_kv_heads, pages: PageTable, page_size, page_logmass,
                      run_max=None, ws=None, stream=None):
     pc = pages.c()
@@ -256,14 +267,15 @@ class StepGraph:
 
     def __init__(self, q, summaries: Summaries, cache: PagedKV, pages: PageTable, budget_tokens,
                  sel_pages, sel_logmass, out, out_lse=None, page_logmass=None, ws=None,
-                 agg=AGG_LSE):
+                 agg=AGG_LSE, refresh_begin=None, refresh_pages=0):
         self._keep = (q, summaries, cache, pages, sel_pages, sel_logmass, out, out_lse,
-                      page_logmass, ws)
+                      page_logmass, ws, refresh_begin)
         a = CStepArgs(q.data_ptr(), q.shape[1], budget_tokens, agg, summaries.c(), cache.c(),
                       pages.c(), sel_pages.data_ptr(), sel_logmass.data_ptr(),
                       None if page_logmass is None else page_logmass.data_ptr(), out.data_ptr(),
                       None if out_lse is None else out_lse.data_ptr(),
-                      None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel())
+                      None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
+                      None if refresh_begin is None else refresh_begin.data_ptr(), refresh_pages)
         h = ctypes.c_void_p()
         _check(lib().locks_step_graph_create(ctypes.byref(a), ctypes.byref(h)),
                "locks_step_graph_create")

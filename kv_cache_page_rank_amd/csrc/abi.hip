@@ -218,11 +218,11 @@ size_t locks_workspace_bytes(int32_t op, int32_t batch, int32_t max_pages, int32
     }
 }
 
-locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
-                                   const int32_t* page_begin, const locks_summaries* out,
-                                   void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
+namespace {
+
+locks_status build_common(const locks_kv_cache* cache, const locks_page_table* pages,
+                          const int32_t* page_begin, int32_t refresh_pages,
+                          const locks_summaries* out, hipStream_t stream) {
     locks_status st = check_cache(cache, false);
     if (st != LOCKS_OK) return st;
     if ((st = check_page_table(pages)) != LOCKS_OK) return st;
@@ -238,6 +238,7 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
     p.block_table = pages->block_table;
     p.seq_lens = pages->seq_lens;
     p.page_begin = page_begin;
+    p.refresh_pages = refresh_pages;
     p.batch = pages->batch;
     p.num_kv_heads = cache->num_kv_heads;
     p.max_pages = pages->max_pages;
@@ -249,8 +250,26 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
     p.basis = out->basis;
     p.coef = out->coef;
     p.out_bf16 = out->dtype == LOCKS_BF16;
-    const hipError_t e = locks::launch_build(p, static_cast<hipStream_t>(stream));
+    const hipError_t e = locks::launch_build(p, stream);
     return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
+}  // namespace
+
+locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
+                                   const int32_t* page_begin, const locks_summaries* out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return build_common(cache, pages, page_begin, 0, out, static_cast<hipStream_t>(stream));
+}
+
+locks_status locks_refresh_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
+                                     const int32_t* page_begin, int32_t max_new_pages,
+                                     const locks_summaries* out, void* stream) {
+    if (!page_begin || max_new_pages <= 0) return LOCKS_ERR_INVALID_ARG;
+    return build_common(cache, pages, page_begin, max_new_pages, out,
+                        static_cast<hipStream_t>(stream));
 }
 
 locks_status locks_scan(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
@@ -384,9 +403,14 @@ locks_status locks_step_graph_create(const locks_step_args* a, locks_step_graph*
         (void)hipStreamDestroy(s);
         return hip_fail(e);
     }
-    locks_status st = locks_select(a->q, a->num_q_heads, &a->summaries, &a->pages, a->budget_tokens,
-                                   a->agg, a->sel_pages, a->sel_logmass, a->page_logmass, a->ws, a->ws_bytes,
-                                   s);
+    locks_status st = LOCKS_OK;
+    if (a->refresh_begin && a->refresh_pages > 0)
+        st = locks_refresh_summaries(&a->cache, &a->pages, a->refresh_begin, a->refresh_pages,
+                                     &a->summaries, s);
+    if (st == LOCKS_OK)
+        st = locks_select(a->q, a->num_q_heads, &a->summaries, &a->pages, a->budget_tokens,
+                          a->agg, a->sel_pages, a->sel_logmass, a->page_logmass, a->ws,
+                          a->ws_bytes, s);
     if (st == LOCKS_OK) {
         void* attn_ws = static_cast<char*>(a->ws) + sel_bytes;
         st = locks_sparse_attend(a->q, a->num_q_heads, &a->cache, &a->pages, a->sel_pages, k, a->out,
@@ -444,6 +468,6 @@ const char* locks_status_string(int32_t status) {
 
 int32_t locks_last_hip_error(void) { return g_last_hip_error; }
 
-int32_t locks_version(void) { return 103; }
+int32_t locks_version(void) { return 104; }
 
 }  // extern "C"

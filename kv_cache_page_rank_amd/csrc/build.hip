@@ -44,15 +44,19 @@ __global__ __launch_bounds__(256) void build_kernel(const BuildParams a) {
     __shared__ int slot[16];
     __shared__ float trace_s;
 
+    // unit -> (b, page j, KV head g): every page of the table, or (refresh)
+    // the refresh_pages pages from page_begin[b] on
     const int Hkv = a.num_kv_heads;
     const long u = blockIdx.x;
     const int g = (int)(u % Hkv);
-    const int j = (int)((u / Hkv) % a.max_pages);
-    const int b = (int)(u / ((long)Hkv * a.max_pages));
+    const int span = a.refresh_pages > 0 ? a.refresh_pages : a.max_pages;
+    const int i = (int)((u / Hkv) % span);
+    const int b = (int)(u / ((long)Hkv * span));
     int full = a.seq_lens[b] / P;
     full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
     const int begin = a.page_begin ? a.page_begin[b] : 0;
-    if (j < begin || j >= full) return;  // uniform over the workgroup
+    const int j = a.refresh_pages > 0 ? begin + i : i;
+    if (j < begin || j < 0 || j >= full) return;  // uniform over the workgroup
     const int phys = a.block_table[(size_t)b * a.max_pages + j];
     if (phys < 0 || phys >= a.num_blocks) return;
     const int t = threadIdx.x;
@@ -271,7 +275,8 @@ __global__ __launch_bounds__(256) void build_kernel(const BuildParams a) {
 
 template <int P, int D>
 hipError_t launch_pd(const BuildParams& p, hipStream_t s) {
-    const long units = (long)p.batch * p.max_pages * p.num_kv_heads;
+    const long units =
+        (long)p.batch * (p.refresh_pages > 0 ? p.refresh_pages : p.max_pages) * p.num_kv_heads;
     if (units == 0) return hipSuccess;
     if (p.bf16)
         hipLaunchKernelGGL((build_kernel<P, D, true>), dim3((unsigned)units), dim3(256), 0, s, p);

@@ -81,6 +81,7 @@ struct BuildParams {
     const int32_t* block_table;
     const int32_t* seq_lens;
     const int32_t* page_begin; // [B] or null
+    int32_t refresh_pages;     // > 0: only pages page_begin[b] .. + refresh_pages - 1
     int32_t batch, num_kv_heads, max_pages, num_blocks;
     int32_t page_size, head_dim, rank;
     void* mu;              // fp32 or bf16 (out_bf16)

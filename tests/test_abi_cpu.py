@@ -39,7 +39,7 @@ def test_header_symbols_exported(lk):
 
 def test_version_and_status_strings(lk):
     lib = lk.lib()
-    assert lib.locks_version() == 103
+    assert lib.locks_version() == 104
     assert lib.locks_status_string(0) == b"ok"
     assert b"workspace" in lib.locks_status_string(3)
     assert lib.locks_status_string(99) == b"unknown status"
@@ -106,6 +106,11 @@ def test_host_validation_rejects_without_launch(lk):
         lk.LOCKS_ERR_INVALID_ARG
     kv_bad, _, _, _ = _fake(lk, dtype=7)
     assert lib.locks_dense_attend(p, 32, by(kv_bad), by(pt), p, None, p, 1 << 30, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    # refresh without page_begin or pages
+    assert lib.locks_refresh_summaries(by(kv), by(pt), None, 1, by(sm), None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_refresh_summaries(by(kv), by(pt), p, 0, by(sm), None) == \
         lk.LOCKS_ERR_INVALID_ARG
     # unknown aggregation; mean-of-share without workspace
     assert lib.locks_select(p, 32, by(sm), by(pt), 2048, 7, p, p, p, p, 1 << 20, None) == \
