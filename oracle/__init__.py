@@ -73,8 +73,16 @@ def lib():
         L.orc_select_pool.argtypes = [lay, c_int, _f32p, c_int, _i32p, ctypes.c_void_p]
         L.orc_attend_pool.argtypes = [lay, _f32p, _f32p, _f32p, ctypes.c_void_p, c_int, _f64p,
                                       ctypes.c_void_p, c_int]
+        vp = ctypes.c_void_p
+        L.orc_quantize_vec.argtypes = [c_int, c_int, vp, c_int, vp, vp]
+        L.orc_quantize_vec.restype = None
+        L.orc_quantize_pool.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
+                                        vp, vp]
+        L.orc_dequantize_pool.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
+                                          vp, vp]
         for fn in ("orc_build_pool", "orc_build_units", "orc_scan_pool", "orc_scan_units",
-                   "orc_exact_pool", "orc_select_pool", "orc_attend_pool"):
+                   "orc_exact_pool", "orc_select_pool", "orc_attend_pool", "orc_quantize_pool",
+                   "orc_dequantize_pool"):
             getattr(L, fn).restype = c_int
         _lib = L
     return _lib
@@ -293,3 +301,48 @@ def attend_pool(L: Layout, q, k_pool, v_pool, sel_pages=None, threads: int = 0):
                                  _f32(v_pool).reshape(-1), _ptr(sel), width, out.reshape(-1),
                                  lse_.ctypes.data, threads), "attend_pool")
     return out, lse_
+
+
+# ------------------------------------------------------------------ quantised summaries
+def quantize_vec(x, qmax: int):
+    """Symmetric absmax quantisation of one float32 vector (technical summary,
+    section 2, "Kwantisatie"; reading in locks_oracle.h): (scale, int8 codes)."""
+    xs = _f32(x).reshape(-1)
+    code = np.zeros(xs.shape, np.int8)
+    scale = np.zeros(1, np.float32)
+    lib().orc_quantize_vec(xs.size, 1, xs.ctypes.data, qmax, scale.ctypes.data, code.ctypes.data)
+    return float(scale[0]), code
+
+
+def quantize_pool(mu, basis, coef):
+    """fp32 summary arrays mu [NB][Hkv][d], basis [NB][Hkv][r][d], coef
+    [NB][Hkv][P][r] -> (mu_q int8, basis_q packed uint8 [NB][Hkv][r][d/2],
+    coef_q int8, scales float32 [NB][Hkv][1+2r])."""
+    mu, basis, coef = _f32(mu), _f32(basis), _f32(coef)
+    NB, H, r, d = basis.shape
+    P = coef.shape[2]
+    mu_q = np.zeros((NB, H, d), np.int8)
+    basis_q = np.zeros((NB, H, r, d // 2), np.uint8)
+    coef_q = np.zeros((NB, H, P, r), np.int8)
+    scales = np.zeros((NB, H, 1 + 2 * r), np.float32)
+    _check(lib().orc_quantize_pool(NB, H, P, d, r, mu.ctypes.data, basis.ctypes.data,
+                                   coef.ctypes.data, mu_q.ctypes.data, basis_q.ctypes.data,
+                                   coef_q.ctypes.data, scales.ctypes.data), "quantize_pool")
+    return mu_q, basis_q, coef_q, scales
+
+
+def dequantize_pool(mu_q, basis_q, coef_q, scales):
+    """Inverse of quantize_pool up to the codes: float32 (mu, basis, coef)."""
+    mu_q = np.ascontiguousarray(mu_q, np.int8)
+    basis_q = np.ascontiguousarray(basis_q, np.uint8)
+    coef_q = np.ascontiguousarray(coef_q, np.int8)
+    scales = _f32(scales)
+    NB, H, r, dh = basis_q.shape
+    d, P = 2 * dh, coef_q.shape[2]
+    mu = np.zeros((NB, H, d), np.float32)
+    basis = np.zeros((NB, H, r, d), np.float32)
+    coef = np.zeros((NB, H, P, r), np.float32)
+    _check(lib().orc_dequantize_pool(NB, H, P, d, r, mu_q.ctypes.data, basis_q.ctypes.data,
+                                     coef_q.ctypes.data, scales.ctypes.data, mu.ctypes.data,
+                                     basis.ctypes.data, coef.ctypes.data), "dequantize_pool")
+    return mu, basis, coef

@@ -530,3 +530,74 @@ int orc_attend_pool(const orc_layout* L, const float* q, const float* k_pool,
     }
     return 0;
 }
+
+/* ---------------- quantised summaries (section 2, "Kwantisatie") ---------------- */
+
+void orc_quantize_vec(int n, int stride, const float* x, int qmax, float* scale, int8_t* code) {
+    float m = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        const float a = fabsf(x[(size_t)i * stride]);
+        if (a > m) m = a;
+    }
+    const float s = m / (float)qmax;
+    *scale = s;
+    for (int i = 0; i < n; ++i) {
+        int c = 0;
+        if (s > 0.0f) {
+            const float y = rintf(x[(size_t)i * stride] / s);  /* ties to even */
+            c = (int)y;
+            if (c > qmax) c = qmax;
+            if (c < -qmax) c = -qmax;
+        }
+        code[(size_t)i * stride] = (int8_t)c;
+    }
+}
+
+int orc_quantize_pool(int num_blocks, int num_kv_heads, int P, int d, int r, const float* mu,
+                      const float* basis, const float* coef, int8_t* mu_q, uint8_t* basis_q,
+                      int8_t* coef_q, float* scales) {
+    if (num_blocks < 0 || num_kv_heads <= 0 || P <= 0 || d <= 0 || d % 2 || r <= 0) return -1;
+    int8_t* row = (int8_t*)malloc((size_t)d);
+    if (!row) return -1;
+    const size_t units = (size_t)num_blocks * num_kv_heads;
+    for (size_t u = 0; u < units; ++u) {
+        float* sc = scales + u * (size_t)(1 + 2 * r);
+        orc_quantize_vec(d, 1, mu + u * d, 127, &sc[0], mu_q + u * d);
+        for (int k = 0; k < r; ++k) {
+            orc_quantize_vec(d, 1, basis + (u * r + k) * d, 7, &sc[1 + k], row);
+            uint8_t* out = basis_q + (u * r + k) * (size_t)(d / 2);
+            for (int t = 0; t < d / 2; ++t)
+                out[t] = (uint8_t)(((uint8_t)row[2 * t] & 0x0F) | (((uint8_t)row[2 * t + 1] & 0x0F) << 4));
+        }
+        for (int k = 0; k < r; ++k)
+            orc_quantize_vec(P, r, coef + u * (size_t)P * r + k, 127, &sc[1 + r + k],
+                             coef_q + u * (size_t)P * r + k);
+    }
+    free(row);
+    return 0;
+}
+
+static int nibble(uint8_t byte, int hi) {
+    const int v = hi ? (byte >> 4) : (byte & 0x0F);
+    return v >= 8 ? v - 16 : v;
+}
+
+int orc_dequantize_pool(int num_blocks, int num_kv_heads, int P, int d, int r,
+                        const int8_t* mu_q, const uint8_t* basis_q, const int8_t* coef_q,
+                        const float* scales, float* mu, float* basis, float* coef) {
+    if (num_blocks < 0 || num_kv_heads <= 0 || P <= 0 || d <= 0 || d % 2 || r <= 0) return -1;
+    const size_t units = (size_t)num_blocks * num_kv_heads;
+    for (size_t u = 0; u < units; ++u) {
+        const float* sc = scales + u * (size_t)(1 + 2 * r);
+        for (int i = 0; i < d; ++i) mu[u * d + i] = (float)((double)sc[0] * mu_q[u * d + i]);
+        for (int k = 0; k < r; ++k)
+            for (int i = 0; i < d; ++i)
+                basis[(u * r + k) * d + i] = (float)((double)sc[1 + k] *
+                    nibble(basis_q[(u * r + k) * (size_t)(d / 2) + i / 2], i & 1));
+        for (int t = 0; t < P; ++t)
+            for (int k = 0; k < r; ++k)
+                coef[(u * P + t) * r + k] =
+                    (float)((double)sc[1 + r + k] * coef_q[(u * P + t) * r + k]);
+    }
+    return 0;
+}

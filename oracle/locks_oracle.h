@@ -17,7 +17,9 @@
  *       English abstract (insight.aitobox.com page, "Abstract");
  *   exact-LSE selection that reads every key: abstract, and section 3
  *       "Retrieval en QA";
- *   attention over the top pages only: abstract.
+ *   attention over the top pages only: abstract;
+ *   stored summary precision (int4 basis, int8 coefficients and centroid):
+ *       section 2, "Kwantisatie".
  * Readings where the pages are silent (all stated again at each function):
  *   GQA aggregation is the LSE over the group's heads; head h belongs to
  *   KV group h / G; k = min(floor(budget / P), full pages); ties go to the
@@ -145,6 +147,36 @@ int orc_select_pool(const orc_layout* L, int budget_tokens, const float* page_ma
 int orc_attend_pool(const orc_layout* L, const float* q, const float* k_pool,
                     const float* v_pool, const int32_t* sel_pages, int width, double* out,
                     double* lse, int nthreads);
+
+/* ---------------- quantised summaries ----------------
+ * Stored precision (technical summary, section 2, "Kwantisatie": the basis
+ * in int4, coefficients and centroid in int8).  The pages fix the widths
+ * only; the reading used here: symmetric absmax scaling of one vector at a
+ * time, in float arithmetic,
+ *   scale = max_i |x_i| / Q          (IEEE float division),
+ *   code_i = round-half-even(x_i / scale), clamped to [-Q, Q],
+ * Q = 127 (int8) or 7 (int4), scale 0 and codes 0 for a zero vector; one
+ * vector per centroid, per basis row and per coefficient column (a column
+ * holds one basis direction's coordinates over the page's tokens).
+ * Dequantised value: scale * code.
+ *
+ * Layout per unit (block, KV head): mu_q [d] int8; basis_q [r][d/2] bytes,
+ * element 2t in the low nibble of byte t and 2t+1 in the high nibble, each a
+ * 4-bit two's complement code; coef_q [P][r] int8; scales [1 + 2r] float:
+ * the centroid's, then the r basis rows', then the r coefficient columns'. */
+
+/* Quantise n values x[i * stride] (Q = qmax). */
+void orc_quantize_vec(int n, int stride, const float* x, int qmax, float* scale, int8_t* code);
+
+/* Quantise every unit of fp32 summary arrays of num_blocks blocks. */
+int orc_quantize_pool(int num_blocks, int num_kv_heads, int P, int d, int r, const float* mu,
+                      const float* basis, const float* coef, int8_t* mu_q, uint8_t* basis_q,
+                      int8_t* coef_q, float* scales);
+
+/* Dequantise into fp32 arrays (scale * code, rounded to float). */
+int orc_dequantize_pool(int num_blocks, int num_kv_heads, int P, int d, int r,
+                        const int8_t* mu_q, const uint8_t* basis_q, const int8_t* coef_q,
+                        const float* scales, float* mu, float* basis, float* coef);
 
 #ifdef __cplusplus
 }

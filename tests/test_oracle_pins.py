@@ -442,3 +442,118 @@ def test_pins_catch_planted_mistakes(orc):
     assert abs(orc.page_estimate(q / math.sqrt(d), mu, basis, coef) - exact) > 1e-3
     # basis used transposed within the page's subspace: coefficient columns permuted
     assert abs(orc.page_estimate(q, mu, basis, coef[:, ::-1]) - exact) > 1e-3
+
+
+# ---------------------------------------------------------------- quantised summaries
+# Stored precision: technical summary, section 2, "Kwantisatie" (int4 basis,
+# int8 coefficients and centroid); scale granularity and rounding are the
+# reading stated in oracle/locks_oracle.h.
+
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_quantize_grid_values_are_lossless(orc, qmax):
+    """Values on a power-of-two grid with a full-range code come back exactly."""
+    g = np.random.default_rng(qmax)
+    k = g.integers(-qmax, qmax + 1, 200)
+    k[17] = -qmax
+    s0 = np.float32(2.0 ** -5)
+    x = (k * s0).astype(np.float32)
+    s, code = orc.quantize_vec(x, qmax)
+    assert s == s0
+    assert np.array_equal(code.astype(np.int64), k)
+
+
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_quantize_error_bound_and_range(orc, qmax):
+    x = np.random.default_rng(7 + qmax).standard_normal(513).astype(np.float32) * 3.0
+    s, code = orc.quantize_vec(x, qmax)
+    c = code.astype(np.float64)
+    assert np.abs(c).max() <= qmax
+    i = int(np.argmax(np.abs(x)))
+    assert c[i] == np.sign(x[i]) * qmax              # the absmax element takes the end code
+    err = np.abs(x.astype(np.float64) - s * c)
+    assert err.max() <= 0.5 * s * (1 + 1e-6)         # round to nearest
+
+
+def test_quantize_matches_numpy_float32_rounding(orc):
+    """The same arithmetic through numpy's float32 division and rint."""
+    for qmax in (127, 7):
+        x = np.random.default_rng(qmax).standard_normal(1000).astype(np.float32)
+        s, code = orc.quantize_vec(x, qmax)
+        s_np = np.float32(np.abs(x).max()) / np.float32(qmax)
+        ref = np.clip(np.rint(x / s_np), -qmax, qmax).astype(np.int8)
+        assert s == s_np and np.array_equal(code, ref)
+
+
+def test_quantize_ties_and_zero(orc):
+    s, code = orc.quantize_vec(np.array([127, 2.5, 3.5, -2.5, -0.5, 0.5], np.float32), 127)
+    assert s == 1.0 and code.tolist() == [127, 2, 4, -2, 0, 0]    # half to even
+    s, code = orc.quantize_vec(np.zeros(9, np.float32), 7)
+    assert s == 0.0 and not code.any()
+
+
+def test_quantize_pool_hand_example(orc):
+    """One unit (P 2, d 4, r 1) worked by hand.
+    centroid [1, -1/4, 1/8, 0]: scale 1/127, codes 127, -31.75 -> -32, 15.875 -> 16, 0;
+    basis row [7, -3, 1, -6] / 16: scale (7/16)/7 = 1/16, codes 7 -3 1 -6, packed low
+      nibble first: 0x7 | 0xD << 4 = 0xD7, 0x1 | 0xA << 4 = 0xA1;
+    coefficient column [1/4, -1]: scale 1/127, codes 31.75 -> 32, -127."""
+    mu = np.array([[[1.0, -0.25, 0.125, 0.0]]], np.float32)
+    basis = (np.array([[[[7.0, -3.0, 1.0, -6.0]]]]) / 16).astype(np.float32)
+    coef = np.array([[[[0.25], [-1.0]]]], np.float32)
+    mu_q, basis_q, coef_q, scales = orc.quantize_pool(mu, basis, coef)
+    assert mu_q.reshape(-1).tolist() == [127, -32, 16, 0]
+    assert basis_q.reshape(-1).tolist() == [0xD7, 0xA1]
+    assert coef_q.reshape(-1).tolist() == [32, -127]
+    third = np.float32(1.0) / np.float32(127.0)
+    assert scales.reshape(-1).tolist() == [third, 1.0 / 16, third]
+    m2, b2, c2 = orc.dequantize_pool(mu_q, basis_q, coef_q, scales)
+    assert b2.reshape(-1).tolist() == basis.reshape(-1).tolist()      # on the grid: exact
+    assert np.allclose(m2, mu, atol=0.5 * third) and np.allclose(c2, coef, atol=0.5 * third)
+
+
+def test_quantize_pool_granularity(orc):
+    """One scale per basis row and per coefficient column: scaling one row (one
+    column) by 2 doubles its scale alone and leaves every code unchanged."""
+    g = np.random.default_rng(5)
+    NB, H, P, d, r = 3, 2, 16, 64, 4
+    mu = g.standard_normal((NB, H, d)).astype(np.float32)
+    basis = g.standard_normal((NB, H, r, d)).astype(np.float32)
+    coef = g.standard_normal((NB, H, P, r)).astype(np.float32)
+    ref = orc.quantize_pool(mu, basis, coef)
+    b2, c2 = basis.copy(), coef.copy()
+    b2[1, 0, 2] *= 2
+    c2[2, 1, :, 3] *= 2
+    out = orc.quantize_pool(mu, b2, c2)
+    for a, b in zip(ref[:3], out[:3]):
+        assert np.array_equal(a, b)
+    ds = out[3] / ref[3]
+    expect = np.ones_like(ds)
+    expect[1, 0, 1 + 2] = 2
+    expect[2, 1, 1 + r + 3] = 2
+    assert np.array_equal(ds, expect)
+
+
+def test_dequantised_estimate_on_grid_equals_unquantised(wl, orc):
+    """Summaries already on the quantiser's grid survive quantisation exactly,
+    so the page masses of the dequantised summaries equal the originals."""
+    spec = wl.config(0)
+    layer = wl.make(spec)
+    L = orc.Layout(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                   layer.block_table, layer.seq_lens)
+    mu, basis, coef = orc.build_pool(L, spec.rank, layer.k_f32(), spec.num_blocks)
+    # snap each vector to a power-of-two grid with a full-range code
+    def snap(x, axis, qmax):
+        m = np.abs(x).max(axis=axis, keepdims=True)
+        s = 2.0 ** np.ceil(np.log2(np.where(m > 0, m, 1) / qmax))
+        y = np.clip(np.round(x / s), -qmax, qmax)
+        y = np.where(np.abs(y).max(axis=axis, keepdims=True) == qmax, y,
+                     np.where(np.abs(x) == m, np.sign(x) * qmax, y))
+        return (y * s).astype(np.float32)
+    mu_g, basis_g, coef_g = snap(mu, -1, 127), snap(basis, -1, 7), snap(coef, -2, 127)
+    deq = orc.dequantize_pool(*orc.quantize_pool(mu_g, basis_g, coef_g))
+    for a, b in zip(deq, (mu_g, basis_g, coef_g)):
+        assert np.array_equal(a, b)
+    q = layer.q
+    _, pm_a = orc.scan_pool(L, spec.rank, q, mu_g, basis_g, coef_g)
+    _, pm_b = orc.scan_pool(L, spec.rank, q, *deq)
+    assert np.array_equal(pm_a, pm_b)
