@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-bf16-summaries", action="store_true",
-                    help="skip the extra measurement of the step with bf16 summaries")
+                    help="skip the extra measurements of the step with bf16 and with "
+                         "int8/int4 summaries")
     ap.add_argument("--cpu-target-s", type=float, default=12.0,
                     help="approximate CPU seconds spent on the oracle sample")
     ap.add_argument("--threads", type=int, default=0)
@@ -242,36 +243,46 @@ def main():
     step_b = traffic.step_bytes(full_total, partial, Hkv, d, P, r, B * Hkv * k)
     log(f"select (scan+topk): {sel_mean:.2f} us, sparse attend+merge: {sparse_mean:.2f} us")
 
-    # --- the same step with bf16 summaries (reported beside the fp32 headline)
-    bf16_summ = None
-    if not args.no_bf16_summaries:
-        summs16 = [lk.Summaries.empty(NB, Hkv, P, d, r, dtype=torch.bfloat16) for _ in range(L)]
-        for i in range(L):
-            lk.locks_build_summaries(kvs[i], pages, summs16[i])
-        g16 = [lk.StepGraph(q, summs16[i], kvs[i], pages, spec.budget_tokens, *bufs[i][:4],
-                            ws=bufs[i][4]) for i in range(L)]
-        for i in range(args.warmup):
-            g16[i % L].launch()
+    # --- the same step with reduced-precision summaries (reported beside the
+    # fp32 headline): bf16 values, and the pages' own int8 / int4 codes.  The
+    # summaries get enough rotated copies that every copy's reuse distance
+    # exceeds 2 x 256 MB (the K/V copies rotate as before).
+    def reduced_precision(dtype, elem, label):
+        scan_b = traffic.scan_bytes(B, Hq, Hkv, MP, full_total, d, P, r, summary_elem=elem)
+        n = max(L, -(-2 * 256 * 2 ** 20 // scan_b) + 1)
+        copies = [lk.Summaries.empty(NB, Hkv, P, d, r, dtype=dtype) for _ in range(n)]
+        for i in range(n):
+            lk.locks_build_summaries(kvs[i % L], pages, copies[i])
+        graphs = [lk.StepGraph(q, copies[i], kvs[i % L], pages, spec.budget_tokens,
+                               *bufs[i % L][:4], ws=bufs[i % L][4]) for i in range(n)]
+        for i in range(max(args.warmup, n)):
+            graphs[i % n].launch()
         torch.cuda.synchronize()
         e0.record()
         for i in range(args.steps):
-            g16[i % L].launch()
+            graphs[i % n].launch()
         e1.record()
         torch.cuda.synchronize()
-        step16 = e0.elapsed_time(e1) * 1e3 / args.steps
-        for i in range(args.warmup):
-            lk.locks_scan(q, summs16[i % L], pages, pms[i % L])
-        scan16, _, _ = time_events(
-            lambda i: lk.locks_scan(q, summs16[i % L], pages, pms[i % L]), args.steps, torch)
-        scan16_b = traffic.scan_bytes(B, Hq, Hkv, MP, full_total, d, P, r, summary_elem=2)
-        gbs16 = scan16_b / (scan16 * 1e-6) / 1e9
-        bf16_summ = {"step_us": round(step16, 3), "scan_us": round(scan16, 3),
-                     "scan_bytes_per_launch": scan16_b, "scan_GBps": round(gbs16, 1),
-                     "scan_frac": round(gbs16 / HBM_PEAK_GBS, 4),
-                     "summary_to_cache_ratio": round(traffic.summary_to_cache_ratio(d, P, r, 2), 4)}
-        for g in g16:
-            g.close()
-        log(f"bf16 summaries: step {step16:.2f} us, scan {scan16:.2f} us, {gbs16:.0f} GB/s")
+        step_us = e0.elapsed_time(e1) * 1e3 / args.steps
+        for i in range(max(args.warmup, n)):
+            lk.locks_scan(q, copies[i % n], pages, pms[i % L])
+        scan_us, _, _ = time_events(
+            lambda i: lk.locks_scan(q, copies[i % n], pages, pms[i % L]), args.steps, torch)
+        gbs = scan_b / (scan_us * 1e-6) / 1e9
+        for g_ in graphs:
+            g_.close()
+        log(f"{label}: step {step_us:.2f} us, scan {scan_us:.2f} us, {gbs:.0f} GB/s "
+            f"({n} summary copies)")
+        return {"step_us": round(step_us, 3), "scan_us": round(scan_us, 3),
+                "scan_bytes_per_launch": scan_b, "scan_GBps": round(gbs, 1),
+                "scan_frac": round(gbs / HBM_PEAK_GBS, 4), "summary_copies": n,
+                "speedup_vs_dense": None,
+                "summary_to_cache_ratio": round(traffic.summary_to_cache_ratio(d, P, r, elem), 4)}
+
+    bf16_summ = q8q4_summ = None
+    if not args.no_bf16_summaries:
+        bf16_summ = reduced_precision(torch.bfloat16, 2, "bf16 summaries")
+        q8q4_summ = reduced_precision(lk.Q8Q4, "q8q4", "int8/int4 summaries")
 
     # --- the same step with the mean-of-share group aggregation (fp32 summaries)
     gm = [lk.StepGraph(q, summs[i], kvs[i], pages, spec.budget_tokens, *bufs[i][:4], ws=bufs[i][4],
@@ -302,12 +313,14 @@ def main():
             lambda i: lk.locks_dense_attend(q, kvs[i % L], pages, dout, dlse, ws=dws),
             max(5, args.steps // 5), torch)
         log(f"dense: {dense_mean:.2f} us, {dense_b / (dense_mean * 1e-6) / 1e9:.0f} GB/s")
+        for rp in (bf16_summ, q8q4_summ):
+            if rp is not None:
+                rp["speedup_vs_dense"] = round(dense_mean / rp["step_us"], 3)
 
     # --- CPU baseline: the oracle on a bounded sample of the same step
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, layer, summs[0], sel_np=bufs[0][0].cpu().numpy(),
-                           target_s=args.cpu_target_s, threads=threads)
+        cpu = cpu_baseline(spec, layer, target_s=args.cpu_target_s, threads=threads)
 
     ratio = traffic.summary_to_cache_ratio(d, P, r)
     result = {
@@ -350,6 +363,7 @@ def main():
             "build_ms": round(build_ms, 3),
             "build_pages_per_s": round(full_total * Hkv / (build_ms * 1e-3), 1),
             "bf16_summaries": bf16_summ,
+            "q8q4_summaries": q8q4_summ,
             "mean_share_step_us": round(share_step, 3),
         },
     }
@@ -358,48 +372,48 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(spec, layer, summ0, sel_np, target_s, threads):
+def cpu_baseline(spec, layer, target_s, threads):
     """Time the oracle's decode step on the host cores: scan + aggregation
-    over every full page (from the same summaries), selection from those
-    masses, and attention over the GPU-selected page list.  The whole step
-    is repeated until about target_s seconds of CPU time have been spent
-    (or, when one step alone is longer, a prefix of the pages is scanned and
-    scaled).  Returns the record for the JSON line."""
+    over every full page, selection from those masses, and attention over
+    the pages it selected.  Nothing here comes from the GPU: the summaries are
+    seeded stand-ins of the layer's shapes (the oracle's cost does not depend
+    on their values).  The whole step is repeated until about target_s
+    seconds of CPU time have been spent (or, when one step alone is longer, a
+    prefix of the pages is scanned and scaled).  Returns the JSON record."""
     import numpy as np
 
     import oracle
 
-    P, Hkv = spec.page_size, spec.num_kv_heads
-    mu = summ0.mu.cpu().numpy()
-    basis = summ0.basis.cpu().numpy()
-    coef = summ0.coef.cpu().numpy()
+    P, Hkv, d, r = spec.page_size, spec.num_kv_heads, spec.head_dim, spec.rank
+    g = np.random.default_rng(spec.seed + 17)
+    NB = spec.num_blocks
+    mu = g.standard_normal((NB, Hkv, d), dtype=np.float32)
+    basis = g.standard_normal((NB, Hkv, r, d), dtype=np.float32) / np.float32(np.sqrt(d))
+    coef = g.standard_normal((NB, Hkv, P, r), dtype=np.float32)
     full_total = sum(n // P for n in spec.seq_lens)
     kf, vf = layer.k_f32(), layer.v_f32()  # widened once, outside the timed calls
 
     def step(npages):
-        """One oracle step over the first npages full pages of each sequence."""
+        """Scan + selection over the first npages full pages of each sequence."""
         seq = np.array([min(n, npages * P) for n in spec.seq_lens], np.int32)
-        lay = oracle.Layout(spec.num_q_heads, Hkv, spec.head_dim, P, layer.block_table, seq)
+        lay = oracle.Layout(spec.num_q_heads, Hkv, d, P, layer.block_table, seq)
         t0 = time.perf_counter()
-        _, pm = oracle.scan_pool(lay, spec.rank, layer.q, mu, basis, coef, threads=threads,
-                                 heads=False)
+        _, pm = oracle.scan_pool(lay, r, layer.q, mu, basis, coef, threads=threads, heads=False)
         t1 = time.perf_counter()
-        oracle.select_pool(lay, spec.budget_tokens, pm.astype(np.float32), spec.k_pages)
+        sel, _ = oracle.select_pool(lay, spec.budget_tokens, pm.astype(np.float32), spec.k_pages)
         t2 = time.perf_counter()
-        return t1 - t0, t2 - t1, int(sum(s // P for s in seq))
+        return t1 - t0, t2 - t1, int(sum(s // P for s in seq)), sel
 
-    lay_full = oracle.Layout(spec.num_q_heads, Hkv, spec.head_dim, P, layer.block_table,
-                             layer.seq_lens)
-    t0 = time.perf_counter()
-    oracle.attend_pool(lay_full, layer.q, kf, vf, sel_np, threads=threads)
-    att_s = time.perf_counter() - t0
-
+    lay_full = oracle.Layout(spec.num_q_heads, Hkv, d, P, layer.block_table, layer.seq_lens)
     npages = max(full_total, 1)
-    scan_s, sel_s, done = step(npages)
+    scan_s, sel_s, done, sel = step(npages)
+    t0 = time.perf_counter()
+    oracle.attend_pool(lay_full, layer.q, kf, vf, sel, threads=threads)
+    att_s = time.perf_counter() - t0
     reps = 1
     if scan_s + sel_s + att_s > target_s:  # one step is already long: scan a prefix
         npages = max(1, int(npages * target_s / (scan_s + sel_s + att_s)))
-        scan_s, sel_s, done = step(npages)
+        scan_s, sel_s, done, _ = step(npages)
         scan_s *= full_total / max(done, 1)
         sample = f"scan+aggregation+selection over the first {done} of {full_total} full pages " \
                  f"(x{Hkv} KV heads), scaled to all pages; attention over the selected pages"
@@ -407,9 +421,9 @@ def cpu_baseline(spec, layer, summ0, sel_np, target_s, threads):
         reps = max(1, int(target_s / (scan_s + sel_s + att_s)))
         tot_scan = tot_sel = tot_att = 0.0
         for _ in range(reps):
-            a, s_, _ = step(npages)
+            a, s_, _, sel = step(npages)
             t0 = time.perf_counter()
-            oracle.attend_pool(lay_full, layer.q, kf, vf, sel_np, threads=threads)
+            oracle.attend_pool(lay_full, layer.q, kf, vf, sel, threads=threads)
             tot_att += time.perf_counter() - t0
             tot_scan += a
             tot_sel += s_

@@ -80,7 +80,8 @@ typedef enum {
     LOCKS_ERR_HIP = 4          /* a HIP call failed; see locks_last_hip_error() */
 } locks_status;
 
-typedef enum { LOCKS_F32 = 0, LOCKS_BF16 = 1 } locks_dtype;
+/* Element types.  LOCKS_Q8Q4 is for summaries only (see locks_summaries). */
+typedef enum { LOCKS_F32 = 0, LOCKS_BF16 = 1, LOCKS_Q8Q4 = 2 } locks_dtype;
 
 /* How the heads of a GQA group are combined into one page score
  * (technical summary, section 2, Group-Shared Selection).  LSE: the log of
@@ -108,11 +109,22 @@ typedef struct {
     const void* v; /* [NB][H_kv][d][P] */
 } locks_kv_cache;
 
-/* Resident summaries of one layer, stored by physical block.  dtype
- * LOCKS_F32, or LOCKS_BF16: each value is the fp32 summary rounded to the
- * nearest bf16 (ties to even), half the bytes for the scan to read
- * (technical summary, section 2, Kwantisatie: the pages store the summary
- * at reduced precision; bf16 is the first step, integer codes are not built). */
+/* Resident summaries of one layer, stored by physical block (technical
+ * summary, section 2, Kwantisatie: the pages keep the summary at reduced
+ * precision, the basis in int4 and coefficients and centroid in int8).
+ *   LOCKS_F32   fp32 values; scales unused (may be NULL).
+ *   LOCKS_BF16  each value is the fp32 summary rounded to the nearest bf16
+ *               (ties to even); scales unused.
+ *   LOCKS_Q8Q4  integer codes with fp32 scales, per unit (block, KV head):
+ *               mu int8 [d]; basis int4 [r][d/2] bytes, element 2t in the
+ *               low nibble of byte t and 2t+1 in the high nibble (4-bit two's
+ *               complement); coef int8 [P][r]; scales fp32 [1 + 2r] = the
+ *               centroid's, the r basis rows', the r coefficient columns'.
+ *               A vector's scale is max|x| / Q (IEEE float division, Q = 127
+ *               for int8, 7 for int4), its codes round-half-even(x / scale)
+ *               clamped to [-Q, Q] (scale 0 and codes 0 for a zero vector);
+ *               the value a code stands for is scale * code.  1220 bytes per
+ *               unit at P 64, d 128, r 8 (fp32: 6656). */
 typedef struct {
     int32_t dtype; /* locks_dtype of mu, basis and coef */
     int32_t num_blocks;
@@ -120,9 +132,10 @@ typedef struct {
     int32_t page_size;
     int32_t head_dim;
     int32_t rank;
-    void* mu;    /* [NB][H_kv][d] */
-    void* basis; /* [NB][H_kv][r][d] */
-    void* coef;  /* [NB][H_kv][P][r] */
+    void* mu;     /* [NB][H_kv][d] (int8 codes for LOCKS_Q8Q4) */
+    void* basis;  /* [NB][H_kv][r][d] (LOCKS_Q8Q4: [NB][H_kv][r][d/2] bytes) */
+    void* coef;   /* [NB][H_kv][P][r] */
+    float* scales; /* LOCKS_Q8Q4: [NB][H_kv][1 + 2r]; otherwise unused */
 } locks_summaries;
 
 /* Block table of a batch of sequences. */
@@ -151,8 +164,9 @@ size_t locks_workspace_bytes(int32_t op, int32_t batch, int32_t max_pages, int32
  * Eigenvalues below 3e-5 * lambda_max give zero basis/coef (numerically null).
  * page_begin: device [B] or NULL (= all full pages).  Summaries of other
  * blocks are left untouched.  summaries->rank is r.  Computed in fp32 and
- * stored in out->dtype (bf16: rounded to nearest even).  Needs no workspace
- * (ws may be NULL).
+ * stored in out->dtype (bf16: rounded to nearest even; Q8Q4: the fp32
+ * summary's codes and scales, exactly as locks_quantize_summaries makes
+ * them).  Needs no workspace (ws may be NULL).
  */
 locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
                                    const int32_t* page_begin, const locks_summaries* out,
@@ -171,6 +185,17 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
 locks_status locks_refresh_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
                                      const int32_t* page_begin, int32_t max_new_pages,
                                      const locks_summaries* out, void* stream);
+
+/*
+ * Quantise fp32 summaries into LOCKS_Q8Q4 codes and scales (technical
+ * summary, section 2, Kwantisatie; the quantiser is the one described at
+ * locks_summaries), for every unit (block, KV head) of the pools.
+ * src: dtype LOCKS_F32; dst: dtype LOCKS_Q8Q4 with the same num_blocks,
+ * num_kv_heads, page_size, head_dim and rank.  Device pointers; the caller
+ * owns both.  LOCKS_ERR_INVALID_ARG on mismatched shapes or dtypes.
+ */
+locks_status locks_quantize_summaries(const locks_summaries* src, const locks_summaries* dst,
+                                      void* stream);
 
 /*
  * Step 2 - score every full page from its summary alone and select the top

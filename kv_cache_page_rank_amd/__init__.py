@@ -18,13 +18,18 @@ LIB_PATH = os.path.join(_HERE, "liblocks.so")
 
 LOCKS_OK, LOCKS_ERR_INVALID_ARG, LOCKS_ERR_UNSUPPORTED, LOCKS_ERR_WORKSPACE, LOCKS_ERR_HIP = \
     range(5)
-LOCKS_F32, LOCKS_BF16 = 0, 1
+LOCKS_F32, LOCKS_BF16, LOCKS_Q8Q4 = 0, 1, 2
+# Summary storage with integer codes (LOCKS_Q8Q4): int8 centroid and
+# coefficients, int4 basis, fp32 scales.  Pass as Summaries.empty(dtype=...).
+Q8Q4 = "q8q4"
 OP_BUILD, OP_SELECT, OP_SPARSE_ATTEND, OP_DENSE_ATTEND, OP_STEP = range(5)
 RUN_PAGES = 16  # pages per run maximum (LOCKS_RUN_PAGES)
 AGG_LSE, AGG_MEAN_SHARE = 0, 1  # locks_agg
 
 EXPORTED = ("locks_workspace_bytes", "locks_build_summaries", "locks_select", "locks_scan",
-            "locks_topk", "locks_mean_share", "locks_refresh_summaries", "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
+            "locks_topk", "locks_mean_share", "locks_refresh_summaries",
+            "locks_quantize_summaries", "locks_sparse_attend", "locks_dense_attend",
+            "locks_step_graph_create",
             "locks_step_graph_launch", "locks_step_graph_destroy", "locks_status_string",
             "locks_last_hip_error", "locks_version")
 
@@ -49,7 +54,7 @@ class CSummaries(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("mu", ctypes.c_void_p), ("basis", ctypes.c_void_p),
-                ("coef", ctypes.c_void_p)]
+                ("coef", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 class CPageTable(ctypes.Structure):
@@ -89,6 +94,7 @@ def lib() -> ctypes.CDLL:
         L.locks_mean_share.argtypes = [vp, i32, i32, P(CPageTable), i32, vp, vp, vp, sz, vp]
         L.locks_refresh_summaries.argtypes = [P(CKVCache), P(CPageTable), vp, i32, P(CSummaries),
                                               vp]
+        L.locks_quantize_summaries.argtypes = [P(CSummaries), P(CSummaries), vp]
         L.locks_scan.argtypes = [vp, i32, P(CSummaries), P(CPageTable), vp, vp, vp, vp]
         L.locks_topk.argtypes = [vp, P(CPageTable), i32, i32, i32, i32, vp, vp, vp, vp]
         L.locks_sparse_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, i32, vp, vp,
@@ -103,7 +109,7 @@ def lib() -> ctypes.CDLL:
         L.locks_last_hip_error.restype = i32
         L.locks_version.restype = i32
         for fn in ("locks_build_summaries", "locks_select", "locks_scan", "locks_topk",
-                   "locks_mean_share", "locks_refresh_summaries",
+                   "locks_mean_share", "locks_refresh_summaries", "locks_quantize_summaries",
                    "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
                    "locks_step_graph_launch"):
             getattr(L, fn).restype = i32
@@ -158,19 +164,43 @@ class PageTable:
 
 @dataclass
 class Summaries:
-    mu: torch.Tensor     # [NB][H_kv][d]
-    basis: torch.Tensor  # [NB][H_kv][r][d]
-    coef: torch.Tensor   # [NB][H_kv][P][r]
+    mu: torch.Tensor     # [NB][H_kv][d]          (int8 codes for Q8Q4)
+    basis: torch.Tensor  # [NB][H_kv][r][d]       (Q8Q4: [NB][H_kv][r][d/2] uint8, int4 pairs)
+    coef: torch.Tensor   # [NB][H_kv][P][r]       (int8 codes for Q8Q4)
+    scales: torch.Tensor | None = None  # Q8Q4: [NB][H_kv][1 + 2r] float32
 
     @staticmethod
     def empty(num_blocks, num_kv_heads, page_size, head_dim, rank, device="cuda",
               dtype=torch.float32):
+        if dtype == Q8Q4:
+            i8 = dict(dtype=torch.int8, device=device)
+            return Summaries(torch.empty(num_blocks, num_kv_heads, head_dim, **i8),
+                             torch.empty(num_blocks, num_kv_heads, rank, head_dim // 2,
+                                         dtype=torch.uint8, device=device),
+                             torch.empty(num_blocks, num_kv_heads, page_size, rank, **i8),
+                             torch.empty(num_blocks, num_kv_heads, 1 + 2 * rank,
+                                         dtype=torch.float32, device=device))
         f = dict(dtype=dtype, device=device)
         return Summaries(torch.empty(num_blocks, num_kv_heads, head_dim, **f),
                          torch.empty(num_blocks, num_kv_heads, rank, head_dim, **f),
                          torch.empty(num_blocks, num_kv_heads, page_size, rank, **f))
 
+    @property
+    def quantised(self) -> bool:
+        return self.scales is not None
+
     def c(self) -> CSummaries:
+        if self.quantised:
+            NB, H, d = self.mu.shape
+            r, P = self.basis.shape[2], self.coef.shape[2]
+            assert self.mu.dtype == torch.int8 and self.basis.dtype == torch.uint8
+            assert self.coef.dtype == torch.int8 and self.scales.dtype == torch.float32
+            assert self.basis.shape[3] * 2 == d and self.scales.shape[2] == 1 + 2 * r
+            for t in (self.mu, self.basis, self.coef, self.scales):
+                assert t.is_contiguous()
+            return CSummaries(LOCKS_Q8Q4, NB, H, P, d, r, self.mu.data_ptr(),
+                              self.basis.data_ptr(), self.coef.data_ptr(),
+                              self.scales.data_ptr())
         NB, H, r, d = self.basis.shape
         P = self.coef.shape[2]
         dt = self.mu.dtype
@@ -178,7 +208,7 @@ class Summaries:
         for t in (self.mu, self.basis, self.coef):
             assert t.dtype == dt and t.is_contiguous()
         return CSummaries(LOCKS_BF16 if dt == torch.bfloat16 else LOCKS_F32, NB, H, P, d, r,
-                          self.mu.data_ptr(), self.basis.data_ptr(), self.coef.data_ptr())
+                          self.mu.data_ptr(), self.basis.data_ptr(), self.coef.data_ptr(), None)
 
 
 def workspace_bytes(op, batch, max_pages, num_q_heads, num_kv_heads, page_size, head_dim, rank,
@@ -232,6 +262,13 @@ def locks_refresh_summaries(cache: PagedKV, pages: PageTable, page_begin, max_ne
     _check(lib().locks_refresh_summaries(ctypes.byref(cc), ctypes.byref(pc), _ptr(page_begin),
                                          max_new_pages, ctypes.byref(sc), _stream(stream)),
            "locks_refresh_summaries")
+
+
+def locks_quantize_summaries(src: Summaries, dst: Summaries, stream=None):
+    """fp32 summaries -> int8 / int4 codes and scales (dst made with dtype=Q8Q4)."""
+    a, b = src.c(), dst.c()
+    _check(lib().locks_quantize_summaries(ctypes.byref(a), ctypes.byref(b), _stream(stream)),
+           "locks_quantize_summaries")
 
 
 def locks_mean_share(head_logmass, num_kv_heads, pages: PageTable, page_size, page_logmass,

@@ -32,12 +32,18 @@ locks_status check_page_table(const locks_page_table* pt) {
     return LOCKS_OK;
 }
 
+static_assert((int)LOCKS_F32 == (int)locks::kSummF32 && (int)LOCKS_BF16 == (int)locks::kSummBF16 &&
+                  (int)LOCKS_Q8Q4 == (int)locks::kSummQ8Q4,
+              "summary dtypes are passed through to the kernels");
+
 locks_status check_summaries(const locks_summaries* s, bool need_data) {
     if (!s || s->num_blocks <= 0 || s->num_kv_heads <= 0 || s->page_size <= 0 ||
         s->head_dim <= 0 || s->rank <= 0)
         return LOCKS_ERR_INVALID_ARG;
-    if (s->dtype != LOCKS_F32 && s->dtype != LOCKS_BF16) return LOCKS_ERR_INVALID_ARG;
+    if (s->dtype != LOCKS_F32 && s->dtype != LOCKS_BF16 && s->dtype != LOCKS_Q8Q4)
+        return LOCKS_ERR_INVALID_ARG;
     if (need_data && (!s->mu || !s->basis || !s->coef)) return LOCKS_ERR_INVALID_ARG;
+    if (need_data && s->dtype == LOCKS_Q8Q4 && !s->scales) return LOCKS_ERR_INVALID_ARG;
     if (!locks::scan_supported(s->page_size, s->head_dim, s->rank)) return LOCKS_ERR_UNSUPPORTED;
     return LOCKS_OK;
 }
@@ -130,7 +136,8 @@ locks_status scan_common(const float* q, int32_t hq, const locks_summaries* s,
     p.mu = s->mu;
     p.basis = s->basis;
     p.coef = s->coef;
-    p.summ_bf16 = s->dtype == LOCKS_BF16;
+    p.summ_dtype = s->dtype;  // locks_dtype values match locks::SummDtype
+    p.scales = s->scales;
     p.block_table = pt->block_table;
     p.seq_lens = pt->seq_lens;
     p.batch = pt->batch;
@@ -249,7 +256,8 @@ locks_status build_common(const locks_kv_cache* cache, const locks_page_table* p
     p.mu = out->mu;
     p.basis = out->basis;
     p.coef = out->coef;
-    p.out_bf16 = out->dtype == LOCKS_BF16;
+    p.out_dtype = out->dtype;
+    p.scales = out->scales;
     const hipError_t e = locks::launch_build(p, stream);
     return e == hipSuccess ? LOCKS_OK : hip_fail(e);
 }
@@ -270,6 +278,32 @@ locks_status locks_refresh_summaries(const locks_kv_cache* cache, const locks_pa
     if (!page_begin || max_new_pages <= 0) return LOCKS_ERR_INVALID_ARG;
     return build_common(cache, pages, page_begin, max_new_pages, out,
                         static_cast<hipStream_t>(stream));
+}
+
+locks_status locks_quantize_summaries(const locks_summaries* src, const locks_summaries* dst,
+                                      void* stream) {
+    locks_status st = check_summaries(src, true);
+    if (st != LOCKS_OK) return st;
+    if ((st = check_summaries(dst, true)) != LOCKS_OK) return st;
+    if (src->dtype != LOCKS_F32 || dst->dtype != LOCKS_Q8Q4 ||
+        src->num_blocks != dst->num_blocks || src->num_kv_heads != dst->num_kv_heads ||
+        src->page_size != dst->page_size || src->head_dim != dst->head_dim ||
+        src->rank != dst->rank)
+        return LOCKS_ERR_INVALID_ARG;
+    locks::QuantParams p{};
+    p.mu = static_cast<const float*>(src->mu);
+    p.basis = static_cast<const float*>(src->basis);
+    p.coef = static_cast<const float*>(src->coef);
+    p.mu_q = static_cast<int8_t*>(dst->mu);
+    p.basis_q = static_cast<uint8_t*>(dst->basis);
+    p.coef_q = static_cast<int8_t*>(dst->coef);
+    p.scales = dst->scales;
+    p.units = (int64_t)src->num_blocks * src->num_kv_heads;
+    p.page_size = src->page_size;
+    p.head_dim = src->head_dim;
+    p.rank = src->rank;
+    const hipError_t e = locks::launch_quantize(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
 }
 
 locks_status locks_scan(const float* q, int32_t num_q_heads, const locks_summaries* summaries,
@@ -468,6 +502,6 @@ const char* locks_status_string(int32_t status) {
 
 int32_t locks_last_hip_error(void) { return g_last_hip_error; }
 
-int32_t locks_version(void) { return 104; }
+int32_t locks_version(void) { return 105; }
 
 }  // extern "C"

@@ -28,6 +28,7 @@
 //     numerically null and gives a zero basis row and coefficient column.
 #include "device_common.hpp"
 #include "launchers.hpp"
+#include "quant.hpp"
 
 namespace locks {
 
@@ -121,7 +122,8 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
     constexpr int S = P + 2;    // row of a position-space matrix (even: 8-byte pairs)
     constexpr int UP = P + 1;   // padded row of U
     // the Jacobi's two position-space buffers of A; afterwards U and the basis rows
-    constexpr int JB = 2 * P * S > P * UP + 16 * D ? 2 * P * S : P * UP + 16 * D;
+    // (and, for quantised output, the coefficients)
+    constexpr int JB = 2 * P * S > P * UP + 16 * D + 16 * P ? 2 * P * S : P * UP + 16 * D + 16 * P;
     // Kc; during the sweeps (Kc idle) the two position-space buffers of U
     constexpr int KB = P * KP > 2 * P * S ? P * KP : 2 * P * S;
     __shared__ __attribute__((aligned(16))) float kbuf[KB];
@@ -133,6 +135,7 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
     __shared__ int more[2];           // a sweep left a coupled pair (by sweep parity)
     __shared__ int slot[16];
     __shared__ float trace_s;
+    __shared__ float q_amax[1 + 2 * 16], q_s[1 + 2 * 16];  // quantiser scratch
     float (*const U)[UP] = reinterpret_cast<float (*)[UP]>(jbuf);
     float (*const vs)[D] = reinterpret_cast<float (*)[D]>(jbuf + P * UP);
     // canonical (upper) slot of position-space entry (x, y)
@@ -407,9 +410,25 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
     }
     __syncthreads();
     // outputs: centroid, basis, coefficients = coordinates Kc V^T, stored as
-    // fp32 or rounded to bf16 (nearest even)
+    // fp32, rounded to bf16 (nearest even), or as int8 / int4 codes
+    if (a.out_dtype == kSummQ8Q4) {
+        float* cs = jbuf + P * UP + 16 * D;  // [P][r] coefficients, after U and the basis rows
+        for (int i = t; i < P * r; i += NT) {
+            const int tok = i / r, k = i % r;
+            float s = 0.f;
+            for (int d = 0; d < D; ++d) s += kc[tok][d] * vs[k][d];
+            cs[i] = s;
+        }
+        __syncthreads();
+        quantize_unit<P, D, NT>(mu_s, &vs[0][0], D, cs, r, r,
+                                static_cast<int8_t*>(a.mu) + unit * D,
+                                static_cast<uint8_t*>(a.basis) + unit * (size_t)r * (D / 2),
+                                static_cast<int8_t*>(a.coef) + unit * (size_t)P * r,
+                                a.scales + unit * (size_t)(1 + 2 * r), q_amax, q_s, t);
+        return;
+    }
     auto put = [&](void* base, size_t idx, float v) {
-        if (a.out_bf16)
+        if (a.out_dtype == kSummBF16)
             static_cast<uint16_t*>(base)[idx] = f32_to_bf16_bits(v);
         else
             static_cast<float*>(base)[idx] = v;

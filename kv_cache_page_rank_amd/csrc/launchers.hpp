@@ -13,12 +13,16 @@ namespace locks {
 // to read only the runs that can hold a winner.
 constexpr int kRunPages = 16;
 
+// Stored summary element types.
+enum SummDtype : int32_t { kSummF32 = 0, kSummBF16 = 1, kSummQ8Q4 = 2 };
+
 struct ScanParams {
     const float* q;        // [B][Hq][D]
-    const void* mu;        // [NB][Hkv][D]       fp32 or bf16 (summ_bf16)
-    const void* basis;     // [NB][Hkv][r][D]
+    const void* mu;        // [NB][Hkv][D]       fp32, bf16 or int8 codes (summ_dtype)
+    const void* basis;     // [NB][Hkv][r][D]    (int4 codes: [NB][Hkv][r][D/2] bytes)
     const void* coef;      // [NB][Hkv][P][r]
-    int32_t summ_bf16;
+    const float* scales;   // kSummQ8Q4: [NB][Hkv][1 + 2r]
+    int32_t summ_dtype;
     const int32_t* block_table;
     const int32_t* seq_lens;
     int32_t batch, num_q_heads, num_kv_heads, max_pages, num_blocks;
@@ -84,12 +88,27 @@ struct BuildParams {
     int32_t refresh_pages;     // > 0: only pages page_begin[b] .. + refresh_pages - 1
     int32_t batch, num_kv_heads, max_pages, num_blocks;
     int32_t page_size, head_dim, rank;
-    void* mu;              // fp32 or bf16 (out_bf16)
+    void* mu;              // fp32, bf16 or int8/int4 codes (out_dtype)
     void* basis;
     void* coef;
-    int32_t out_bf16;
+    float* scales;         // kSummQ8Q4: [NB][Hkv][1 + 2r]
+    int32_t out_dtype;     // SummDtype
 };
 hipError_t launch_build(const BuildParams& p, hipStream_t s);
 bool build_supported(int page_size, int head_dim, int rank);
+
+// fp32 summaries -> int8 / int4 codes and scales, every unit of the pools.
+struct QuantParams {
+    const float* mu;       // [units][D]
+    const float* basis;    // [units][r][D]
+    const float* coef;     // [units][P][r]
+    int8_t* mu_q;          // [units][D]
+    uint8_t* basis_q;      // [units][r][D/2]
+    int8_t* coef_q;        // [units][P][r]
+    float* scales;         // [units][1 + 2r]
+    int64_t units;
+    int32_t page_size, head_dim, rank;
+};
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 
 }  // namespace locks

@@ -45,11 +45,16 @@ struct WaveCtx {
     float qf[D / 4];
 };
 
-// Summary element types: fp32, or bf16 bit patterns (uint16_t).  E =
-// elements per 16-byte load.
+// Summary element types: fp32, bf16 bit patterns (uint16_t), or int8 / int4
+// codes (int8_t).  E = elements per lane and 32-wide d chunk of the query
+// fragment (16-byte loads for fp32 and bf16; the codes reuse bf16's layout).
 template <typename TS>
 struct Summ {
     static constexpr int E = 16 / (int)sizeof(TS);
+};
+template <>
+struct Summ<int8_t> {
+    static constexpr int E = 8;
 };
 
 // Address of element `off` of `base`.  kOff32: every summary array is below
@@ -450,6 +455,208 @@ __device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveC
     }
 }
 
+// Integer codes widened to bf16: small integers are exact in bf16, so the
+// bf16 MFMA products of the codes with the split query stay exact; the
+// scales are applied in fp32 to the accumulated sums.  The codes are read
+// as unsigned fields with the sign bit flipped (excess-8 / excess-128) and
+// the bias subtracted in float, which is exact: a sign-extending field
+// extract followed by an int-to-float convert is folded by this compiler into
+// an unsigned convert of the sign-extended value, wrong for negative codes.
+// 8 int4 codes (element e in bits 4e..4e+3) -> 8 bf16, pairs packed low first.
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+__device__ __forceinline__ u32x4 widen_i4x8(uint32_t w) {
+    const uint32_t u = w ^ 0x88888888u;  // two's complement -> excess-8
+    u32x4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float lo = (float)((u >> (8 * p)) & 15u) - 8.f;
+        const float hi = (float)((u >> (8 * p + 4)) & 15u) - 8.f;
+        o[p] = bf16_pair(lo, hi);
+    }
+    return o;
+}
+// 4 int8 codes (element e in byte e) -> 4 bf16.
+__device__ __forceinline__ u32x2 widen_i8x4(uint32_t w) {
+    const uint32_t u = w ^ 0x80808080u;  // two's complement -> excess-128
+    u32x2 o;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const float lo = (float)((u >> (16 * p)) & 255u) - 128.f;
+        const float hi = (float)((u >> (16 * p + 8)) & 255u) - 128.f;
+        o[p] = bf16_pair(lo, hi);
+    }
+    return o;
+}
+
+// One batch of kBatch pages with int8 / int4 summaries: the bf16 scan's
+// operand layout and MFMAs on the widened codes.  With codes m (centroid),
+// v (basis), c (coefficients) and scales s_mu, s_v[k], s_c[k]:
+//   beta = s_mu (m . q),   t_k = s_v[k] s_c[k] (v_k . q),   logit_i = beta + sum_k c_ik t_k,
+// the same estimator on the dequantised summary (scale * code).
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
+__device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<D>& x) {
+    constexpr int PPT = 16 / RR;          // pages per tile
+    constexpr int NTILE = kBatch / PPT;
+    constexpr int MT = P / 16;            // token tiles per page
+    constexpr int NCH = D / 32;           // 32-wide d chunks
+    constexpr int WPP = RR / 4;           // lane groups per page in the coefficient operand
+    constexpr int PF = kPrefetch;
+    using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
+    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
+    const int my_phys = x.my_phys;
+    const int SC = 1 + 2 * r;             // scales per unit
+    const uint8_t* const mu_q = static_cast<const uint8_t*>(a.mu);
+    const uint8_t* const basis_q = static_cast<const uint8_t*>(a.basis);
+    const uint8_t* const coef_q = static_cast<const uint8_t*>(a.coef);
+
+    // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e
+    bf16x8 qp[3][NCH];
+#pragma unroll
+    for (int t = 0; t < NCH; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            __bf16 h, m, l;
+            split3(x.qf[8 * t + e], h, m, l);
+            qp[0][t][e] = h;
+            qp[1][t][e] = m;
+            qp[2][t][e] = l;
+        }
+
+    const int a_pin = c / RR, a_k = c % RR;   // basis row loaded by this lane
+    const int c_pin = w / WPP;                // page whose coefficients this lane supplies
+    const int c_k0 = 4 * (w % WPP);           // its first coefficient index
+    const int s_pin = (4 * w) / RR;           // page of the T rows 4w..4w+3 this lane holds
+    const int s_k0 = (4 * w) % RR;            // their first basis index
+    struct Tile {
+        uint32_t v[NCH];   // 8 int4 codes per chunk
+        uint32_t cf[MT];   // 4 int8 codes per token tile
+        float sc[4];       // s_v[k] s_c[k] of the lane's four T rows
+    };
+    auto load_tile = [&](int tt, Tile& T) {
+        const int pj = __shfl(my_phys, tt * PPT + a_pin, kWave);
+        const bool row_ok = !kMasked || (pj >= 0 && a_k < r);
+        const Off src = (((Off)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
+                         (kMasked && a_k >= r ? r - 1 : a_k)) * (D / 2) + 4 * w;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(basis_q + src + 16 * t);
+            T.v[t] = row_ok ? v : 0u;
+        }
+        const int pp = __shfl(my_phys, tt * PPT + c_pin, kWave);
+        const bool ok = !kMasked || pp >= 0;
+        const Off csrc = ((Off)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const Off row = csrc + (Off)(16 * mt + c) * r;
+            if constexpr (kExact) {
+                const uint32_t v = *reinterpret_cast<const uint32_t*>(coef_q + row + c_k0);
+                T.cf[mt] = ok ? v : 0u;
+            } else {  // padded rank: byte by byte, clamped and zeroed past it
+                uint32_t hv = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kk = c_k0 + e;
+                    const uint32_t b = coef_q[row + (kk < r ? kk : r - 1)];
+                    hv |= ((ok && kk < r) ? b : 0u) << (8 * e);
+                }
+                T.cf[mt] = hv;
+            }
+        }
+        const int ps = __shfl(my_phys, tt * PPT + s_pin, kWave);
+        const float* sp = a.scales + ((size_t)(kMasked && ps < 0 ? 0 : ps) * Hkv + g) * SC;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int k = s_k0 + v;
+            const bool kok = (!kMasked || ps >= 0) && (kExact || k < r);
+            const int kc = kExact || k < r ? k : r - 1;
+            T.sc[v] = kok ? sp[1 + kc] * sp[1 + r + kc] : 0.f;
+        }
+    };
+
+    Tile ring[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF && i < NTILE; ++i) load_tile(i, ring[i]);
+
+    // beta tile: A row m = page j0 + m (lane column c supplies row c).
+    f32x4 beta;
+    {
+        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + 8 * w;
+        f32x4 bacc[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) bacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            u32x2 m8 = *reinterpret_cast<const u32x2*>(mu_q + src + 32 * t);
+            if (kMasked && my_phys < 0) m8 = u32x2{0u, 0u};
+            const u32x2 lo = widen_i8x4(m8[0]), hi = widen_i8x4(m8[1]);
+            const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int i = 0; i < 3; ++i) bacc[i] = mfma_16x16x32_bf16(as_bf16x8(v), qp[i][t], bacc[i]);
+        }
+        beta = bacc[0] + bacc[1] + bacc[2];
+        // rows 4w + v are pages j0 + 4w + v: their centroid scales
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int pv = __shfl(my_phys, 4 * w + v, kWave);
+            const float sm = a.scales[((size_t)(pv < 0 ? 0 : pv) * Hkv + g) * SC];
+            beta[v] *= pv < 0 ? 0.f : sm;
+        }
+    }
+
+    float run_mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) {
+        if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
+        const Tile& cur = ring[tt % (PF + 1)];
+        f32x4 tacc[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const bf16x8 vb = as_bf16x8(widen_i4x8(cur.v[t]));
+#pragma unroll
+            for (int i = 0; i < 3; ++i) tacc[i] = mfma_16x16x32_bf16(vb, qp[i][t], tacc[i]);
+        }
+        f32x4 T = tacc[0] + tacc[1] + tacc[2];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) T[v] *= cur.sc[v];
+        // lane (w, c) holds T[tile row 4w + v][head c]: its B operand rows of the
+        // coefficient product, split into three bf16 parts
+        bf16x4 tp[3];
+        {
+            __bf16 hv[4], mv[4], lv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) split3(T[v], hv[v], mv[v], lv[v]);
+            typedef __bf16 bf16v4 __attribute__((ext_vector_type(4)));
+            tp[0] = __builtin_bit_cast(bf16x4, bf16v4{hv[0], hv[1], hv[2], hv[3]});
+            tp[1] = __builtin_bit_cast(bf16x4, bf16v4{mv[0], mv[1], mv[2], mv[3]});
+            tp[2] = __builtin_bit_cast(bf16x4, bf16v4{lv[0], lv[1], lv[2], lv[3]});
+        }
+        f32x4 L[PPT][MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const bf16x4 cw = as_bf16x4(widen_i8x4(cur.cf[mt]));
+#pragma unroll
+            for (int p = 0; p < PPT; ++p) {
+                const bf16x4 A = c_pin == p ? cw : bf16x4{0, 0, 0, 0};
+                f32x4 acc = mfma_16x16x16_bf16(A, tp[0], f32x4{0.f, 0.f, 0.f, 0.f});
+                acc = mfma_16x16x16_bf16(A, tp[1], acc);
+                L[p][mt] = mfma_16x16x16_bf16(A, tp[2], acc);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], tt * PPT + p, beta, run_mx);
+    }
+    if (a.run_max) {
+        run_mx = max_over_rows(run_mx);
+        const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
+        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
+    }
+}
+
 template <typename TS, int P, int D, int RR, bool kExact, bool kHeads, bool kOff32>
 __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     static_assert(P % 16 == 0 && D % 32 == 0, "P a multiple of 16, d of 32");
@@ -518,14 +725,18 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     // every page of the batch present and the rank not padded: no masking
     if constexpr (kExact) {
         if (x.j0 + kBatch <= full && __ballot(c < kBatch && x.my_phys < 0) == 0ull) {
-            if constexpr (sizeof(TS) == 2)
+            if constexpr (sizeof(TS) == 1)
+                scan_batch_q<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
+            else if constexpr (sizeof(TS) == 2)
                 scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
             else
                 scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
             return;
         }
     }
-    if constexpr (sizeof(TS) == 2)
+    if constexpr (sizeof(TS) == 1)
+        scan_batch_q<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
+    else if constexpr (sizeof(TS) == 2)
         scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
     else
         scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
@@ -545,7 +756,11 @@ hipError_t launch4(const ScanParams& p, hipStream_t s, unsigned blocks) {
 template <typename TS, int P, int D, int RR>
 hipError_t launch_ts(const ScanParams& p, hipStream_t s, unsigned blocks) {
     // largest summary array (basis or coefficients) in bytes
-    const size_t per_unit = (size_t)p.rank * (D > P ? D : P) * sizeof(TS);
+    size_t per_unit = (size_t)p.rank * (D > P ? D : P) * sizeof(TS);
+    if (sizeof(TS) == 1) {  // codes: centroid D, basis r D/2, coefficients P r bytes
+        per_unit = (size_t)p.rank * (D / 2 > P ? D / 2 : P);
+        per_unit = per_unit > (size_t)D ? per_unit : (size_t)D;
+    }
     const bool off32 = (size_t)p.num_blocks * p.num_kv_heads * per_unit < (size_t(1) << 32);
     if (p.head_logmass != nullptr)
         return off32 ? launch4<TS, P, D, RR, true, true>(p, s, blocks)
@@ -559,8 +774,9 @@ hipError_t launch(const ScanParams& p, hipStream_t s) {
     const long waves = (long)p.batch * p.num_kv_heads * ((p.max_pages + kBatch - 1) / kBatch);
     const unsigned blocks = (unsigned)((waves + 3) / 4);
     if (blocks == 0) return hipSuccess;
-    return p.summ_bf16 ? launch_ts<uint16_t, P, D, RR>(p, s, blocks)
-                       : launch_ts<float, P, D, RR>(p, s, blocks);
+    if (p.summ_dtype == kSummQ8Q4) return launch_ts<int8_t, P, D, RR>(p, s, blocks);
+    return p.summ_dtype == kSummBF16 ? launch_ts<uint16_t, P, D, RR>(p, s, blocks)
+                                     : launch_ts<float, P, D, RR>(p, s, blocks);
 }
 
 template <int P, int D>

@@ -8,7 +8,11 @@ An attended unit is one (page, KV head) of K and V.
 from __future__ import annotations
 
 
-def summary_unit_bytes(d: int, P: int, r: int, elem: int = 4) -> int:
+def summary_unit_bytes(d: int, P: int, r: int, elem=4) -> int:
+    """elem: bytes per value (4 fp32, 2 bf16), or "q8q4" for integer codes:
+    int8 centroid and coefficients, int4 basis, 1 + 2r fp32 scales."""
+    if elem == "q8q4":
+        return d + r * d // 2 + P * r + 4 * (1 + 2 * r)
     return elem * (d + r * d + P * r)
 
 

@@ -39,7 +39,7 @@ def test_header_symbols_exported(lk):
 
 def test_version_and_status_strings(lk):
     lib = lk.lib()
-    assert lib.locks_version() == 104
+    assert lib.locks_version() == 105
     assert lib.locks_status_string(0) == b"ok"
     assert b"workspace" in lib.locks_status_string(3)
     assert lib.locks_status_string(99) == b"unknown status"
@@ -64,11 +64,11 @@ def test_workspace_sizes(lk):
     assert ws(lk.OP_SELECT, 0, 16384, 32, 2, 64, 128, 8, 32) == 0
 
 
-def _fake(lk, P=64, d=128, r=8, H=2, NB=4, B=1, MP=4, dtype=1, sdtype=0):
+def _fake(lk, P=64, d=128, r=8, H=2, NB=4, B=1, MP=4, dtype=1, sdtype=0, scales=True):
     # non-null "device" addresses: validation never dereferences them
     addr = 0x1000
     kv = lk.CKVCache(dtype, NB, H, P, d, addr, addr)
-    sm = lk.CSummaries(sdtype, NB, H, P, d, r, addr, addr, addr)
+    sm = lk.CSummaries(sdtype, NB, H, P, d, r, addr, addr, addr, addr if scales else None)
     pt = lk.CPageTable(B, MP, addr, addr)
     return kv, sm, pt, ctypes.c_void_p(addr)
 
@@ -121,13 +121,25 @@ def test_host_validation_rejects_without_launch(lk):
         lk.LOCKS_ERR_WORKSPACE
     assert lib.locks_mean_share(None, 32, 2, by(pt), 64, p, None, p, 1024, None) == \
         lk.LOCKS_ERR_INVALID_ARG
-    _, sm_dt, _, _ = _fake(lk, sdtype=5)  # summary dtype neither fp32 nor bf16
+    _, sm_dt, _, _ = _fake(lk, sdtype=5)  # not a summary dtype
     assert lib.locks_scan(p, 32, by(sm_dt), by(pt), p, None, None, None) == lk.LOCKS_ERR_INVALID_ARG
     assert lib.locks_build_summaries(by(kv), by(pt), None, by(sm_dt), None, 0, None) == \
         lk.LOCKS_ERR_INVALID_ARG
     _, sm_d, _, _ = _fake(lk, d=64)
     assert lib.locks_build_summaries(by(kv), by(pt), None, by(sm_d), None, 0, None) == \
         lk.LOCKS_ERR_INVALID_ARG
+    # integer-code summaries need their scales; quantise wants fp32 -> Q8Q4 of one shape
+    _, sm_q, _, _ = _fake(lk, sdtype=lk.LOCKS_Q8Q4)
+    _, sm_qn, _, _ = _fake(lk, sdtype=lk.LOCKS_Q8Q4, scales=False)
+    assert lib.locks_scan(p, 32, by(sm_qn), by(pt), p, None, None, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_build_summaries(by(kv), by(pt), None, by(sm_qn), None, 0, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_quantize_summaries(by(sm_q), by(sm_q), None) == lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_quantize_summaries(by(sm), by(sm), None) == lk.LOCKS_ERR_INVALID_ARG
+    _, sm_q4, _, _ = _fake(lk, sdtype=lk.LOCKS_Q8Q4, r=4)
+    assert lib.locks_quantize_summaries(by(sm), by(sm_q4), None) == lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_quantize_summaries(None, by(sm_q), None) == lk.LOCKS_ERR_INVALID_ARG
     # sparse attend with pages requested but no list
     assert lib.locks_sparse_attend(p, 32, by(kv), by(pt), None, 4, p, None, p, 1 << 30, None) == \
         lk.LOCKS_ERR_INVALID_ARG

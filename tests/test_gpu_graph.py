@@ -5,7 +5,8 @@ import pytest
 import torch
 
 from gpu_cases import DEV, Case, bf16_small, say, tiny
-from workload.device import summaries_to_device
+import oracle
+from workload.device import codes_to_device, summaries_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -13,13 +14,17 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("mk,sdt,agg", [(lambda: tiny(), torch.float32, 0),
                                         (lambda: bf16_small(), torch.float32, 0),
                                         (lambda: bf16_small(), torch.bfloat16, 0),
+                                        (lambda: bf16_small(), "q8q4", 0),
                                         (lambda: bf16_small(), torch.float32, 1)],
-                         ids=["tiny", "bf16", "bf16-summaries", "mean-share"])
+                         ids=["tiny", "bf16", "bf16-summaries", "code-summaries", "mean-share"])
 def test_graph_replay_equals_eager(mk, sdt, agg):
     import kv_cache_page_rank_amd as lk
     case = Case(mk())
     s = case.spec
-    summ = summaries_to_device(*case.oracle_summaries(), dtype=sdt)
+    if sdt == "q8q4":
+        summ = codes_to_device(*oracle.quantize_pool(*case.oracle_summaries()))
+    else:
+        summ = summaries_to_device(*case.oracle_summaries(), dtype=sdt)
     k = s.k_pages
     ws_b = lk.workspace_bytes(lk.OP_STEP, s.batch, s.max_pages, s.num_q_heads, s.num_kv_heads,
                               s.page_size, s.head_dim, s.rank, k)

@@ -87,17 +87,16 @@ def test_scan_bf16_summaries_match_oracle(name, mk):
 
 
 def test_select_bf16_summaries_band():
-    """locks_select over GPU-built bf16 summaries against the oracle's
-    selection from the same (downloaded) summaries."""
+    """locks_select over bf16 summaries (the oracle's, rounded to nearest
+    even) against the oracle's selection from the same rounded values."""
     case = Case(bf16_small())
     s = case.spec
     import kv_cache_page_rank_amd as lk
-    summ = lk.Summaries.empty(s.num_blocks, s.num_kv_heads, s.page_size, s.head_dim, s.rank,
-                              dtype=torch.bfloat16)
+    mu, basis, coef = (torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+                       for x in case.oracle_summaries())
+    summ = lk.Summaries(mu.to(DEV), basis.to(DEV), coef.to(DEV))
     say("select bf16 summaries")
-    lk.locks_build_summaries(case.kv, case.pages, summ)
-    torch.cuda.synchronize()
-    wide = [x.float().cpu().numpy() for x in (summ.mu, summ.basis, summ.coef)]
+    wide = [x.float().numpy() for x in (mu, basis, coef)]
     _, page_o = oracle.scan_pool(case.lay, s.rank, case.layer.q, *wide, heads=False)
     k = s.k_pages
     sel_o, _ = oracle.select_pool(case.lay, s.budget_tokens, page_o.astype(np.float32), k)

@@ -32,3 +32,13 @@ def summaries_to_device(mu, basis, coef, device="cuda", dtype=torch.float32):
     import kv_cache_page_rank_amd as lk
     return lk.Summaries(*(torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device).to(dtype)
                           for x in (mu, basis, coef)))
+
+
+def codes_to_device(mu_q, basis_q, coef_q, scales, device="cuda"):
+    """Host int8 / int4 summary codes and fp32 scales as device Summaries
+    (dtype Q8Q4 in the library's layout)."""
+    import kv_cache_page_rank_amd as lk
+    return lk.Summaries(torch.from_numpy(np.ascontiguousarray(mu_q, np.int8)).to(device),
+                        torch.from_numpy(np.ascontiguousarray(basis_q, np.uint8)).to(device),
+                        torch.from_numpy(np.ascontiguousarray(coef_q, np.int8)).to(device),
+                        torch.from_numpy(np.ascontiguousarray(scales, np.float32)).to(device))
