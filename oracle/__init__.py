@@ -74,6 +74,8 @@ def lib():
         L.orc_attend_pool.argtypes = [lay, _f32p, _f32p, _f32p, ctypes.c_void_p, c_int, _f64p,
                                       ctypes.c_void_p, c_int]
         vp = ctypes.c_void_p
+        L.orc_pooled_covariance.argtypes = [lay, vp, vp, c_int]
+        L.orc_sketch_pool.argtypes = [lay, c_int, vp, vp, vp, vp, c_int]
         L.orc_quantize_vec.argtypes = [c_int, c_int, vp, c_int, vp, vp]
         L.orc_quantize_vec.restype = None
         L.orc_quantize_pool.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
@@ -82,7 +84,7 @@ def lib():
                                           vp, vp]
         for fn in ("orc_build_pool", "orc_build_units", "orc_scan_pool", "orc_scan_units",
                    "orc_exact_pool", "orc_select_pool", "orc_attend_pool", "orc_quantize_pool",
-                   "orc_dequantize_pool"):
+                   "orc_dequantize_pool", "orc_pooled_covariance", "orc_sketch_pool"):
             getattr(L, fn).restype = c_int
         _lib = L
     return _lib
@@ -346,3 +348,47 @@ def dequantize_pool(mu_q, basis_q, coef_q, scales):
                                      coef_q.ctypes.data, scales.ctypes.data, mu.ctypes.data,
                                      basis.ctypes.data, coef.ctypes.data), "dequantize_pool")
     return mu, basis, coef
+
+
+# ------------------------------------------------------------------ shared-basis sketch
+def pooled_covariance(L: Layout, k_pool, threads: int = 0):
+    """sum over every full page of Kc^T Kc, per KV head: [Hkv][d][d] float64."""
+    kp = _f32(k_pool)
+    cov = np.zeros((L.num_kv_heads, L.head_dim, L.head_dim))
+    ref, _keep = L.c()
+    _check(lib().orc_pooled_covariance(ref, kp.ctypes.data, cov.ctypes.data, threads),
+           "pooled_covariance")
+    return cov
+
+
+def shared_basis(L: Layout, rho: int, k_pool, threads: int = 0):
+    """One rank-rho basis per KV head for the shared-basis ablation (reading in
+    locks_oracle.h): the top rho eigenvectors of the pooled within-page
+    covariance, eigenvalues descending (LAPACK eigh as the eigensolver).
+    Returns (basis [Hkv][rho][d] float64 rows, eigenvalues [Hkv][d] descending)."""
+    cov = pooled_covariance(L, k_pool, threads)
+    H, d = L.num_kv_heads, L.head_dim
+    basis = np.zeros((H, rho, d))
+    eig = np.zeros((H, d))
+    for g in range(H):
+        w, v = np.linalg.eigh(cov[g])
+        order = np.argsort(-w, kind="stable")
+        eig[g] = w[order]
+        basis[g] = v[:, order[:rho]].T
+    return basis, eig
+
+
+def sketch_pool(L: Layout, rho: int, k_pool, basis, num_blocks: int, threads: int = 0):
+    """Summaries of the shared-basis sketch in the page-summary layout, for the
+    same estimator: mu [NB][Hkv][d], the shared basis copied to every block
+    [NB][Hkv][rho][d], coordinates [NB][Hkv][P][rho] (float32)."""
+    kp = _f32(k_pool)
+    B = np.ascontiguousarray(basis, np.float64)
+    H, d, P = L.num_kv_heads, L.head_dim, L.page_size
+    mu = np.zeros((num_blocks, H, d), np.float32)
+    coef = np.zeros((num_blocks, H, P, rho), np.float32)
+    ref, _keep = L.c()
+    _check(lib().orc_sketch_pool(ref, rho, kp.ctypes.data, B.ctypes.data, mu.ctypes.data,
+                                 coef.ctypes.data, threads), "sketch_pool")
+    rep = np.broadcast_to(B.astype(np.float32)[None], (num_blocks, H, rho, d)).copy()
+    return mu, rep, coef

@@ -531,6 +531,80 @@ int orc_attend_pool(const orc_layout* L, const float* q, const float* k_pool,
     return 0;
 }
 
+/* ---------------- shared-basis sketch (ablation baseline) ---------------- */
+
+int orc_pooled_covariance(const orc_layout* L, const float* k_pool, double* cov, int nthreads) {
+    if (!layout_ok(L)) return -1;
+    const int P = L->page_size, d = L->head_dim, H = L->num_kv_heads;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    for (int g = 0; g < H; ++g) {
+        double* C = cov + (size_t)g * d * d;
+        memset(C, 0, sizeof(double) * (size_t)d * d);
+        for (int b = 0; b < L->batch; ++b) {
+            const int nf = full_pages(L, b) < L->max_pages ? full_pages(L, b) : L->max_pages;
+            #pragma omp parallel
+            {
+                double* part = (double*)calloc((size_t)d * d, sizeof(double));
+                double* kc = (double*)malloc(sizeof(double) * (size_t)P * d);
+                double* mu = (double*)malloc(sizeof(double) * (size_t)d);
+                #pragma omp for schedule(static)
+                for (int j = 0; j < nf; ++j) {
+                    const float* k = page_ptr(L, k_pool, b, g, j);
+                    for (int e = 0; e < d; ++e) {
+                        double acc = 0.0;
+                        for (int i = 0; i < P; ++i) acc += k[(size_t)i * d + e];
+                        mu[e] = acc / P;
+                    }
+                    for (int i = 0; i < P; ++i)
+                        for (int e = 0; e < d; ++e) kc[(size_t)i * d + e] = k[(size_t)i * d + e] - mu[e];
+                    for (int i = 0; i < P; ++i)
+                        for (int x = 0; x < d; ++x) {
+                            const double a = kc[(size_t)i * d + x];
+                            for (int y = 0; y < d; ++y) part[(size_t)x * d + y] += a * kc[(size_t)i * d + y];
+                        }
+                }
+                #pragma omp critical
+                for (size_t e = 0; e < (size_t)d * d; ++e) C[e] += part[e];
+                free(part);
+                free(kc);
+                free(mu);
+            }
+        }
+    }
+    return 0;
+}
+
+int orc_sketch_pool(const orc_layout* L, int rho, const float* k_pool, const double* basis,
+                    float* mu_out, float* coef_out, int nthreads) {
+    if (!layout_ok(L) || rho <= 0 || L->head_dim > 1024) return -1;
+    const int P = L->page_size, d = L->head_dim, H = L->num_kv_heads;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    for (int b = 0; b < L->batch; ++b) {
+        const int nf = full_pages(L, b) < L->max_pages ? full_pages(L, b) : L->max_pages;
+        #pragma omp parallel for collapse(2) schedule(static)
+        for (int j = 0; j < nf; ++j)
+            for (int g = 0; g < H; ++g) {
+                const float* k = page_ptr(L, k_pool, b, g, j);
+                const size_t unit = (size_t)L->block_table[(size_t)b * L->max_pages + j] * H + g;
+                double mu[1024];
+                for (int e = 0; e < d; ++e) {
+                    double acc = 0.0;
+                    for (int i = 0; i < P; ++i) acc += k[(size_t)i * d + e];
+                    mu[e] = acc / P;
+                    mu_out[unit * d + e] = (float)mu[e];
+                }
+                const double* V = basis + (size_t)g * rho * d;
+                for (int i = 0; i < P; ++i)
+                    for (int t = 0; t < rho; ++t) {
+                        double acc = 0.0;
+                        for (int e = 0; e < d; ++e) acc += (k[(size_t)i * d + e] - mu[e]) * V[(size_t)t * d + e];
+                        coef_out[(unit * P + i) * rho + t] = (float)acc;
+                    }
+            }
+    }
+    return 0;
+}
+
 /* ---------------- quantised summaries (section 2, "Kwantisatie") ---------------- */
 
 void orc_quantize_vec(int n, int stride, const float* x, int qmax, float* scale, int8_t* code) {

@@ -148,6 +148,25 @@ int orc_attend_pool(const orc_layout* L, const float* q, const float* k_pool,
                     const float* v_pool, const int32_t* sel_pages, int width, double* out,
                     double* lse, int nthreads);
 
+/* ---------------- shared-basis sketch (ablation baseline) ----------------
+ * The pages argue that a query-independent projection shared by every page
+ * is blind to page-specific directions (technical summary, section 3, the
+ * proposition on a shared rank-rho projection; the abstract's contrast with
+ * fixed sketches).  The baseline built to measure that: one rank-rho basis
+ * per KV head, the top rho eigenvectors of the pooled within-page covariance
+ * sum_j Kc_j^T Kc_j over every full page j (Kc_j = the page's keys minus its
+ * centroid); every page keeps its centroid and its tokens' coordinates in the
+ * shared basis, and is scored with the same estimator.  At rho =
+ * r (1 + d / P) it stores as many values per page as a rank-r page summary. */
+
+/* Pooled within-page covariance cov [Hkv][d][d] over every full page. */
+int orc_pooled_covariance(const orc_layout* L, const float* k_pool, double* cov, int nthreads);
+
+/* Centroids and shared-basis coordinates of every full page: mu [NB][Hkv][d],
+ * coef [NB][Hkv][P][rho] = (k_i - mu) . basis_k, basis [Hkv][rho][d]. */
+int orc_sketch_pool(const orc_layout* L, int rho, const float* k_pool, const double* basis,
+                    float* mu, float* coef, int nthreads);
+
 /* ---------------- quantised summaries ----------------
  * Stored precision (technical summary, section 2, "Kwantisatie": the basis
  * in int4, coefficients and centroid in int8).  The pages fix the widths

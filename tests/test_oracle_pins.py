@@ -557,3 +557,88 @@ def test_dequantised_estimate_on_grid_equals_unquantised(wl, orc):
     _, pm_a = orc.scan_pool(L, spec.rank, q, mu_g, basis_g, coef_g)
     _, pm_b = orc.scan_pool(L, spec.rank, q, *deq)
     assert np.array_equal(pm_a, pm_b)
+
+
+# ---------------------------------------------------------------- shared-basis sketch (ablation)
+# Baseline of the ablation: one basis per KV head, shared by every page
+# (technical summary, section 3, the proposition on shared projections).
+
+def _manual_layout(orc, K, Hq=2):
+    """Pool [NB][1][P][d] as one sequence of NB full pages."""
+    NB, H, P, d = K.shape
+    return orc.Layout(Hq, H, d, P, np.arange(NB, dtype=np.int32)[None],
+                      np.array([NB * P], np.int32))
+
+
+def test_pooled_covariance_matches_numpy(wl, orc):
+    spec, layer, lay = _small_layout(wl, orc, num_q_heads=2, num_kv_heads=2, seq_lens=[16 * 9 + 5])
+    K = layer.k_f32()
+    cov = orc.pooled_covariance(lay, K)
+    for g in range(2):
+        ref = np.zeros((spec.head_dim, spec.head_dim))
+        for j in range(9):
+            Kp = K[layer.block_table[0, j], g].astype(np.float64)
+            Kc = Kp - Kp.mean(0)
+            ref += Kc.T @ Kc
+        np.testing.assert_allclose(cov[g], ref, rtol=1e-12, atol=1e-10)
+
+
+def test_shared_basis_captures_the_top_energy(wl, orc):
+    """Eckart-Young for the pooled covariance: the residual of projecting every
+    page's centred keys on the shared basis is the sum of the trailing
+    eigenvalues; the basis is orthonormal."""
+    spec, layer, lay = _small_layout(wl, orc)
+    K = layer.k_f32()
+    rho = 10
+    basis, eig = orc.shared_basis(lay, rho, K)
+    V = basis[0]
+    assert np.abs(V @ V.T - np.eye(rho)).max() < 1e-12
+    resid = 0.0
+    for j in range(spec.seq_lens[0] // spec.page_size):
+        Kp = K[layer.block_table[0, j], 0].astype(np.float64)
+        Kc = Kp - Kp.mean(0)
+        resid += np.sum((Kc - Kc @ V.T @ V) ** 2)
+    assert resid == pytest.approx(eig[0, rho:].sum(), rel=1e-9)
+
+
+def test_sketch_is_exact_when_pages_share_one_subspace(orc):
+    """Keys of every page in one common m-dimensional subspace (plus the
+    page's own centroid): a shared basis of rank m spans every page, so the
+    sketch's page masses equal the exact ones."""
+    g = np.random.default_rng(8)
+    NB, P, d, m = 12, 16, 64, 5
+    W = g.standard_normal((m, d))
+    K = np.stack([g.standard_normal(d) + g.standard_normal((P, m)) @ W for _ in range(NB)])
+    K = K.astype(np.float32)[:, None]
+    lay = _manual_layout(orc, K)
+    q = (g.standard_normal((1, 2, d)) / 8).astype(np.float32)
+    basis, _ = orc.shared_basis(lay, m, K)
+    mu, rep, coef = orc.sketch_pool(lay, m, K, basis, NB)
+    _, est = orc.scan_pool(lay, m, q, mu, rep, coef)
+    _, exact = orc.exact_pool(lay, q, K)
+    np.testing.assert_allclose(est[0, 0, :NB], exact[0, 0, :NB], atol=1e-4)
+
+
+def test_sketch_is_blind_where_page_summaries_are_exact(orc):
+    """Every page in its own m-dimensional subspace: rank-m page summaries
+    are exact on every page, while the shared basis at the same storage
+    (rho = m (1 + d / P)) is not (the union of the subspaces is wider than
+    rho) - the pages' claim, on a constructed example; at rho = d it is."""
+    g = np.random.default_rng(9)
+    NB, P, d, m = 24, 16, 64, 3
+    K = np.stack([g.standard_normal(d) + g.standard_normal((P, m)) @ g.standard_normal((m, d))
+                  for _ in range(NB)]).astype(np.float32)[:, None]
+    lay = _manual_layout(orc, K)
+    q = (g.standard_normal((1, 2, d)) / 8).astype(np.float32)
+    _, exact = orc.exact_pool(lay, q, K)
+    exact = exact[0, 0, :NB]
+    mu, basis, coef = orc.build_pool(lay, m, K, NB)
+    _, page = orc.scan_pool(lay, m, q, mu, basis, coef)
+    assert np.abs(page[0, 0, :NB] - exact).max() < 1e-4
+    rho = m * (1 + d // P)
+    sb, _ = orc.shared_basis(lay, rho, K)
+    _, sketch = orc.scan_pool(lay, rho, q, *orc.sketch_pool(lay, rho, K, sb, NB))
+    assert np.abs(sketch[0, 0, :NB] - exact).max() > 1e-2
+    sb_full, _ = orc.shared_basis(lay, d, K)
+    _, full = orc.scan_pool(lay, d, q, *orc.sketch_pool(lay, d, K, sb_full, NB))
+    np.testing.assert_allclose(full[0, 0, :NB], exact, atol=1e-4)
