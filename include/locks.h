@@ -187,6 +187,25 @@ locks_status locks_refresh_summaries(const locks_kv_cache* cache, const locks_pa
                                      const locks_summaries* out, void* stream);
 
 /*
+ * Ablation baseline, not the method: the shared-basis sketch (technical
+ * summary, section 3, the proposition that a query-independent projection
+ * shared by every page is blind to page-specific directions; the abstract
+ * contrasts page-local summaries with fixed sketches).  Given one rank-rho
+ * basis per KV head, shared_basis [H_kv][rho][d] fp32 device (orthonormal
+ * rows; how it is chosen is the caller's: the ablation uses the top
+ * eigenvectors of the pooled within-page key covariance), every full page j
+ * >= page_begin[b] (NULL: all) gets mu = its mean key and coef[i][k] =
+ * (k_i - mu) . shared_basis[g][k]; out (LOCKS_F32, rank = rho) receives mu,
+ * coef and the shared basis copied to each block, so locks_select scores it
+ * with the same estimator.  At rho = r (1 + d / P) a page stores as many
+ * values (mu + P rho) as a rank-r page summary.
+ */
+locks_status locks_build_sketch_summaries(const locks_kv_cache* cache,
+                                          const locks_page_table* pages,
+                                          const int32_t* page_begin, const float* shared_basis,
+                                          const locks_summaries* out, void* stream);
+
+/*
  * Quantise fp32 summaries into LOCKS_Q8Q4 codes and scales (technical
  * summary, section 2, Kwantisatie; the quantiser is the one described at
  * locks_summaries), for every unit (block, KV head) of the pools.

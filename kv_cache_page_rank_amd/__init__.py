@@ -28,7 +28,8 @@ AGG_LSE, AGG_MEAN_SHARE = 0, 1  # locks_agg
 
 EXPORTED = ("locks_workspace_bytes", "locks_build_summaries", "locks_select", "locks_scan",
             "locks_topk", "locks_mean_share", "locks_refresh_summaries",
-            "locks_quantize_summaries", "locks_sparse_attend", "locks_dense_attend",
+            "locks_quantize_summaries", "locks_build_sketch_summaries", "locks_sparse_attend",
+            "locks_dense_attend",
             "locks_step_graph_create",
             "locks_step_graph_launch", "locks_step_graph_destroy", "locks_status_string",
             "locks_last_hip_error", "locks_version")
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.locks_refresh_summaries.argtypes = [P(CKVCache), P(CPageTable), vp, i32, P(CSummaries),
                                               vp]
         L.locks_quantize_summaries.argtypes = [P(CSummaries), P(CSummaries), vp]
+        L.locks_build_sketch_summaries.argtypes = [P(CKVCache), P(CPageTable), vp, vp,
+                                                   P(CSummaries), vp]
         L.locks_scan.argtypes = [vp, i32, P(CSummaries), P(CPageTable), vp, vp, vp, vp]
         L.locks_topk.argtypes = [vp, P(CPageTable), i32, i32, i32, i32, vp, vp, vp, vp]
         L.locks_sparse_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, i32, vp, vp,
@@ -110,6 +113,7 @@ def lib() -> ctypes.CDLL:
         L.locks_version.restype = i32
         for fn in ("locks_build_summaries", "locks_select", "locks_scan", "locks_topk",
                    "locks_mean_share", "locks_refresh_summaries", "locks_quantize_summaries",
+                   "locks_build_sketch_summaries",
                    "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
                    "locks_step_graph_launch"):
             getattr(L, fn).restype = i32
@@ -262,6 +266,18 @@ def locks_refresh_summaries(cache: PagedKV, pages: PageTable, page_begin, max_ne
     _check(lib().locks_refresh_summaries(ctypes.byref(cc), ctypes.byref(pc), _ptr(page_begin),
                                          max_new_pages, ctypes.byref(sc), _stream(stream)),
            "locks_refresh_summaries")
+
+
+def locks_build_sketch_summaries(cache: PagedKV, pages: PageTable, shared_basis, out: Summaries,
+                                 page_begin=None, stream=None):
+    """Shared-basis sketch (ablation baseline): shared_basis [H_kv][rho][d]
+    float32 on the device; out made with rank rho, float32."""
+    assert shared_basis.dtype == torch.float32 and shared_basis.is_contiguous()
+    cc, pc, sc = cache.c(), pages.c(), out.c()
+    _check(lib().locks_build_sketch_summaries(ctypes.byref(cc), ctypes.byref(pc),
+                                              _ptr(page_begin), _ptr(shared_basis),
+                                              ctypes.byref(sc), _stream(stream)),
+           "locks_build_sketch_summaries")
 
 
 def locks_quantize_summaries(src: Summaries, dst: Summaries, stream=None):

@@ -264,6 +264,41 @@ locks_status build_common(const locks_kv_cache* cache, const locks_page_table* p
 
 }  // namespace
 
+locks_status locks_build_sketch_summaries(const locks_kv_cache* cache,
+                                          const locks_page_table* pages,
+                                          const int32_t* page_begin, const float* shared_basis,
+                                          const locks_summaries* out, void* stream) {
+    locks_status st = check_cache(cache, false);
+    if (st != LOCKS_OK) return st;
+    if ((st = check_page_table(pages)) != LOCKS_OK) return st;
+    if ((st = check_summaries(out, true)) != LOCKS_OK) return st;
+    if (!shared_basis || out->dtype != LOCKS_F32 || out->num_blocks != cache->num_blocks ||
+        out->num_kv_heads != cache->num_kv_heads || out->page_size != cache->page_size ||
+        out->head_dim != cache->head_dim)
+        return LOCKS_ERR_INVALID_ARG;
+    if (!locks::build_supported(cache->page_size, cache->head_dim, out->rank))
+        return LOCKS_ERR_UNSUPPORTED;
+    locks::BuildParams p{};
+    p.k = cache->k;
+    p.bf16 = cache->dtype == LOCKS_BF16;
+    p.block_table = pages->block_table;
+    p.seq_lens = pages->seq_lens;
+    p.page_begin = page_begin;
+    p.batch = pages->batch;
+    p.num_kv_heads = cache->num_kv_heads;
+    p.max_pages = pages->max_pages;
+    p.num_blocks = cache->num_blocks;
+    p.page_size = cache->page_size;
+    p.head_dim = cache->head_dim;
+    p.rank = out->rank;
+    p.mu = out->mu;
+    p.basis = out->basis;
+    p.coef = out->coef;
+    p.out_dtype = out->dtype;
+    const hipError_t e = locks::launch_sketch(p, shared_basis, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
 locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
                                    const int32_t* page_begin, const locks_summaries* out,
                                    void* ws, size_t ws_bytes, void* stream) {
@@ -502,6 +537,6 @@ const char* locks_status_string(int32_t status) {
 
 int32_t locks_last_hip_error(void) { return g_last_hip_error; }
 
-int32_t locks_version(void) { return 105; }
+int32_t locks_version(void) { return 106; }
 
 }  // extern "C"

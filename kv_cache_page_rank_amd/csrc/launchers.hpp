@@ -97,6 +97,12 @@ struct BuildParams {
 hipError_t launch_build(const BuildParams& p, hipStream_t s);
 bool build_supported(int page_size, int head_dim, int rank);
 
+// Shared-basis sketch (ablation baseline): the centroid of every full page
+// and its tokens' coordinates in one basis per KV head, written as fp32
+// summaries with that basis copied to every block.  Uses BuildParams (mu,
+// basis, coef: fp32 outputs) and shared_basis [Hkv][rank][D].
+hipError_t launch_sketch(const BuildParams& p, const float* shared_basis, hipStream_t s);
+
 // fp32 summaries -> int8 / int4 codes and scales, every unit of the pools.
 struct QuantParams {
     const float* mu;       // [units][D]

@@ -39,7 +39,7 @@ def test_header_symbols_exported(lk):
 
 def test_version_and_status_strings(lk):
     lib = lk.lib()
-    assert lib.locks_version() == 105
+    assert lib.locks_version() == 106
     assert lib.locks_status_string(0) == b"ok"
     assert b"workspace" in lib.locks_status_string(3)
     assert lib.locks_status_string(99) == b"unknown status"
@@ -140,6 +140,12 @@ def test_host_validation_rejects_without_launch(lk):
     _, sm_q4, _, _ = _fake(lk, sdtype=lk.LOCKS_Q8Q4, r=4)
     assert lib.locks_quantize_summaries(by(sm), by(sm_q4), None) == lk.LOCKS_ERR_INVALID_ARG
     assert lib.locks_quantize_summaries(None, by(sm_q), None) == lk.LOCKS_ERR_INVALID_ARG
+    # sketch: needs the shared basis and fp32 output
+    assert lib.locks_build_sketch_summaries(by(kv), by(pt), None, None, by(sm), None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    _, sm_bf, _, _ = _fake(lk, sdtype=lk.LOCKS_BF16)
+    assert lib.locks_build_sketch_summaries(by(kv), by(pt), None, p, by(sm_bf), None) == \
+        lk.LOCKS_ERR_INVALID_ARG
     # sparse attend with pages requested but no list
     assert lib.locks_sparse_attend(p, 32, by(kv), by(pt), None, 4, p, None, p, 1 << 30, None) == \
         lk.LOCKS_ERR_INVALID_ARG
