@@ -317,19 +317,33 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
     const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
 
-    for (int pi = 0; pi < sp.count; ++pi) {
-        int j = sp.first + pi;
-        if constexpr (kSparse) {
-            j = sparse_slot_page(a, b, g, j, full, n_all);
-            if (j < 0) continue;
+    // The run's page indices and blocks are resolved up front, one lane per
+    // page (64 at a time), so each page's K/V loads issue without waiting for
+    // its list and block-table entries.
+    for (int base = 0; base < sp.count; base += kWave) {
+        const int n = sp.count - base < kWave ? sp.count - base : kWave;
+        int jl = -1, pl = -1;
+        if (lane < n) {
+            int j = sp.first + base + lane;
+            if constexpr (kSparse) j = sparse_slot_page(a, b, g, j, full, n_all);
+            if (j >= 0) {
+                const int ph = bt[j];
+                if (ph >= 0 && ph < a.num_blocks) {
+                    jl = j;
+                    pl = ph;
+                }
+            }
         }
-        const int phys = bt[j];
-        if (phys < 0 || phys >= a.num_blocks) continue;
-        const int nv = seq - j * P < P ? seq - j * P : P;  // valid tokens of this page
-        PageFrag<P, D> f;
-        load_page<P, D>(kpool + ((size_t)phys * Hkv + g) * P * D,
-                        vpool + ((size_t)phys * Hkv + g) * D * P, w, c, f);
-        attend_page<P, D>(f, nv, w, qhi, qlo, m_run, l_run, acc);
+        for (int pi = 0; pi < n; ++pi) {
+            const int j = __builtin_amdgcn_readlane(jl, pi);
+            const int phys = __builtin_amdgcn_readlane(pl, pi);
+            if (j < 0) continue;
+            const int nv = seq - j * P < P ? seq - j * P : P;  // valid tokens of this page
+            PageFrag<P, D> f;
+            load_page<P, D>(kpool + ((size_t)phys * Hkv + g) * P * D,
+                            vpool + ((size_t)phys * Hkv + g) * D * P, w, c, f);
+            attend_page<P, D>(f, nv, w, qhi, qlo, m_run, l_run, acc);
+        }
     }
     finish_waves<D>(a, sm_m, sm_l, sm_o, m_run, l_run, acc, wv, w, c, b, g, G, part, NPART);
 }
