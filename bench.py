@@ -132,6 +132,19 @@ def time_events(fn, iters, torch):
     return statistics.mean(ms) * 1e3, statistics.median(ms) * 1e3, ms
 
 
+def time_batch(fn, iters, torch):
+    """Average device time per call over `iters` back-to-back calls between
+    two events on the current stream (no event between calls; the figure
+    includes the dispatch gap between consecutive kernels)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / iters
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -225,11 +238,16 @@ def main():
     pms = [torch.empty((B, Hkv, MP), device="cuda") for _ in range(L)]
     for i in range(args.warmup):
         lk.locks_scan(q, summs[i % L], pages, pms[i % L])
-    scan_mean, scan_med, _ = time_events(
+    scan_ev_mean, scan_med, _ = time_events(
         lambda i: lk.locks_scan(q, summs[i % L], pages, pms[i % L]), args.steps, torch)
+    # the roofline's launch duration: back-to-back launches between two
+    # events (per-launch event pairs add their own ~1-2 us to every launch)
+    scan_mean = time_batch(lambda i: lk.locks_scan(q, summs[i % L], pages, pms[i % L]),
+                           args.steps, torch)
     scan_b = traffic.scan_bytes(B, Hq, Hkv, MP, full_total, d, P, r)
     scan_gbs = scan_b / (scan_mean * 1e-6) / 1e9
-    log(f"scan: {scan_mean:.2f} us mean ({scan_med:.2f} median), {scan_gbs:.0f} GB/s")
+    log(f"scan: {scan_mean:.2f} us per launch back to back ({scan_ev_mean:.2f} mean, "
+        f"{scan_med:.2f} median with an event pair per launch), {scan_gbs:.0f} GB/s")
 
     # --- select alone and sparse attention alone
     sel_ws = lk.workspace(lk.workspace_bytes(lk.OP_SELECT, B, MP, Hq, Hkv, P, d, r, k))
@@ -266,8 +284,8 @@ def main():
         step_us = e0.elapsed_time(e1) * 1e3 / args.steps
         for i in range(max(args.warmup, n)):
             lk.locks_scan(q, copies[i % n], pages, pms[i % L])
-        scan_us, _, _ = time_events(
-            lambda i: lk.locks_scan(q, copies[i % n], pages, pms[i % L]), args.steps, torch)
+        scan_us = time_batch(lambda i: lk.locks_scan(q, copies[i % n], pages, pms[i % L]),
+                             args.steps, torch)
         gbs = scan_b / (scan_us * 1e-6) / 1e9
         for g_ in graphs:
             g_.close()
@@ -345,7 +363,8 @@ def main():
                      "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
                      "traffic": counted_traffic(SCAN_COUNTERS, SCAN_SOURCES, spec.name),
-                     "bytes_per_launch": scan_b, "avg_launch_us": round(scan_mean, 3)},
+                     "bytes_per_launch": scan_b, "avg_launch_us": round(scan_mean, 3),
+                     "avg_launch_us_event_pairs": round(scan_ev_mean, 3)},
         "cpu_baseline": cpu,
         "breakdown": {
             "scan_us": round(scan_mean, 3),
