@@ -16,8 +16,11 @@ namespace {
 
 constexpr int kShareThreads = 256;
 
-// Z for one (b, h): every thread keeps a running (max, sum) over its strided
-// pages (log2 units), then the block combines them.
+// Z for one (b, h).  Per chunk of 64 x 256 pages every thread issues its 64
+// strided loads at once, takes their maximum, then sums 2^(x - max) (one
+// exp2 per page); chunks and then waves are combined as (max, sum) pairs
+// (log2 units).
+constexpr int kShareVals = 64;  // pages per thread and chunk
 __global__ __launch_bounds__(kShareThreads) void head_total_kernel(const ShareParams a) {
     __shared__ float sm_m[kShareThreads / kWave], sm_s[kShareThreads / kWave];
     const int bh = blockIdx.x;
@@ -27,11 +30,23 @@ __global__ __launch_bounds__(kShareThreads) void head_total_kernel(const SharePa
     full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
     const float* row = a.head_logmass + (size_t)bh * a.max_pages;
     float m = -INFINITY, sum = 0.f;
-    for (int j = t; j < full; j += kShareThreads) {
-        const float x = row[j] * kLog2e;
-        const float mn = fmaxf(m, x);
-        if (mn != -INFINITY) {
-            sum = sum * fast_exp2(m - mn) + fast_exp2(x - mn);
+    for (int base = 0; base < full; base += kShareThreads * kShareVals) {
+        float x[kShareVals];
+#pragma unroll
+        for (int e = 0; e < kShareVals; ++e) {
+            const int j = base + t + kShareThreads * e;
+            const float v = row[j < full ? j : 0];  // in-bounds address either way
+            x[e] = j < full ? v * kLog2e : -INFINITY;
+        }
+        float cm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kShareVals; ++e) cm = fmaxf(cm, x[e]);
+        if (cm != -INFINITY) {
+            float cs = 0.f;
+#pragma unroll
+            for (int e = 0; e < kShareVals; ++e) cs += fast_exp2(x[e] - cm);
+            const float mn = fmaxf(m, cm);
+            sum = (m == -INFINITY ? 0.f : sum * fast_exp2(m - mn)) + cs * fast_exp2(cm - mn);
             m = mn;
         }
     }
