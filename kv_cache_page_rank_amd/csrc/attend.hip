@@ -133,14 +133,35 @@ __device__ __forceinline__ void load_page(const uint16_t* kp, const uint16_t* vp
                 *reinterpret_cast<const u32x4*>(vp + (size_t)(16 * md + c) * P + 32 * ks2 + 8 * w);
 }
 
-// Online-softmax update of one wave's (m, l, O^T) with one page of nv valid
-// tokens (scores in log2 units).
+// K and V of a page: loaded separately so a wave can fetch the next page's
+// keys while it still uses this page's values.
 template <int P, int D>
-__device__ __forceinline__ void attend_page(const PageFrag<P, D>& f, int nv, int w,
-                                            const bf16x8* qhi, const bf16x8* qlo, float& m_run,
-                                            float& l_run, f32x4* acc) {
+__device__ __forceinline__ void load_page_k(const uint16_t* kp, int w, int c, PageFrag<P, D>& f) {
     using F = PageFrag<P, D>;
-    f32x4 sc[F::MT];
+#pragma unroll
+    for (int mt = 0; mt < F::MT; ++mt) {
+        const int tok = 32 * (mt >> 1) + 8 * (c >> 2) + 4 * (mt & 1) + (c & 3);
+#pragma unroll
+        for (int ks = 0; ks < F::KS; ++ks)
+            f.k[mt][ks] = *reinterpret_cast<const u32x4*>(kp + (size_t)tok * D + 32 * ks + 8 * w);
+    }
+}
+template <int P, int D>
+__device__ __forceinline__ void load_page_v(const uint16_t* vp, int w, int c, PageFrag<P, D>& f) {
+    using F = PageFrag<P, D>;
+#pragma unroll
+    for (int ks2 = 0; ks2 < F::KS2; ++ks2)
+#pragma unroll
+        for (int md = 0; md < F::MD; ++md)
+            f.v[ks2][md] =
+                *reinterpret_cast<const u32x4*>(vp + (size_t)(16 * md + c) * P + 32 * ks2 + 8 * w);
+}
+
+// Scores of one page (log2 units), tokens past nv set to -inf.
+template <int P, int D>
+__device__ __forceinline__ void page_scores(const PageFrag<P, D>& f, int nv, int w,
+                                            const bf16x8* qhi, const bf16x8* qlo, f32x4* sc) {
+    using F = PageFrag<P, D>;
 #pragma unroll
     for (int mt = 0; mt < F::MT; ++mt) {
         sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -161,6 +182,14 @@ __device__ __forceinline__ void attend_page(const PageFrag<P, D>& f, int nv, int
                 sc[mt][v] = tok < nv ? sc[mt][v] : -INFINITY;
             }
     }
+}
+
+// Online-softmax update of one wave's (m, l, O^T) with the scores of a page
+// and its values.
+template <int P, int D>
+__device__ __forceinline__ void page_values(const PageFrag<P, D>& f, f32x4* sc, int nv, int w,
+                                            float& m_run, float& l_run, f32x4* acc) {
+    using F = PageFrag<P, D>;
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < F::MT; ++mt)
@@ -213,6 +242,17 @@ __device__ __forceinline__ void attend_page(const PageFrag<P, D>& f, int nv, int
             acc[md] = mfma_16x16x32_bf16(vf, blo, acc[md]);
         }
     }
+}
+
+// Online-softmax update of one wave's (m, l, O^T) with one page of nv valid
+// tokens (scores in log2 units).
+template <int P, int D>
+__device__ __forceinline__ void attend_page(const PageFrag<P, D>& f, int nv, int w,
+                                            const bf16x8* qhi, const bf16x8* qlo, float& m_run,
+                                            float& l_run, f32x4* acc) {
+    f32x4 sc[PageFrag<P, D>::MT];
+    page_scores<P, D>(f, nv, w, qhi, qlo, sc);
+    page_values<P, D>(f, sc, nv, w, m_run, l_run, acc);
 }
 
 // q fragment of head hq in log2 units, split into bf16 hi + lo:
@@ -334,15 +374,32 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
                 }
             }
         }
-        for (int pi = 0; pi < n; ++pi) {
-            const int j = __builtin_amdgcn_readlane(jl, pi);
-            const int phys = __builtin_amdgcn_readlane(pl, pi);
-            if (j < 0) continue;
+        // valid pages in run order; the next page's keys load while this
+        // page's values are used, and its values while its own keys are
+        uint64_t todo = __ballot(lane < n && jl >= 0);
+        if (todo == 0) continue;
+        int cur = __builtin_ffsll((long long)todo) - 1;
+        todo &= todo - 1;
+        int j = __builtin_amdgcn_readlane(jl, cur);
+        int phys = __builtin_amdgcn_readlane(pl, cur);
+        PageFrag<P, D> f;
+        load_page_k<P, D>(kpool + ((size_t)phys * Hkv + g) * P * D, w, c, f);
+        load_page_v<P, D>(vpool + ((size_t)phys * Hkv + g) * D * P, w, c, f);
+        while (true) {
             const int nv = seq - j * P < P ? seq - j * P : P;  // valid tokens of this page
-            PageFrag<P, D> f;
-            load_page<P, D>(kpool + ((size_t)phys * Hkv + g) * P * D,
-                            vpool + ((size_t)phys * Hkv + g) * D * P, w, c, f);
-            attend_page<P, D>(f, nv, w, qhi, qlo, m_run, l_run, acc);
+            const bool more = todo != 0;
+            const int nxt = more ? __builtin_ffsll((long long)todo) - 1 : 0;
+            const int jn = __builtin_amdgcn_readlane(jl, nxt);
+            const int pn = __builtin_amdgcn_readlane(pl, nxt);
+            f32x4 sc[PageFrag<P, D>::MT];
+            page_scores<P, D>(f, nv, w, qhi, qlo, sc);
+            if (more) load_page_k<P, D>(kpool + ((size_t)pn * Hkv + g) * P * D, w, c, f);
+            page_values<P, D>(f, sc, nv, w, m_run, l_run, acc);
+            if (!more) break;
+            load_page_v<P, D>(vpool + ((size_t)pn * Hkv + g) * D * P, w, c, f);
+            todo &= todo - 1;
+            j = jn;
+            phys = pn;
         }
     }
     finish_waves<D>(a, sm_m, sm_l, sm_o, m_run, l_run, acc, wv, w, c, b, g, G, part, NPART);
