@@ -206,6 +206,16 @@ def main():
     torch.cuda.synchronize()
     log(f"built {full_total * Hkv} page summaries in {build_ms:.2f} ms (x{L} layers)")
 
+    # --- page-crossing refresh: the last full page of every sequence (what a
+    # decode step that completes a page rebuilds), B x H_kv units
+    last = torch.tensor([max(n // P - 1, 0) for n in spec.seq_lens], dtype=torch.int32,
+                        device="cuda")
+    for _ in range(2):
+        lk.locks_refresh_summaries(kvs[0], pages, last, 1, summs[0])
+    refresh_us = time_batch(lambda i: lk.locks_refresh_summaries(kvs[0], pages, last, 1, summs[0]),
+                            5, torch)
+    log(f"one-page refresh ({B * Hkv} units): {refresh_us:.1f} us")
+
     # --- one step graph per layer copy
     ws_step = lk.workspace_bytes(lk.OP_STEP, B, MP, Hq, Hkv, P, d, r, k)
     bufs = []
@@ -381,6 +391,7 @@ def main():
             "summary_to_cache_ratio": round(ratio, 4),
             "build_ms": round(build_ms, 3),
             "build_pages_per_s": round(full_total * Hkv / (build_ms * 1e-3), 1),
+            "refresh_one_page_us": round(refresh_us, 1),
             "bf16_summaries": bf16_summ,
             "q8q4_summaries": q8q4_summ,
             "mean_share_step_us": round(share_step, 3),
