@@ -18,8 +18,8 @@
 //     index between rounds, so each thread owns one 2x2 block with read and
 //     write slots fixed for the whole kernel (a round is a few loads, eight
 //     multiply-adds and four stores); only the upper triangle is kept.  U's
-//     columns move the same way; its updates trail by a round and overlap
-//     the next round's rotation latency.  U's buffers take Kc's place
+//     columns move the same way; its updates trail by a round and run on
+//     every other wave while wave 0 computes the next round's rotations.  U's buffers take Kc's place
 //     during the sweeps, and Kc is read again afterwards.
 //  4. Eigenvalues (diag A) ranked descending, ties by index; for the top r:
 //     basis_k = Kc^T u / sqrt(lambda), re-orthonormalised by modified
@@ -114,10 +114,12 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
     constexpr int NOFF = NPAIR * (NPAIR - 1) / 2;           // off-diagonal 2x2 blocks
     constexpr int NOFFW = build_off_waves<P>();             // their waves
     constexpr int UW0 = NOFFW + 1;                          // first U wave
-    constexpr int NUT = kWave * build_u_waves<P>();         // U threads
-    constexpr int UROWS = P * NPAIR / NUT;                  // rows per U thread
+    // U's updates run in the rotation phase, when every wave but wave 0 is
+    // otherwise idle: all of them share the rows (2-3 per thread at P = 64)
+    constexpr int NUT = NT - kWave;                         // threads rotating U
     constexpr int USTEP = NUT / NPAIR;                      // row stride of a U thread
-    static_assert(NPAIR <= kWave && NUT % NPAIR == 0 && UROWS * NUT == P * NPAIR, "wave roles");
+    constexpr int UROWS = (P + USTEP - 1) / USTEP;          // rows per U thread, at most
+    static_assert(NPAIR <= kWave && NUT % NPAIR == 0, "wave roles");
     constexpr int KP = D + 4;   // padded row of Kc
     constexpr int S = P + 2;    // row of a position-space matrix (even: 8-byte pairs)
     constexpr int UP = P + 1;   // padded row of U
@@ -262,9 +264,9 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
     const int s0 = sigma<P>(r0), s1 = sigma<P>(r1), e0 = sigma<P>(c0), e1 = sigma<P>(c1);
     const int src0 = r0 * S + c0, src1 = r1 * S + c0;  // 8-byte row pairs (upper: r < c)
     const int d00 = at(s0, e0), d01 = at(s0, e1), d10 = at(s1, e0), d11 = at(s1, e1);
-    // U thread: column pair ui, rows urow + USTEP * m
-    const bool uthr = wave >= UW0;
-    const int ut = t - UW0 * kWave;
+    // U thread: column pair ui, rows urow + USTEP * m below P
+    const bool uthr = wave >= 1;
+    const int ut = t - kWave;
     const int ui = uthr ? ut % NPAIR : 0, urow = uthr ? ut / NPAIR : 0;
     const int usrc = urow * S + 2 * ui;
     const int ud0 = urow * S + sigma<P>(2 * ui), ud1 = urow * S + sigma<P>(2 * ui + 1);
@@ -275,9 +277,11 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
         float* nxt = ubuf + ((k + 1) & 1) * (P * S);
 #pragma unroll
         for (int m = 0; m < UROWS; ++m) {
-            const f32x2 v = *reinterpret_cast<const f32x2*>(cur + usrc + m * USTEP * S);
-            nxt[ud0 + m * USTEP * S] = rot[0] * v[0] - rot[1] * v[1];
-            nxt[ud1 + m * USTEP * S] = rot[1] * v[0] + rot[0] * v[1];
+            if (urow + m * USTEP < P) {
+                const f32x2 v = *reinterpret_cast<const f32x2*>(cur + usrc + m * USTEP * S);
+                nxt[ud0 + m * USTEP * S] = rot[0] * v[0] - rot[1] * v[1];
+                nxt[ud1 + m * USTEP * S] = rot[1] * v[0] + rot[0] * v[1];
+            }
         }
     };
     __syncthreads();
