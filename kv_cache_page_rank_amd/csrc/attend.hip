@@ -114,47 +114,48 @@ struct PageFrag {
     u32x4 v[KS2][MD];
 };
 
+// Buffer descriptor of one page of `bytes` bytes at `base`; with `present`
+// false it holds no records, so every load through it fetches nothing and
+// returns zeros.  Loads through such descriptors can be issued
+// unconditionally, which keeps the compiler's wait counts exact: after a
+// branch that issues loads on one side only, its waits must hold for both
+// sides and so also wait for loads that are not needed yet.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, bool present,
+                                                            int bytes) {
+    constexpr int kRawWord3 = 0x00020000;  // gfx9 family: 32-bit data format, raw access
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, present ? bytes : 0,
+                                             kRawWord3);
+}
+// Keys of a page for one wave: score tile mt, A row m <-> token
+// 32(mt/2) + 8(m/4) + 4(mt%2) + m%4; 16 bytes of d per load (byte offsets
+// within the page).
 template <int P, int D>
-__device__ __forceinline__ void load_page(const uint16_t* kp, const uint16_t* vp, int w, int c,
-                                          PageFrag<P, D>& f) {
+__device__ __forceinline__ void load_page_k_rsrc(__amdgpu_buffer_rsrc_t rs, int w, int c,
+                                                 PageFrag<P, D>& f) {
     using F = PageFrag<P, D>;
 #pragma unroll
     for (int mt = 0; mt < F::MT; ++mt) {
         const int tok = 32 * (mt >> 1) + 8 * (c >> 2) + 4 * (mt & 1) + (c & 3);
 #pragma unroll
         for (int ks = 0; ks < F::KS; ++ks)
-            f.k[mt][ks] = *reinterpret_cast<const u32x4*>(kp + (size_t)tok * D + 32 * ks + 8 * w);
+            f.k[mt][ks] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 2 * (tok * D + 32 * ks + 8 * w), 0, 0));
     }
-#pragma unroll
-    for (int ks2 = 0; ks2 < F::KS2; ++ks2)
-#pragma unroll
-        for (int md = 0; md < F::MD; ++md)
-            f.v[ks2][md] =
-                *reinterpret_cast<const u32x4*>(vp + (size_t)(16 * md + c) * P + 32 * ks2 + 8 * w);
 }
 
-// K and V of a page: loaded separately so a wave can fetch the next page's
-// keys while it still uses this page's values.
+// Values of a page (stored [d][P]) for one wave: 8 consecutive tokens of one
+// V^T row per 16-byte load.
 template <int P, int D>
-__device__ __forceinline__ void load_page_k(const uint16_t* kp, int w, int c, PageFrag<P, D>& f) {
-    using F = PageFrag<P, D>;
-#pragma unroll
-    for (int mt = 0; mt < F::MT; ++mt) {
-        const int tok = 32 * (mt >> 1) + 8 * (c >> 2) + 4 * (mt & 1) + (c & 3);
-#pragma unroll
-        for (int ks = 0; ks < F::KS; ++ks)
-            f.k[mt][ks] = *reinterpret_cast<const u32x4*>(kp + (size_t)tok * D + 32 * ks + 8 * w);
-    }
-}
-template <int P, int D>
-__device__ __forceinline__ void load_page_v(const uint16_t* vp, int w, int c, PageFrag<P, D>& f) {
+__device__ __forceinline__ void load_page_v_rsrc(__amdgpu_buffer_rsrc_t rs, int w, int c,
+                                                 PageFrag<P, D>& f) {
     using F = PageFrag<P, D>;
 #pragma unroll
     for (int ks2 = 0; ks2 < F::KS2; ++ks2)
 #pragma unroll
         for (int md = 0; md < F::MD; ++md)
-            f.v[ks2][md] =
-                *reinterpret_cast<const u32x4*>(vp + (size_t)(16 * md + c) * P + 32 * ks2 + 8 * w);
+            f.v[ks2][md] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rs, 2 * ((16 * md + c) * P + 32 * ks2 + 8 * w), 0, 0));
 }
 
 // Scores of one page (log2 units), tokens past nv set to -inf.
@@ -242,17 +243,6 @@ __device__ __forceinline__ void page_values(const PageFrag<P, D>& f, f32x4* sc, 
             acc[md] = mfma_16x16x32_bf16(vf, blo, acc[md]);
         }
     }
-}
-
-// Online-softmax update of one wave's (m, l, O^T) with one page of nv valid
-// tokens (scores in log2 units).
-template <int P, int D>
-__device__ __forceinline__ void attend_page(const PageFrag<P, D>& f, int nv, int w,
-                                            const bf16x8* qhi, const bf16x8* qlo, float& m_run,
-                                            float& l_run, f32x4* acc) {
-    f32x4 sc[PageFrag<P, D>::MT];
-    page_scores<P, D>(f, nv, w, qhi, qlo, sc);
-    page_values<P, D>(f, sc, nv, w, m_run, l_run, acc);
 }
 
 // q fragment of head hq in log2 units, split into bf16 hi + lo:
@@ -374,32 +364,47 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
                 }
             }
         }
-        // valid pages in run order; the next page's keys load while this
-        // page's values are used, and its values while its own keys are
+        // valid pages in run order (lanes of `todo`, lowest first)
         uint64_t todo = __ballot(lane < n && jl >= 0);
         if (todo == 0) continue;
-        int cur = __builtin_ffsll((long long)todo) - 1;
-        todo &= todo - 1;
-        int j = __builtin_amdgcn_readlane(jl, cur);
-        int phys = __builtin_amdgcn_readlane(pl, cur);
+        // page descriptors: K and V of block ph (no records when absent)
+        auto kpage = [&](int ph, bool present) {
+            return page_rsrc(kpool + (present ? ((size_t)ph * Hkv + g) * P * D : 0), present,
+                             2 * P * D);
+        };
+        auto vpage = [&](int ph, bool present) {
+            return page_rsrc(vpool + (present ? ((size_t)ph * Hkv + g) * D * P : 0), present,
+                             2 * P * D);
+        };
+        // next page of the run: its index and block; false when none is left
+        auto take = [&](int& jj, int& ph) -> bool {
+            const bool has = todo != 0;
+            const int ln = has ? __builtin_ffsll((long long)todo) - 1 : 0;
+            jj = __builtin_amdgcn_readlane(jl, ln);
+            ph = __builtin_amdgcn_readlane(pl, ln);
+            todo &= todo - 1;
+            return has;
+        };
+        // One page buffer: the next page's keys load while this page's
+        // values are used, and its values while its own keys are.  Loads for
+        // a page past the end are issued too (they fetch nothing): no load
+        // sits under a branch, so each wait covers only the loads it needs.
         PageFrag<P, D> f;
-        load_page_k<P, D>(kpool + ((size_t)phys * Hkv + g) * P * D, w, c, f);
-        load_page_v<P, D>(vpool + ((size_t)phys * Hkv + g) * D * P, w, c, f);
+        int j, ph;
+        take(j, ph);
+        load_page_k_rsrc<P, D>(kpage(ph, true), w, c, f);
+        load_page_v_rsrc<P, D>(vpage(ph, true), w, c, f);
         while (true) {
-            const int nv = seq - j * P < P ? seq - j * P : P;  // valid tokens of this page
-            const bool more = todo != 0;
-            const int nxt = more ? __builtin_ffsll((long long)todo) - 1 : 0;
-            const int jn = __builtin_amdgcn_readlane(jl, nxt);
-            const int pn = __builtin_amdgcn_readlane(pl, nxt);
+            const int nv = seq - j * P < P ? seq - j * P : P;  // valid tokens of the page
+            int jn, pn;
+            const bool more = take(jn, pn);
             f32x4 sc[PageFrag<P, D>::MT];
             page_scores<P, D>(f, nv, w, qhi, qlo, sc);
-            if (more) load_page_k<P, D>(kpool + ((size_t)pn * Hkv + g) * P * D, w, c, f);
+            load_page_k_rsrc<P, D>(kpage(pn, more), w, c, f);
             page_values<P, D>(f, sc, nv, w, m_run, l_run, acc);
+            load_page_v_rsrc<P, D>(vpage(pn, more), w, c, f);
             if (!more) break;
-            load_page_v<P, D>(vpool + ((size_t)pn * Hkv + g) * D * P, w, c, f);
-            todo &= todo - 1;
             j = jn;
-            phys = pn;
         }
     }
     finish_waves<D>(a, sm_m, sm_l, sm_o, m_run, l_run, acc, wv, w, c, b, g, G, part, NPART);
