@@ -434,10 +434,11 @@ locks_status locks_sparse_attend(const float* q, int32_t num_q_heads, const lock
                                  int32_t k_pages, void* out, float* out_lse, void* ws,
                                  size_t ws_bytes, void* stream) {
     if (k_pages > 0 && !sel_pages) return LOCKS_ERR_INVALID_ARG;
-    // With k_pages == 0 the sparse path still attends the partial last page; a
-    // non-null marker selects that path and is never dereferenced.
-    static const int32_t kNoPages = -1;
-    const int32_t* sel = sel_pages ? sel_pages : &kNoPages;
+    // With k_pages == 0 the sparse path still attends the partial last page;
+    // a non-null marker selects that path.  The marker is a device array (the
+    // sequence lengths) because the kernels read a list entry before they
+    // know whether they use it; with k_pages == 0 they never use it.
+    const int32_t* sel = k_pages > 0 ? sel_pages : pages->seq_lens;
     return attend_common(q, num_q_heads, cache, pages, sel, k_pages, out, out_lse, ws, ws_bytes,
                          static_cast<hipStream_t>(stream));
 }

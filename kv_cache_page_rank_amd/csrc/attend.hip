@@ -245,17 +245,26 @@ __device__ __forceinline__ void page_values(const PageFrag<P, D>& f, f32x4* sc, 
     }
 }
 
-// q fragment of head hq in log2 units, split into bf16 hi + lo:
-// q[hq][32ks + 8w + e] (zero for padding heads).
+// q fragment of head hq: the raw loads (q[hq][32ks + 8w + e], every chunk's
+// loads in flight together) and their split into bf16 hi + lo in log2 units
+// (zero for padding heads).
 template <int D>
-__device__ __forceinline__ void load_q_split(const AttnParams& a, int b, int hq, bool head_ok,
-                                             int w, bf16x8* qhi, bf16x8* qlo) {
-    const float qscale = kLog2e / sqrtf((float)D);
+__device__ __forceinline__ void load_q_raw(const AttnParams& a, int b, int hq, int w, f32x4* xa,
+                                           f32x4* xb) {
     const float* qp = a.q + ((size_t)b * a.num_q_heads + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
+        xa[ks] = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w);
+        xb[ks] = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
+    }
+}
+template <int D>
+__device__ __forceinline__ void split_q(const f32x4* xa, const f32x4* xb, bool head_ok,
+                                       bf16x8* qhi, bf16x8* qlo) {
+    const float qscale = kLog2e / sqrtf((float)D);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        const f32x4 x0 = xa[ks], x1 = xb[ks];
         u32x4 hi, lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -317,7 +326,17 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     const bool head_ok = c < G;
     const int hq = g * G + (head_ok ? c : 0);
 
-    const int seq = a.seq_lens[b] < 0 ? 0 : a.seq_lens[b];
+    const int seq_raw = a.seq_lens[b];
+    // sparse: this lane's list entry (slot s * pages_per_split + lane; a run
+    // has at most 16 slots), read together with the sequence length; the
+    // list is a readable device array even when k_sel = 0
+    int j_list0 = 0;
+    if constexpr (kSparse) {
+        const int slot = s * a.pages_per_split + lane;
+        j_list0 = a.sel_pages[((size_t)b * Hkv + g) * a.k_sel + (slot < a.k_sel ? slot : 0)];
+        asm volatile("" ::"s"(seq_raw), "v"(j_list0));
+    }
+    const int seq = seq_raw < 0 ? 0 : seq_raw;
     int full = seq / P, n_all = (seq + P - 1) / P;
     full = full > a.max_pages ? a.max_pages : full;
     n_all = n_all > a.max_pages ? a.max_pages : n_all;
@@ -336,8 +355,6 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     }
 
     bf16x8 qhi[KS], qlo[KS];
-    load_q_split<D>(a, b, hq, head_ok, w, qhi, qlo);
-
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[MD];
 #pragma unroll
@@ -347,36 +364,36 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
     const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
 
-    // The run's page indices and blocks are resolved up front, one lane per
-    // page (64 at a time), so each page's K/V loads issue without waiting for
-    // its list and block-table entries.
-    for (int base = 0; base < sp.count; base += kWave) {
-        const int n = sp.count - base < kWave ? sp.count - base : kWave;
-        int jl = -1, pl = -1;
-        if (lane < n) {
-            int j = sp.first + base + lane;
-            if constexpr (kSparse) j = sparse_slot_page(a, b, g, j, full, n_all);
-            if (j >= 0) {
-                const int ph = bt[j];
-                if (ph >= 0 && ph < a.num_blocks) {
-                    jl = j;
-                    pl = ph;
-                }
+    // page descriptors: K and V of block ph (no records when absent)
+    auto kpage = [&](int ph, bool present) {
+        return page_rsrc(kpool + (present ? ((size_t)ph * Hkv + g) * P * D : 0), present,
+                         2 * P * D);
+    };
+    auto vpage = [&](int ph, bool present) {
+        return page_rsrc(vpool + (present ? ((size_t)ph * Hkv + g) * D * P : 0), present,
+                         2 * P * D);
+    };
+    // Dense: page idx of the run and its block; -1 / -1 when the lane holds
+    // no valid page.
+    auto resolve = [&](int idx, int& jl, int& pl) {
+        jl = -1;
+        pl = -1;
+        const int j = idx;
+        if (j >= 0) {
+            const int ph = bt[j];
+            if (ph >= 0 && ph < a.num_blocks) {
+                jl = j;
+                pl = ph;
             }
         }
-        // valid pages in run order (lanes of `todo`, lowest first)
-        uint64_t todo = __ballot(lane < n && jl >= 0);
-        if (todo == 0) continue;
-        // page descriptors: K and V of block ph (no records when absent)
-        auto kpage = [&](int ph, bool present) {
-            return page_rsrc(kpool + (present ? ((size_t)ph * Hkv + g) * P * D : 0), present,
-                             2 * P * D);
-        };
-        auto vpage = [&](int ph, bool present) {
-            return page_rsrc(vpool + (present ? ((size_t)ph * Hkv + g) * D * P : 0), present,
-                             2 * P * D);
-        };
-        // next page of the run: its index and block; false when none is left
+    };
+    // Walks the valid pages (lanes of `todo`, lowest first) with one page
+    // buffer: the next page's keys load while this page's values are used,
+    // and its values while its own keys are.  Loads for a page past the end
+    // are issued too (they fetch nothing): no load sits under a branch, so
+    // each wait covers only the loads it needs.  `ready` runs once the
+    // first page's loads are issued.
+    auto walk = [&](uint64_t todo, int jl, int pl, auto&& ready) {
         auto take = [&](int& jj, int& ph) -> bool {
             const bool has = todo != 0;
             const int ln = has ? __builtin_ffsll((long long)todo) - 1 : 0;
@@ -385,15 +402,12 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
             todo &= todo - 1;
             return has;
         };
-        // One page buffer: the next page's keys load while this page's
-        // values are used, and its values while its own keys are.  Loads for
-        // a page past the end are issued too (they fetch nothing): no load
-        // sits under a branch, so each wait covers only the loads it needs.
         PageFrag<P, D> f;
         int j, ph;
         take(j, ph);
         load_page_k_rsrc<P, D>(kpage(ph, true), w, c, f);
         load_page_v_rsrc<P, D>(vpage(ph, true), w, c, f);
+        ready();
         while (true) {
             const int nv = seq - j * P < P ? seq - j * P : P;  // valid tokens of the page
             int jn, pn;
@@ -405,6 +419,49 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
             load_page_v_rsrc<P, D>(vpage(pn, more), w, c, f);
             if (!more) break;
             j = jn;
+        }
+    };
+
+    if constexpr (kSparse) {
+        // A sparse run is one chunk (at most 16 slots).  Its block-table
+        // reads go out first, then the query's loads, then the first page's
+        // loads; the query is split only after those are issued.
+        // This lane's page (slot sp.first + lane): its list entry was read up
+        // front; the block-table read is unconditional (clamped to entry 0,
+        // the table has at least one column) and checked after the query's
+        // loads are issued.
+        const int slot = sp.first + lane;
+        int jc = -1;
+        if (slot < a.k_sel)
+            jc = (j_list0 >= 0 && j_list0 < full) ? j_list0 : -1;
+        else if (slot == a.k_sel && n_all > full)
+            jc = full;  // partial last page
+        jc = lane < sp.count ? jc : -1;
+        const int ph_raw = bt[jc >= 0 ? jc : 0];
+        f32x4 xa[KS], xb[KS];
+        load_q_raw<D>(a, b, hq, w, xa, xb);
+        // keeps the query's loads ahead of the first use of ph_raw (which
+        // waits for the block-table read)
+        asm volatile("" ::: "memory");
+        const bool ok = jc >= 0 && ph_raw >= 0 && ph_raw < a.num_blocks;
+        const int jl = ok ? jc : -1, pl = ok ? ph_raw : -1;
+        const uint64_t todo = __ballot(ok);
+        if (todo != 0) walk(todo, jl, pl, [&] { split_q<D>(xa, xb, head_ok, qhi, qlo); });
+    } else {
+        {
+            f32x4 xa[KS], xb[KS];
+            load_q_raw<D>(a, b, hq, w, xa, xb);
+            split_q<D>(xa, xb, head_ok, qhi, qlo);
+        }
+        // The run's page indices and blocks are resolved up front, one lane
+        // per page (64 at a time), so each page's K/V loads issue without
+        // waiting for its block-table entry.
+        for (int base = 0; base < sp.count; base += kWave) {
+            const int n = sp.count - base < kWave ? sp.count - base : kWave;
+            int jl = -1, pl = -1;
+            if (lane < n) resolve(sp.first + base + lane, jl, pl);
+            const uint64_t todo = __ballot(lane < n && jl >= 0);
+            if (todo != 0) walk(todo, jl, pl, [] {});
         }
     }
     finish_waves<D>(a, sm_m, sm_l, sm_o, m_run, l_run, acc, wv, w, c, b, g, G, part, NPART);
@@ -441,11 +498,26 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
     const int hq = g * G + (head_ok ? c : 0);
     const int tok0 = 16 * wv;
 
-    const int seq = a.seq_lens[b] < 0 ? 0 : a.seq_lens[b];
+    // The list entry of this split is read together with the sequence length
+    // (it does not depend on it), and the block-table entry as soon as both
+    // are in: three dependent reads become two.
+    // (sel_pages is always a readable device array: with k_sel = 0 it is a
+    // marker that is read but never used)
+    const int seq_raw = a.seq_lens[b];
+    const int j_list = a.sel_pages[((size_t)b * Hkv + g) * a.k_sel + (s < a.k_sel ? s : 0)];
+    // both values are consumed here, so both reads issue before one wait
+    // (otherwise the list read is sunk into the branch that uses it)
+    asm volatile("" ::"s"(seq_raw), "s"(j_list));
+    const int seq = seq_raw < 0 ? 0 : seq_raw;
     int full = seq / P, n_all = (seq + P - 1) / P;
     full = full > a.max_pages ? a.max_pages : full;
     n_all = n_all > a.max_pages ? a.max_pages : n_all;
-    const SplitPages sp = split_pages(a, true, b, g, s, full, n_all);
+    SplitPages sp{0, 0};
+    if (s < a.k_sel) {
+        if (j_list >= 0 && j_list < full) sp = {j_list, 1};
+    } else if (n_all > full) {
+        sp = {full, 1};  // partial last page
+    }
     int phys = sp.count ? a.block_table[(size_t)b * a.max_pages + sp.first] : -1;
     const bool page_ok = sp.count && phys >= 0 && phys < a.num_blocks;
     phys = page_ok ? phys : 0;
@@ -469,10 +541,15 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
     {
         const float qscale = kLog2e / sqrtf((float)D);
         const float* qp = a.q + ((size_t)b * a.num_q_heads + hq) * D;
+        f32x4 xa[KS], xb[KS];  // every chunk's loads first, in flight together
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
+            xa[ks] = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w);
+            xb[ks] = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const f32x4 x0 = xa[ks], x1 = xb[ks];
             u32x4 hi, lo;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
