@@ -182,7 +182,26 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
     const int wave = t >> 6;
     const int lane = t & 63;
 
-    int n = a.seq_lens[b] / a.page_size;
+    // The run maxima this thread may need (runs t, t + 1024) are read
+    // together with the sequence length, clamped to the table's runs; which
+    // of them hold full pages is decided once the length is in.
+    const int nruns_all = (a.max_pages + kRunPages - 1) / kRunPages;
+    const int seq_raw = a.seq_lens[b];
+    float rmv[kRunPer];
+#pragma unroll
+    for (int i = 0; i < kRunPer; ++i) rmv[i] = 0.f;
+    if (a.run_max) {
+        const float* rm = a.run_max + (size_t)bg * nruns_all;
+#pragma unroll
+        for (int i = 0; i < kRunPer; ++i) {
+            const int r = i * kThreads + t;
+            rmv[i] = rm[r < nruns_all ? r : nruns_all - 1];
+        }
+    }
+    // both reads issue before one wait (the run-maxima reads would otherwise
+    // be sunk below the branches on the length)
+    asm volatile("" ::"s"(seq_raw), "v"(rmv[0]), "v"(rmv[kRunPer - 1]));
+    int n = seq_raw / a.page_size;
     n = n < 0 ? 0 : (n > a.max_pages ? a.max_pages : n);
     const int k = a.k_req < n ? a.k_req : n;
     const float* row = a.page_logmass + (size_t)bg * a.max_pages;
@@ -211,16 +230,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
         bool done = false;
         if (a.run_max) {
             // ---- bound from the run maxima: thread t holds runs t, t + 1024
-            const int nruns_all = (a.max_pages + kRunPages - 1) / kRunPages;
             const int nruns = (n + kRunPages - 1) / kRunPages;  // runs holding full pages
-            const float* rm = a.run_max + (size_t)bg * nruns_all;
             uint32_t rkey[kRunPer];
             uint32_t my_max = 0;
 #pragma unroll
             for (int i = 0; i < kRunPer; ++i) {
                 const int r = i * kThreads + t;
-                const float v = rm[r < nruns ? r : nruns - 1];
-                rkey[i] = r < nruns ? orderable_bits(v) : 0u;
+                rkey[i] = r < nruns ? orderable_bits(rmv[i]) : 0u;
                 my_max = rkey[i] > my_max ? rkey[i] : my_max;
             }
             const uint32_t T = group_bound(my_max, k, s_tmax, s_gmax, &s_T);

@@ -143,3 +143,20 @@ def test_attend_deterministic():
     c = _run_dense(case)
     d = _run_dense(case)
     assert np.array_equal(c[0], d[0]) and np.array_equal(c[1], d[1])
+
+
+@pytest.mark.parametrize("mk,bf16", [(lambda: tiny(num_q_heads=4, num_kv_heads=1, seq_lens=[1000]),
+                                      False),
+                                     (lambda: bf16_small(seq_lens=[64 * 20 + 17, 64 * 9 + 63]),
+                                      True)])
+def test_zero_pages_attends_partial_page_only(mk, bf16):
+    """k_pages = 0 (a budget below one page): each sequence attends only its
+    partial last page (the list passed to the kernels is then a stand-in that
+    is read but never used)."""
+    case = Case(mk())
+    s = case.spec
+    sel = np.zeros((s.batch, s.num_kv_heads, 0), np.int32)
+    out_o, lse_o = oracle.attend_pool(case.lay, case.layer.q, case.k_f32, case.layer.v_f32(), sel)
+    say("zero selected pages")
+    out_g, lse_g = _run_sparse(case, sel)
+    _check(out_g, lse_g, out_o, lse_o, bf16)
