@@ -810,7 +810,8 @@ hipError_t launch_pd(AttnParams p, hipStream_t s) {
                                        p);
             } else if (sparse) {  // many pages: one wave per run of selected pages
                 // ~1024 waves (one per SIMD), each walking its run of pages: measured
-                // faster than more, shorter runs at two waves per SIMD
+                // faster than more, shorter runs, also with two waves resident per
+                // SIMD (256 registers, a few spills)
                 long pps = (total + 1023) / 1024;
                 pps = pps < 1 ? 1 : (pps > 16 ? 16 : pps);
                 p.pages_per_split = (int)pps;
