@@ -43,18 +43,6 @@ __device__ __forceinline__ SplitPages split_pages(const AttnParams& a, bool spar
     return r;
 }
 
-// Page of slot `slot` of the sparse list of (b, g): the selected pages
-// (slots < k_sel; -1 entries and pages that are not full are skipped), then
-// the partial last page (slot k_sel).  -1: nothing to attend.
-__device__ __forceinline__ int sparse_slot_page(const AttnParams& a, int b, int g, int slot,
-                                                int full, int n_all) {
-    if (slot < a.k_sel) {
-        const int j = a.sel_pages[((size_t)b * a.num_kv_heads + g) * a.k_sel + slot];
-        return (j >= 0 && j < full) ? j : -1;
-    }
-    return (slot == a.k_sel && n_all > full) ? full : -1;
-}
-
 // Combine the (m, l, o) partials of the 4 waves of a workgroup (4
 // consecutive splits of one (b, g)) into one partial, in wave order.
 // sm_o[w][h][d]; thread t combines head t/16, dims [8*(t%16), +8).
@@ -373,19 +361,13 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
         return page_rsrc(vpool + (present ? ((size_t)ph * Hkv + g) * D * P : 0), present,
                          2 * P * D);
     };
-    // Dense: page idx of the run and its block; -1 / -1 when the lane holds
-    // no valid page.
-    auto resolve = [&](int idx, int& jl, int& pl) {
-        jl = -1;
-        pl = -1;
-        const int j = idx;
-        if (j >= 0) {
-            const int ph = bt[j];
-            if (ph >= 0 && ph < a.num_blocks) {
-                jl = j;
-                pl = ph;
-            }
-        }
+    // Dense: page j of the run and its block; -1 / -1 when the block-table
+    // entry is out of range.
+    auto resolve = [&](int j, int& jl, int& pl) {
+        const int ph = bt[j];
+        const bool ok = ph >= 0 && ph < a.num_blocks;
+        jl = ok ? j : -1;
+        pl = ok ? ph : -1;
     };
     // Walks the valid pages (lanes of `todo`, lowest first) with one page
     // buffer: the next page's keys load while this page's values are used,
@@ -423,13 +405,12 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     };
 
     if constexpr (kSparse) {
-        // A sparse run is one chunk (at most 16 slots).  Its block-table
-        // reads go out first, then the query's loads, then the first page's
-        // loads; the query is split only after those are issued.
-        // This lane's page (slot sp.first + lane): its list entry was read up
-        // front; the block-table read is unconditional (clamped to entry 0,
-        // the table has at least one column) and checked after the query's
-        // loads are issued.
+        // A sparse run is one chunk (at most 16 slots).  Lane l's page is
+        // slot sp.first + l, whose list entry was read up front.  Its
+        // block-table read is unconditional (clamped to entry 0: the table
+        // has at least one column) and goes out before the query's loads;
+        // the page is checked once those are issued, and the query is split
+        // only after the first page's loads are out.
         const int slot = sp.first + lane;
         int jc = -1;
         if (slot < a.k_sel)
