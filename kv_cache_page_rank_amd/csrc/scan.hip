@@ -43,7 +43,8 @@ struct WaveCtx {
     bool head_ok;
     int my_phys;  // block of page j0 + c (-1: absent)
     float* out_page;
-    float qf[D / 4];
+    float qf[D / 4];  // query words as loaded (head c, or head 0 for padding heads)
+    float qs;         // scale to log2 units, 0 for padding heads
 };
 
 // Summary element types: fp32, bf16 bit patterns (uint16_t), or int8 / int4
@@ -135,6 +136,24 @@ __device__ __forceinline__ void page_mass(const ScanParams& a, const WaveCtx<D>&
     }
 }
 
+// The query words, passed through empty asm statements that clobber memory:
+// they stay after every load issued before them, and the query's arithmetic
+// stays after them, so a wave's first summary loads go out before it waits
+// for its query.
+template <int N>
+__device__ __forceinline__ void query_after_loads(const float* qf, float* qv) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        qv[i] = qf[i];
+        asm volatile("" : "+v"(qv[i])::"memory");
+    }
+}
+// The same for loaded summary words that are used before the first tile.
+template <typename T>
+__device__ __forceinline__ void after_loads(T& v) {
+    asm volatile("" : "+v"(v)::"memory");
+}
+
 // x = hi + lo + e with hi = bf16(x), lo = bf16(x - hi), both rounded to
 // nearest even, |e| <= 2^-18 |x|.  A product of two such splits keeps
 // hi*hi + hi*lo + lo*hi; the dropped lo*lo and the two residuals leave a
@@ -195,14 +214,20 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
     // d = 16 (s/4) + 4w + s%4 (the fp32 load layout); chunk u of the
     // 16x16x32 MFMA takes words 8u..8u+7 as the lane's k-group w, so every d
     // of the chunk's 32 appears once.  The query parts follow the same order.
+    // Split after the first tile's and the centroids' loads are issued (the
+    // split waits for the query's loads; the summary loads need not).
     bf16x8 qh[NC32], ql[NC32];
+    auto split_q = [&]() {
+        float qv[D / 4];
+        query_after_loads<D / 4>(x.qf, qv);
 #pragma unroll
-    for (int u = 0; u < NC32; ++u) {
-        uint32_t qw[8];
+        for (int u = 0; u < NC32; ++u) {
+            uint32_t qw[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qw[e] = __float_as_uint(x.qf[8 * u + e]);
-        split2_x8(qw, qh[u], ql[u]);
-    }
+            for (int e = 0; e < 8; ++e) qw[e] = __float_as_uint(qv[8 * u + e] * x.qs);
+            split2_x8(qw, qh[u], ql[u]);
+        }
+    };
     // (rows of A) . q for the lane's 32 / 16 words (NC32 chunks)
     auto dot_q = [&](const uint32_t* words) {
         f32x4 acc[3];
@@ -311,9 +336,14 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
             float v[E];
             load_f32<kOff32, E>(a.mu, src + 4 * E * t, v);
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                mv[E * t + e] = (!kMasked || my_phys >= 0) ? __float_as_uint(v[e]) : 0u;
+            for (int e = 0; e < E; ++e) mv[E * t + e] = __float_as_uint(v[e]);
         }
+#pragma unroll
+        for (int i = 0; i < DS; ++i) {
+            after_loads(mv[i]);
+            mv[i] = (!kMasked || my_phys >= 0) ? mv[i] : 0u;
+        }
+        split_q();
         beta = dot_q(mv);
     }
     // lane (w, c) now holds beta[page j0 + 4w + v][head c] in element v.
@@ -388,18 +418,23 @@ __device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveC
     const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
     const int my_phys = x.my_phys;
 
-    // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e
+    // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e.
+    // Split after the first tile's and the centroids' loads are issued.
     bf16x8 qp[3][NCH];
+    auto split_q = [&]() {
+        float qv[D / 4];
+        query_after_loads<D / 4>(x.qf, qv);
 #pragma unroll
-    for (int t = 0; t < NCH; ++t)
+        for (int t = 0; t < NCH; ++t)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            __bf16 h, m, l;
-            split3(x.qf[8 * t + e], h, m, l);
-            qp[0][t][e] = h;
-            qp[1][t][e] = m;
-            qp[2][t][e] = l;
-        }
+            for (int e = 0; e < 8; ++e) {
+                __bf16 h, m, l;
+                split3(qv[8 * t + e] * x.qs, h, m, l);
+                qp[0][t][e] = h;
+                qp[1][t][e] = m;
+                qp[2][t][e] = l;
+            }
+    };
 
     const int a_pin = c / RR, a_k = c % RR;   // basis row loaded by this lane
     const int c_pin = w / WPP;                // page whose coefficients this lane supplies
@@ -455,14 +490,22 @@ __device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveC
         f32x4 bacc[3];
 #pragma unroll
         for (int i = 0; i < 3; ++i) bacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 mv[NCH];
 #pragma unroll
         for (int t = 0; t < NCH; ++t) {
-            u32x4 v = *reinterpret_cast<const u32x4*>(elem_addr<TS, kOff32>(a.mu, src + 32 * t));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (!kMasked || my_phys >= 0) ? v[e] : 0u;
-#pragma unroll
-            for (int i = 0; i < 3; ++i) bacc[i] = mfma_16x16x32_bf16(as_bf16x8(v), qp[i][t], bacc[i]);
+            mv[t] = *reinterpret_cast<const u32x4*>(elem_addr<TS, kOff32>(a.mu, src + 32 * t));
         }
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            after_loads(mv[t]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mv[t][e] = (!kMasked || my_phys >= 0) ? mv[t][e] : 0u;
+        }
+        split_q();
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) bacc[i] = mfma_16x16x32_bf16(as_bf16x8(mv[t]), qp[i][t], bacc[i]);
         beta = bacc[0] + bacc[1] + bacc[2];
     }
 
@@ -570,18 +613,23 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
     const uint8_t* const basis_q = static_cast<const uint8_t*>(a.basis);
     const uint8_t* const coef_q = static_cast<const uint8_t*>(a.coef);
 
-    // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e
+    // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e.
+    // Split after the first tile's and the centroids' loads are issued.
     bf16x8 qp[3][NCH];
+    auto split_q = [&]() {
+        float qv[D / 4];
+        query_after_loads<D / 4>(x.qf, qv);
 #pragma unroll
-    for (int t = 0; t < NCH; ++t)
+        for (int t = 0; t < NCH; ++t)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            __bf16 h, m, l;
-            split3(x.qf[8 * t + e], h, m, l);
-            qp[0][t][e] = h;
-            qp[1][t][e] = m;
-            qp[2][t][e] = l;
-        }
+            for (int e = 0; e < 8; ++e) {
+                __bf16 h, m, l;
+                split3(qv[8 * t + e] * x.qs, h, m, l);
+                qp[0][t][e] = h;
+                qp[1][t][e] = m;
+                qp[2][t][e] = l;
+            }
+    };
 
     const int a_pin = c / RR, a_k = c % RR;   // basis row loaded by this lane
     const int c_pin = w / WPP;                // page whose coefficients this lane supplies
@@ -645,11 +693,20 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
         f32x4 bacc[3];
 #pragma unroll
         for (int i = 0; i < 3; ++i) bacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x2 m8[NCH];
 #pragma unroll
         for (int t = 0; t < NCH; ++t) {
-            u32x2 m8 = *reinterpret_cast<const u32x2*>(mu_q + src + 32 * t);
-            if (kMasked && my_phys < 0) m8 = u32x2{0u, 0u};
-            const u32x2 lo = widen_i8x4(m8[0]), hi = widen_i8x4(m8[1]);
+            m8[t] = *reinterpret_cast<const u32x2*>(mu_q + src + 32 * t);
+        }
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            after_loads(m8[t]);
+            if (kMasked && my_phys < 0) m8[t] = u32x2{0u, 0u};
+        }
+        split_q();
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const u32x2 lo = widen_i8x4(m8[t][0]), hi = widen_i8x4(m8[t][1]);
             const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
             for (int i = 0; i < 3; ++i) bacc[i] = mfma_16x16x32_bf16(as_bf16x8(v), qp[i][t], bacc[i]);
@@ -765,8 +822,10 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
         (c < kBatch && x.j0 + c < full && p_spec >= 0 && p_spec < a.num_blocks) ? p_spec : -1;
 
     // Query fragment, in the contraction order of the summary loads:
-    // qf[E t + e] = q[h][4E t + E w + e] for head h = c, scaled to log2 units.
-    const float qscale = kLog2e / sqrtf((float)D);
+    // qf[E t + e] = q[h][4E t + E w + e] for head h = c, as loaded; the batch
+    // functions scale it to log2 units (qs, 0 for padding heads) when they
+    // split it, after their first summary loads are issued.
+    x.qs = x.head_ok ? kLog2e / sqrtf((float)D) : 0.0f;
     {
         const float* qp =
             a.q + ((size_t)x.b * a.num_q_heads + x.g * x.G + (x.head_ok ? c : 0)) * D;
@@ -777,7 +836,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
                 const f32x4 v = *reinterpret_cast<const f32x4*>(qp + 4 * E * t + E * w + 4 * h4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    x.qf[E * t + 4 * h4 + e] = x.head_ok ? v[e] * qscale : 0.0f;
+                    x.qf[E * t + 4 * h4 + e] = v[e];
             }
     }
 
