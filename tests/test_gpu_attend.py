@@ -76,6 +76,12 @@ CASES = [
                                                    budget_tokens=4096,
                                                    seq_lens=[64 * (36 + i) + 5 * i for i in range(16)]),
      True),
+    # 32 (sequence, KV head) groups of 65 slots: the wave-per-run kernel with
+    # 4-page runs and partial pages at the end of every run
+    ("bf16-batch4-G4-k64-runs", lambda: bf16_small(batch=4, num_kv_heads=8, budget_tokens=4096,
+                                                   seq_lens=[64 * (70 + 3 * i) + 9 * i
+                                                             for i in range(4)]),
+     True),
 ]
 
 
