@@ -268,8 +268,15 @@ def main():
     sparse_mean, _, _ = time_events(
         lambda i: lk.locks_sparse_attend(q, kvs[i % L], pages, bufs[i % L][0], bufs[i % L][2],
                                          bufs[i % L][3], ws=att_ws), args.steps, torch)
+    # the same calls back to back (attention kernel + merge kernel per call), and
+    # the K/V bytes they must read: the selected pages and the partial last pages
+    sparse_b2b = time_batch(
+        lambda i: lk.locks_sparse_attend(q, kvs[i % L], pages, bufs[i % L][0], bufs[i % L][2],
+                                         bufs[i % L][3], ws=att_ws), args.steps, torch)
+    sparse_b = (B * Hkv * k + partial * Hkv) * traffic.kv_unit_bytes(d, P)
     step_b = traffic.step_bytes(full_total, partial, Hkv, d, P, r, B * Hkv * k)
-    log(f"select (scan+topk): {sel_mean:.2f} us, sparse attend+merge: {sparse_mean:.2f} us")
+    log(f"select (scan+topk): {sel_mean:.2f} us, sparse attend+merge: {sparse_mean:.2f} us "
+        f"({sparse_b2b:.2f} us back to back, {sparse_b / (sparse_b2b * 1e-6) / 1e9:.0f} GB/s)")
 
     # --- the same step with reduced-precision summaries (reported beside the
     # fp32 headline): bf16 values, and the pages' own int8 / int4 codes.  The
@@ -380,6 +387,9 @@ def main():
             "scan_us": round(scan_mean, 3),
             "select_us": round(sel_mean, 3),
             "sparse_attend_us": round(sparse_mean, 3),
+            "sparse_attend_back_to_back_us": round(sparse_b2b, 3),
+            "sparse_attend_bytes": sparse_b,
+            "sparse_attend_GBps": round(sparse_b / (sparse_b2b * 1e-6) / 1e9, 1),
             "dense_attend_us": None if dense_mean is None else round(dense_mean, 3),
             "speedup_vs_dense": None if dense_mean is None else round(dense_mean / step_us, 3),
             "step_bytes": step_b,

@@ -45,7 +45,8 @@ constexpr int kFastK = 64;
 constexpr int kCandCap = 1024;
 constexpr int kMaxRuns = kTopkMaxPages / kRunPages;  // 2048
 constexpr int kRunPer = kMaxRuns / kThreads;         // run maxima per thread
-constexpr int kListCap = kThreads / kRunPages;       // runs read, one page per thread
+constexpr int kListPer = 4;                          // pages of listed runs per thread
+constexpr int kListCap = kListPer * kThreads / kRunPages;  // runs read (256)
 
 __device__ __forceinline__ uint32_t popc64(unsigned long long m) { return __popcll(m); }
 
@@ -94,6 +95,47 @@ __device__ __forceinline__ uint32_t group_bound(uint32_t my_max, int k, uint32_t
     }
     const int rank = (int)sum_in_row((float)cnt);
     if (q == 0 && rank == k - 1) *s_T = v;
+    __syncthreads();
+    return *s_T;
+}
+
+// For larger k: the k-th largest of the 128 values formed by the two
+// largest thread maxima of each of the 64 groups.  The two come from
+// different threads, so they are keys of different pages, and at least k
+// keys are >= the result: a lower bound on the k-th largest key, tighter
+// than group_bound's once k approaches 64.  Key 0 marks an absent value.
+// Contains two barriers; every thread gets T.  s_gmax holds 128 entries.
+__device__ __forceinline__ uint32_t group_bound2(uint32_t my_max, int k, uint32_t* s_tmax,
+                                                 uint32_t* s_gmax, uint32_t* s_T) {
+    const int t = threadIdx.x, i_row = t >> 4, q = t & 15;
+    s_tmax[t] = my_max;
+    __syncthreads();
+    const uint32_t x = s_tmax[i_row + 64 * q];
+    const uint32_t m1 = umax_in_row(x);
+    // the second largest: the row's maximum without its first holder
+    const unsigned long long eq = __ballot(x == m1);
+    const uint32_t row_eq = (uint32_t)(eq >> (16 * ((t & 63) >> 4))) & 0xffffu;
+    const int first = __builtin_ctz(row_eq);  // the row's own lane holds m1
+    const uint32_t m2 = umax_in_row(q == first ? 0u : x);
+    if (q == 0) {
+        s_gmax[i_row] = m1;
+        s_gmax[64 + i_row] = m2;
+    }
+    __syncthreads();
+    // ranks of values i_row and 64 + i_row (larger first, then lower index):
+    // a permutation of 0..127, so exactly one value has rank k-1
+    const uint32_t v1 = s_gmax[i_row], v2 = s_gmax[64 + i_row];
+    int c1 = 0, c2 = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int u = 8 * q + e;
+        const uint32_t o = s_gmax[u];
+        c1 += (o > v1 || (o == v1 && u < i_row)) ? 1 : 0;
+        c2 += (o > v2 || (o == v2 && u < 64 + i_row)) ? 1 : 0;
+    }
+    const int r1 = (int)sum_in_row((float)c1), r2 = (int)sum_in_row((float)c2);
+    if (q == 0 && r1 == k - 1) *s_T = v1;
+    if (q == 0 && r2 == k - 1) *s_T = v2;
     __syncthreads();
     return *s_T;
 }
@@ -167,7 +209,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* b
 
 __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
     __shared__ uint32_t s_tmax[kThreads];
-    __shared__ uint32_t s_gmax[64];
+    __shared__ uint32_t s_gmax[128];
     __shared__ uint32_t s_T;
     __shared__ uint32_t s_count[2];  // runs listed, candidates
     __shared__ uint32_t s_list[kListCap];
@@ -239,7 +281,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
                 rkey[i] = r < nruns ? orderable_bits(rmv[i]) : 0u;
                 my_max = rkey[i] > my_max ? rkey[i] : my_max;
             }
-            const uint32_t T = group_bound(my_max, k, s_tmax, s_gmax, &s_T);
+            const uint32_t T = k > 32 ? group_bound2(my_max, k, s_tmax, s_gmax, &s_T)
+                                      : group_bound(my_max, k, s_tmax, s_gmax, &s_T);
 #pragma unroll
             for (int i = 0; i < kRunPer; ++i)
                 wave_append<uint32_t>(rkey[i] != 0u && rkey[i] >= T, (uint32_t)(i * kThreads + t),
@@ -247,22 +290,29 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
             __syncthreads();
             const int nlist = (int)s_count[0];
             if (nlist <= kListCap) {
-                // one page of a listed run per thread; candidates are its keys >= T
-                bool hit = false;
-                unsigned long long ck = 0;
+                // page t%16 of listed runs t/16 + 64 m (m < kListPer) per thread, all
+                // loads in flight together; candidates are the keys >= T (more than
+                // kCandCap of them fall back to the exact search below)
                 const int i_row = t >> 4;
-                if (i_row < nlist) {
-                    const int j = (int)s_list[i_row] * kRunPages + (t & 15);
-                    if (j < n) {
-                        const uint32_t kk = orderable_bits(row[j]);
-                        hit = kk >= T;
-                        ck = ((unsigned long long)kk << 32) |
-                             (unsigned long long)(0xffffffffu - (uint32_t)j);
-                    }
+                float mv[kListPer];
+#pragma unroll
+                for (int m = 0; m < kListPer; ++m) {
+                    const int li = i_row + 64 * m;
+                    const int j = li < nlist ? (int)s_list[li] * kRunPages + (t & 15) : 0;
+                    mv[m] = row[j < n ? j : 0];
                 }
-                wave_append<unsigned long long>(hit, ck, s_cand, &s_count[1], kCandCap);
+#pragma unroll
+                for (int m = 0; m < kListPer; ++m) {
+                    const int li = i_row + 64 * m;
+                    const int j = li < nlist ? (int)s_list[li] * kRunPages + (t & 15) : n;
+                    const uint32_t kk = orderable_bits(mv[m]);
+                    const bool hit = j < n && kk >= T;
+                    const unsigned long long ck = ((unsigned long long)kk << 32) |
+                                                  (unsigned long long)(0xffffffffu - (uint32_t)j);
+                    wave_append<unsigned long long>(hit, ck, s_cand, &s_count[1], kCandCap);
+                }
                 __syncthreads();
-                done = true;  // at most one candidate per thread: never more than kCandCap
+                done = true;
             } else if (t == 0) {
                 s_count[1] = 0;  // read every mass below
             }
