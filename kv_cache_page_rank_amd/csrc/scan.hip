@@ -6,14 +6,13 @@
 //
 // For page j of (b, g) and head h of the group, in log2 units with q
 // pre-scaled by log2(e)/sqrt(d):
-//   T[k][h]   = basis_k . q_h                       (MFMA 16x16x32 bf16, split operands)
-//   beta[h]   = mu . q_h                            (same, 16 pages per tile)
-//   L[i][h]   = sum_k coef[i][k] T[k][h]            (MFMA 16x16x16 bf16, split operands)
+//   T[k][h]   = basis_k . q_h                       (MFMA 16x16x4 fp32)
+//   beta[h]   = mu . q_h                            (MFMA, 16 pages per tile)
+//   L[i][h]   = sum_k coef[i][k] T[k][h]            (MFMA 16x16x4 fp32)
 //   s2[h]     = beta[h] + log2 sum_i 2^L[i][h]      (VALU: max, exp2, sum)
 //   a2        = log2 sum_h 2^s2[h]                  (VALU, 16-lane row)
-// and the outputs are s2 * ln 2 and a2 * ln 2.  fp32 operands enter the bf16
-// matrix cores as two bf16 parts each (hi + lo, ~17 significant bits); the
-// three leading partial products accumulate in fp32.
+// and the outputs are s2 * ln 2 and a2 * ln 2.  bf16 and integer-code
+// summaries run the same products on the bf16 matrix cores (below).
 //
 // One wave scans 16 consecutive logical pages of one (b, g).  Its query
 // fragment (16 heads x d, heads >= G zero) stays in registers.  All loads
@@ -35,6 +34,7 @@ namespace {
 
 constexpr int kBatch = kRunPages;  // pages per wave (one run)
 constexpr int kPrefetch = 1;       // basis tiles in flight ahead of the one computed
+constexpr int kChains = 4;         // independent accumulator chains of an fp32 d contraction
 
 // State of one wave's batch, shared by the two specialisations below.
 template <int D>
@@ -154,44 +154,11 @@ __device__ __forceinline__ void after_loads(T& v) {
     asm volatile("" : "+v"(v)::"memory");
 }
 
-// x = hi + lo + e with hi = bf16(x), lo = bf16(x - hi), both rounded to
-// nearest even, |e| <= 2^-18 |x|.  A product of two such splits keeps
-// hi*hi + hi*lo + lo*hi; the dropped lo*lo and the two residuals leave a
-// relative error of about 3 * 2^-18 of sum |a_d b_d| (each bf16 product is
-// exact in the fp32 accumulator).  Two values at a time: one packed convert
-// for the hi pair, its halves widened back by a shift and a mask, two
-// subtractions and one packed convert for the lo pair.
-__device__ __forceinline__ void split2_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-    typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
-    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16v2));
-    const float r0 = x0 - __uint_as_float(h << 16);
-    const float r1 = x1 - __uint_as_float(h & 0xffff0000u);
-    hi = h;
-    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16v2));
-}
-// 8 fp32 words -> hi and lo bf16x8 operands (element e from word e).
-__device__ __forceinline__ void split2_x8(const uint32_t* words, bf16x8& hi, bf16x8& lo) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        split2_pair(__uint_as_float(words[2 * e]), __uint_as_float(words[2 * e + 1]), h[e], l[e]);
-    hi = as_bf16x8(u32x4{h[0], h[1], h[2], h[3]});
-    lo = as_bf16x8(u32x4{l[0], l[1], l[2], l[3]});
-}
-// 4 floats -> hi and lo bf16x4 operands.
-__device__ __forceinline__ void split2_x4(const float* v, bf16x4& hi, bf16x4& lo) {
-    uint32_t h[2], l[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) split2_pair(v[2 * e], v[2 * e + 1], h[e], l[e]);
-    hi = as_bf16x4(u32x2{h[0], h[1]});
-    lo = as_bf16x4(u32x2{l[0], l[1]});
-}
-
 // One wave's batch of kBatch pages.  kMasked: some page of the batch is
 // absent or the rank is padded, so loads are zeroed per row; otherwise no
 // masking code is emitted.  kHeads: per-head masses are written too.
 // fp32 summaries: the word layout keeps the fp32 loads 64 contiguous bytes
-// per row; the contraction order of the bf16 MFMA is chosen to match it.
+// per row; the contraction order of the MFMA steps is chosen to match it.
 template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
 __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCtx<D>& x) {
     using TS = float;
@@ -202,7 +169,6 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
     constexpr int DS = D / 4;             // words of a row held per lane
     constexpr int E = Summ<TS>::E;        // elements per 16-byte load
     constexpr int NCH = D / (4 * E);      // 16-byte loads per row and lane
-    constexpr int NC32 = D / 32;          // 32-wide contraction chunks of the bf16 MFMA
     constexpr int PF = kPrefetch;
     using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
     const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
@@ -210,38 +176,29 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
     auto phys_at = [&](int pb) { return __shfl(my_phys, pb, kWave); };
     auto phys_uniform = [&](int pb) { return __builtin_amdgcn_readlane(my_phys, pb); };
 
-    // Contraction order: lane (w, c) holds word s of its row at
-    // d = 16 (s/4) + 4w + s%4 (the fp32 load layout); chunk u of the
-    // 16x16x32 MFMA takes words 8u..8u+7 as the lane's k-group w, so every d
-    // of the chunk's 32 appears once.  The query parts follow the same order.
-    // Split after the first tile's and the centroids' loads are issued (the
-    // split waits for the query's loads; the summary loads need not).
-    bf16x8 qh[NC32], ql[NC32];
-    auto split_q = [&]() {
-        float qv[D / 4];
-        query_after_loads<D / 4>(x.qf, qv);
+    // The query in fp32, word s of lane (w, c) at d = 16 (s/4) + 4w + s%4
+    // (the fp32 load layout): MFMA step s contracts these 4 d's.  Scaled once
+    // the first tile's and the centroids' loads are issued (scaling waits for
+    // the query's loads; the summary loads need not).
+    float qv[DS];
+    auto prepare_q = [&]() {
+        query_after_loads<DS>(x.qf, qv);
 #pragma unroll
-        for (int u = 0; u < NC32; ++u) {
-            uint32_t qw[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qw[e] = __float_as_uint(qv[8 * u + e] * x.qs);
-            split2_x8(qw, qh[u], ql[u]);
-        }
+        for (int i = 0; i < DS; ++i) qv[i] *= x.qs;
     };
-    // (rows of A) . q for the lane's 32 / 16 words (NC32 chunks)
+    // (rows of A) . q for the lane's DS words: 16x16x4 fp32 steps in
+    // kChains independent accumulator chains
     auto dot_q = [&](const uint32_t* words) {
-        f32x4 acc[3];
+        f32x4 acc[kChains];
 #pragma unroll
-        for (int i = 0; i < 3; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < kChains; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < NC32; ++u) {
-            bf16x8 ah, al;
-            split2_x8(words + 8 * u, ah, al);
-            acc[0] = mfma_16x16x32_bf16(ah, qh[u], acc[0]);
-            acc[1] = mfma_16x16x32_bf16(ah, ql[u], acc[1]);
-            acc[2] = mfma_16x16x32_bf16(al, qh[u], acc[2]);
-        }
-        return acc[0] + (acc[1] + acc[2]);
+        for (int st = 0; st < DS; ++st)
+            acc[st % kChains] = mfma_16x16x4_f32(__uint_as_float(words[st]), qv[st], acc[st % kChains]);
+        f32x4 T = acc[0];
+#pragma unroll
+        for (int i = 1; i < kChains; ++i) T += acc[i];
+        return T;
     };
 
     // Basis-tile row assignment for the loading lane (row m = c):
@@ -343,7 +300,7 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
             after_loads(mv[i]);
             mv[i] = (!kMasked || my_phys >= 0) ? mv[i] : 0u;
         }
-        split_q();
+        prepare_q();
         beta = dot_q(mv);
     }
     // lane (w, c) now holds beta[page j0 + 4w + v][head c] in element v.
@@ -354,28 +311,18 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
         if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
         const Tile& cur = ring[tt % (PF + 1)];
         const f32x4 Tcur = dot_q(cur.v);
-        // lane (w, c) holds tile rows 4w + v: its B operand k = 4w + v of the
-        // 16x16x16 coefficient product, k <-> (page v / KS2, basis row KS2 w + v % KS2)
-        bf16x4 th, tl;
-        {
-            const float tv[4] = {Tcur[0], Tcur[1], Tcur[2], Tcur[3]};
-            split2_x4(tv, th, tl);
-        }
+        // coefficient product in fp32 (8 accumulating 16x16x4 steps per page at
+        // rank 8): lane (w, c) element v holds T[page v/KS2][KS2 w + v%KS2][head c],
+        // its B operand for k-step v%KS2 of page v/KS2
         f32x4 L[PPT][MT];
 #pragma unroll
         for (int p = 0; p < PPT; ++p)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                // A row = token 16 mt + c; element v is page p's coefficient
-                // for k = 4w + v, zero where row 4w + v belongs to another page
-                float cv[4];
+                L[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int v = 0; v < 4; ++v) cv[v] = v / KS2 == p ? coef_el(cur, p, mt, v % KS2) : 0.f;
-                bf16x4 ch, cl;
-                split2_x4(cv, ch, cl);
-                f32x4 acc = mfma_16x16x16_bf16(ch, th, f32x4{0.f, 0.f, 0.f, 0.f});
-                acc = mfma_16x16x16_bf16(ch, tl, acc);
-                L[p][mt] = mfma_16x16x16_bf16(cl, th, acc);
+                for (int ks = 0; ks < KS2; ++ks)
+                    L[p][mt] = mfma_16x16x4_f32(coef_el(cur, p, mt, ks), Tcur[p * KS2 + ks], L[p][mt]);
             }
 
 #pragma unroll

@@ -368,3 +368,28 @@ def test_select_deterministic():
         outs.append((sel.cpu(), mass.cpu(), pm.cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("scale", [16.0])
+def test_scan_large_logits(scale):
+    """Logits of tens (queries scaled up, page centroids offset): the fp32
+    scan still matches the oracle's masses within 1e-4 (its products carry
+    an error relative to the logits' size, so this is the demanding case)."""
+    case = Case(bf16_small(num_kv_heads=8, page_offset_std=4.0))
+    s = case.spec
+    mu, basis, coef = case.oracle_summaries()
+    q_host = (case.layer.q.astype(np.float64) * scale).astype(np.float32)
+    head_o, page_o = oracle.scan_pool(case.lay, s.rank, q_host, mu, basis, coef)
+    summ = summaries_to_device(mu, basis, coef)
+    import kv_cache_page_rank_amd as lk
+    q = torch.from_numpy(q_host).to(DEV)
+    pm = torch.empty((s.batch, s.num_kv_heads, s.max_pages), device=DEV)
+    hm = torch.empty((s.batch, s.num_q_heads, s.max_pages), device=DEV)
+    say("scan large logits", scale, s)
+    lk.locks_scan(q, summ, case.pages, pm, hm)
+    torch.cuda.synchronize()
+    fin = np.isfinite(page_o)
+    assert float(np.abs(page_o[fin]).max()) > 8.0  # the regime this case is for
+    err_page, err_head = masses_close(to_np(pm), page_o), masses_close(to_np(hm), head_o)
+    say("max |log-mass error|", err_page, err_head)
+    assert err_page <= 1e-4 and err_head <= 1e-4
