@@ -10,8 +10,8 @@
 // lse = (M + log2 L) ln 2.
 //
 // bf16 caches (P = 64): MFMA for both products with the group's (up to 16)
-// heads as the 16-wide MFMA dimension; q and p are split into two bf16
-// parts so the products carry ~16 significant bits.  V pages are stored
+// heads as the 16-wide MFMA dimension; q is split into three bf16 parts
+// (~24 significant bits) and p into two (~16).  V pages are stored
 // transposed ([d][P]) so that each lane's contraction elements (tokens) are
 // contiguous.
 #include "device_common.hpp"
@@ -87,7 +87,7 @@ __device__ __forceinline__ void combine_waves(const AttnParams& a, float (*sm_m)
 // a run of pages); the 4 waves of a workgroup take 4 consecutive splits of
 // one (b, g) and are combined in LDS into one partial.  Per page and wave,
 // with the group's heads as the 16-wide MFMA dimension:
-//   S^T (64 tok x 16 h) = K (64 x d) . q^T   v_mfma_f32_16x16x32_bf16 (q as hi + lo)
+//   S^T (64 tok x 16 h) = K (64 x d) . q^T   v_mfma_f32_16x16x32_bf16 (q in three parts)
 //   O^T (d x 16 h)     += V^T (d x 64) . p^T v_mfma_f32_16x16x32_bf16 (p as hi + lo)
 // All of a page's K and V fragments (32 KB per wave) are requested before
 // any is used.  The token order inside the score tiles is chosen so that
@@ -100,6 +100,14 @@ struct PageFrag {
     static constexpr int KS = D / 32, MT = P / 16, KS2 = P / 32, MD = D / 16;
     u32x4 k[MT][KS];
     u32x4 v[KS2][MD];
+};
+
+// The query's three bf16 parts per 32-wide chunk: q = hi + mid + lo, each the
+// nearest-even bf16 of what the previous parts leave (~24 significant bits),
+// so a score from bf16 keys carries fp32-level error whatever its size.
+template <int KS>
+struct QParts {
+    bf16x8 part[3][KS];
 };
 
 // Buffer descriptor of one page of `bytes` bytes at `base`; with `present`
@@ -149,7 +157,7 @@ __device__ __forceinline__ void load_page_v_rsrc(__amdgpu_buffer_rsrc_t rs, int 
 // Scores of one page (log2 units), tokens past nv set to -inf.
 template <int P, int D>
 __device__ __forceinline__ void page_scores(const PageFrag<P, D>& f, int nv, int w,
-                                            const bf16x8* qhi, const bf16x8* qlo, f32x4* sc) {
+                                            const QParts<D / 32>& q, f32x4* sc) {
     using F = PageFrag<P, D>;
 #pragma unroll
     for (int mt = 0; mt < F::MT; ++mt) {
@@ -157,8 +165,9 @@ __device__ __forceinline__ void page_scores(const PageFrag<P, D>& f, int nv, int
 #pragma unroll
         for (int ks = 0; ks < F::KS; ++ks) {
             const bf16x8 kf = as_bf16x8(f.k[mt][ks]);
-            sc[mt] = mfma_16x16x32_bf16(kf, qhi[ks], sc[mt]);
-            sc[mt] = mfma_16x16x32_bf16(kf, qlo[ks], sc[mt]);
+            sc[mt] = mfma_16x16x32_bf16(kf, q.part[2][ks], sc[mt]);
+            sc[mt] = mfma_16x16x32_bf16(kf, q.part[1][ks], sc[mt]);
+            sc[mt] = mfma_16x16x32_bf16(kf, q.part[0][ks], sc[mt]);
         }
     }
     // lane (w, c) element v of tile mt: token 32(mt/2) + 8w + 4(mt%2) + v, head c
@@ -234,7 +243,7 @@ __device__ __forceinline__ void page_values(const PageFrag<P, D>& f, f32x4* sc, 
 }
 
 // q fragment of head hq: the raw loads (q[hq][32ks + 8w + e], every chunk's
-// loads in flight together) and their split into bf16 hi + lo in log2 units
+// loads in flight together) and their split into three bf16 parts in log2 units
 // (zero for padding heads).
 template <int D>
 __device__ __forceinline__ void load_q_raw(const AttnParams& a, int b, int hq, int w, f32x4* xa,
@@ -246,26 +255,32 @@ __device__ __forceinline__ void load_q_raw(const AttnParams& a, int b, int hq, i
         xb[ks] = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
     }
 }
+__device__ __forceinline__ void split3_bits(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+    h = f32_to_bf16_bits(x);
+    const float r = x - bf16_bits_to_f32(h);
+    m = f32_to_bf16_bits(r);
+    l = f32_to_bf16_bits(r - bf16_bits_to_f32(m));
+}
 template <int D>
 __device__ __forceinline__ void split_q(const f32x4* xa, const f32x4* xb, bool head_ok,
-                                       bf16x8* qhi, bf16x8* qlo) {
+                                       QParts<D / 32>& q) {
     const float qscale = kLog2e / sqrtf((float)D);
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
         const f32x4 x0 = xa[ks], x1 = xb[ks];
-        u32x4 hi, lo;
+        u32x4 w3[3];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float v0 = head_ok ? (e < 2 ? x0[2 * e] : x1[2 * e - 4]) * qscale : 0.f;
             const float v1 = head_ok ? (e < 2 ? x0[2 * e + 1] : x1[2 * e - 3]) * qscale : 0.f;
-            uint16_t h0, l0, h1, l1;
-            split_bf16(v0, h0, l0);
-            split_bf16(v1, h1, l1);
-            hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lo[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            uint16_t p0[3], p1[3];
+            split3_bits(v0, p0[0], p0[1], p0[2]);
+            split3_bits(v1, p1[0], p1[1], p1[2]);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) w3[i][e] = (uint32_t)p0[i] | ((uint32_t)p1[i] << 16);
         }
-        qhi[ks] = as_bf16x8(hi);
-        qlo[ks] = as_bf16x8(lo);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) q.part[i][ks] = as_bf16x8(w3[i]);
     }
 }
 
@@ -342,7 +357,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
         }
     }
 
-    bf16x8 qhi[KS], qlo[KS];
+    QParts<KS> qp;
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[MD];
 #pragma unroll
@@ -395,7 +410,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
             int jn, pn;
             const bool more = take(jn, pn);
             f32x4 sc[PageFrag<P, D>::MT];
-            page_scores<P, D>(f, nv, w, qhi, qlo, sc);
+            page_scores<P, D>(f, nv, w, qp, sc);
             load_page_k_rsrc<P, D>(kpage(pn, more), w, c, f);
             page_values<P, D>(f, sc, nv, w, m_run, l_run, acc);
             load_page_v_rsrc<P, D>(vpage(pn, more), w, c, f);
@@ -427,12 +442,12 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
         const bool ok = jc >= 0 && ph_raw >= 0 && ph_raw < a.num_blocks;
         const int jl = ok ? jc : -1, pl = ok ? ph_raw : -1;
         const uint64_t todo = __ballot(ok);
-        if (todo != 0) walk(todo, jl, pl, [&] { split_q<D>(xa, xb, head_ok, qhi, qlo); });
+        if (todo != 0) walk(todo, jl, pl, [&] { split_q<D>(xa, xb, head_ok, qp); });
     } else {
         {
             f32x4 xa[KS], xb[KS];
             load_q_raw<D>(a, b, hq, w, xa, xb);
-            split_q<D>(xa, xb, head_ok, qhi, qlo);
+            split_q<D>(xa, xb, head_ok, qp);
         }
         // The run's page indices and blocks are resolved up front, one lane
         // per page (64 at a time), so each page's K/V loads issue without
@@ -451,7 +466,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
 // Sparse path (bf16, latency-bound at small batch): one workgroup per split
 // (one selected page, or the partial last page), wave wv owns tokens
 // [16wv, 16wv + 16), so each page is fetched by 4 waves at once.  Per wave:
-//   S^T (16 tok x 16 h) = K_tile (16 x d) . q^T   v_mfma_f32_16x16x32_bf16, q as hi + lo
+//   S^T (16 tok x 16 h) = K_tile (16 x d) . q^T   v_mfma_f32_16x16x32_bf16, q in three parts
 //   O^T (d x 16 h)     += V^T (d x 16 tok) . p^T  v_mfma_f32_16x16x16bf16_1k, p as hi + lo
 // Lane (w, c) receives the scores of tokens 4w..4w+3 of its slice for head c,
 // which are exactly its 4 contraction elements of the value product; its
@@ -518,33 +533,11 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
             vraw[md] = *reinterpret_cast<const u32x2*>(vp + (size_t)(16 * md + c) * P);
     }
 
-    bf16x8 qhi[KS], qlo[KS];
+    QParts<KS> qp;
     {
-        const float qscale = kLog2e / sqrtf((float)D);
-        const float* qp = a.q + ((size_t)b * a.num_q_heads + hq) * D;
-        f32x4 xa[KS], xb[KS];  // every chunk's loads first, in flight together
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            xa[ks] = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w);
-            xb[ks] = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 8 * w + 4);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const f32x4 x0 = xa[ks], x1 = xb[ks];
-            u32x4 hi, lo;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v0 = head_ok ? (e < 2 ? x0[2 * e] : x1[2 * e - 4]) * qscale : 0.f;
-                const float v1 = head_ok ? (e < 2 ? x0[2 * e + 1] : x1[2 * e - 3]) * qscale : 0.f;
-                uint16_t h0, l0, h1, l1;
-                split_bf16(v0, h0, l0);
-                split_bf16(v1, h1, l1);
-                hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                lo[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-            }
-            qhi[ks] = as_bf16x8(hi);
-            qlo[ks] = as_bf16x8(lo);
-        }
+        f32x4 xa[KS], xb[KS];
+        load_q_raw<D>(a, b, hq, w, xa, xb);
+        split_q<D>(xa, xb, head_ok, qp);
     }
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -557,8 +550,9 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 kf = as_bf16x8(kraw[ks]);
-            sc = mfma_16x16x32_bf16(kf, qhi[ks], sc);
-            sc = mfma_16x16x32_bf16(kf, qlo[ks], sc);
+            sc = mfma_16x16x32_bf16(kf, qp.part[2][ks], sc);
+            sc = mfma_16x16x32_bf16(kf, qp.part[1][ks], sc);
+            sc = mfma_16x16x32_bf16(kf, qp.part[0][ks], sc);
         }
         if (nv < P) {
 #pragma unroll

@@ -166,3 +166,29 @@ def test_zero_pages_attends_partial_page_only(mk, bf16):
     say("zero selected pages")
     out_g, lse_g = _run_sparse(case, sel)
     _check(out_g, lse_g, out_o, lse_o, bf16)
+
+
+@pytest.mark.parametrize("scale", [16.0])
+def test_attend_large_logits(scale):
+    """Logits of tens (queries scaled up, keys offset per page): outputs within
+    the bf16 bar and lse within 1e-4 of the oracle, on the sparse (one
+    workgroup per page and wave-per-run) and dense kernels."""
+    lk = _lk()
+    for mk in (lambda: bf16_small(page_offset_std=4.0),
+               lambda: bf16_small(batch=16, num_kv_heads=8, page_offset_std=4.0,
+                                  seq_lens=[64 * 40 + (7 * i) % 64 for i in range(16)])):
+        case = Case(mk())
+        s = case.spec
+        q_host = (case.layer.q.astype(np.float64) * scale).astype(np.float32)
+        case.q = torch.from_numpy(q_host).to(DEV)
+        sel = _random_sel(case, case.spec.k_pages, 9)
+        out_o, lse_o = oracle.attend_pool(case.lay, q_host, case.k_f32, case.layer.v_f32(), sel)
+        assert float(np.abs(lse_o).max()) > 8.0  # the regime this case is for
+        say("attend large logits", scale, s)
+        out_g, lse_g = _run_sparse(case, sel)
+        say("sparse max |lse error|", float(np.abs(lse_g - lse_o).max()))
+        _check(out_g, lse_g, out_o, lse_o, True)
+        outd_o, lsed_o = oracle.attend_pool(case.lay, q_host, case.k_f32, case.layer.v_f32(), None)
+        outd_g, lsed_g = _run_dense(case)
+        say("dense max |lse error|", float(np.abs(lsed_g - lsed_o).max()))
+        _check(outd_g, lsed_g, outd_o, lsed_o, True)
