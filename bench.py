@@ -149,7 +149,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path is single-GPU; see DESIGN.md for how it would shard).",
+              "(the hot path is measured on one GPU; sharding over GPUs is not built).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -1,6 +1,7 @@
 """Build step of the HIP library: compiles csrc/*.hip for gfx950 into liblocks.so.
 
-Run ``python -m kv_cache_page_rank_amd.build`` (or ``__graft_entry__.build()``).
+Run ``python -m kv_cache_page_rank_amd.build`` (the repository's build entry
+point calls it too).
 Packed-fp32 instructions are disabled on purpose: the compiler otherwise
 forms v_pk_*_f32 from ordinary float code.
 """
