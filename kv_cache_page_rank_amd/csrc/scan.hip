@@ -34,7 +34,7 @@ namespace {
 
 constexpr int kBatch = kRunPages;  // pages per wave (one run)
 constexpr int kPrefetch = 1;       // basis tiles in flight ahead of the one computed
-constexpr int kChains = 4;         // independent accumulator chains of an fp32 d contraction
+constexpr int kChains = 2;         // independent accumulator chains of an fp32 d contraction
 
 // State of one wave's batch, shared by the two specialisations below.
 template <int D>
