@@ -294,8 +294,8 @@ locks_status locks_mean_share(const float* head_logmass, int32_t num_q_heads,
  * tokens.  sel_pages [B][H_kv][k_pages] as written by locks_select (-1 and
  * indices that are not full pages are ignored).  Split-K: one partial
  * (max, sum, output) per selected page (few pages) or per run of selected
- * pages (many), merged by log-sum-exp in page-list order; results do not
- * depend on which.  out: cache dtype; out_lse optional.
+ * pages (many), merged by log-sum-exp in page-list order (the two differ
+ * only by rounding).  out: cache dtype; out_lse optional.
  * Workspace: locks_workspace_bytes(LOCKS_OP_SPARSE_ATTEND, ...).
  */
 locks_status locks_sparse_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,
