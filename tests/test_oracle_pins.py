@@ -642,3 +642,33 @@ def test_sketch_is_blind_where_page_summaries_are_exact(orc):
     sb_full, _ = orc.shared_basis(lay, d, K)
     _, full = orc.scan_pool(lay, d, q, *orc.sketch_pool(lay, d, K, sb_full, NB))
     np.testing.assert_allclose(full[0, 0, :NB], exact, atol=1e-4)
+
+
+def test_degenerate_sequences_reduce_to_plain_softmax(wl, orc):
+    """Sequences the selection cannot thin out: with no full page nothing is
+    selected and the step attends the partial page alone; when every full
+    page fits the budget all are selected in order.  Either way the step's
+    attention is plain softmax attention over every token (scipy), and an
+    empty sequence gives a zero output with lse -inf."""
+    from scipy.special import softmax
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=[0, 9, 16 * 40 + 3, 16 * 2], batch=4,
+                                     num_q_heads=4, carriers=0)
+    K, V = layer.k_f32(), layer.v_f32()
+    r, P, G = spec.rank, spec.page_size, spec.group
+    mu, basis, coef = orc.build_pool(lay, r, K, spec.num_blocks)
+    _, page = orc.scan_pool(lay, r, layer.q, mu, basis, coef, heads=False)
+    k = spec.k_pages
+    sel, mass = orc.select_pool(lay, spec.budget_tokens, page.astype(np.float32), k)
+    out, lse = orc.attend_pool(lay, layer.q, K, V, sel)
+    assert np.all(sel[0] == -1) and np.all(np.isneginf(mass[0]))
+    assert np.all(out[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    assert np.all(sel[1] == -1)
+    assert list(sel[3, 0]) == [0, 1] + [-1] * (k - 2)
+    for b in (1, 3):
+        for h in range(spec.num_q_heads):
+            g = h // G
+            keys = _tokens(layer, spec, b, g, K)
+            vals = _tokens(layer, spec, b, g, V)
+            s = keys @ layer.q[b, h].astype(np.float64) / math.sqrt(spec.head_dim)
+            assert abs(lse[b, h] - logsumexp(s)) < 1e-12
+            assert np.allclose(out[b, h], softmax(s) @ vals, rtol=0, atol=1e-12)
