@@ -295,7 +295,8 @@ locks_status locks_mean_share(const float* head_logmass, int32_t num_q_heads,
  * indices that are not full pages are ignored).  Split-K: one partial
  * (max, sum, output) per selected page (few pages) or per run of selected
  * pages (many), merged by log-sum-exp in page-list order (the two differ
- * only by rounding).  out: cache dtype; out_lse optional.
+ * only by rounding).  out: cache dtype; out_lse optional.  A sequence with
+ * no token to attend (length 0) gets a zero output and out_lse -inf.
  * Workspace: locks_workspace_bytes(LOCKS_OP_SPARSE_ATTEND, ...).
  */
 locks_status locks_sparse_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,
@@ -306,6 +307,7 @@ locks_status locks_sparse_attend(const float* q, int32_t num_q_heads, const lock
 /*
  * Baseline - the same attention over every token of every sequence (the
  * dense attention the pages compare decode latency against; abstract).
+ * A length-0 sequence gets a zero output and out_lse -inf.
  * Workspace: locks_workspace_bytes(LOCKS_OP_DENSE_ATTEND, ...).
  */
 locks_status locks_dense_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,
