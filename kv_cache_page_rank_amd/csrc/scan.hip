@@ -15,7 +15,8 @@
 // summaries run the same products on the bf16 matrix cores (below).
 //
 // One wave scans 16 consecutive logical pages of one (b, g).  Its query
-// fragment (16 heads x d, heads >= G zero) stays in registers.  All loads
+// fragment (16 heads x d; heads >= G load head 0 and scale it by 0) stays in
+// registers.  All loads
 // are 16-byte vector loads; each MFMA operand is taken straight from the
 // loaded registers thanks to the free choice of contraction order:
 // MFMA step s of a tile contracts d = 16*(s/4) + 4*(l/16) + s%4, so lane l
