@@ -234,6 +234,85 @@ def test_scan_group_aggregation(wl, orc):
     np.testing.assert_array_equal(h1, p1)
 
 
+def test_scan_pool_full_rank_equals_exact_pool_on_shuffled_layout(wl, orc):
+    """Paged indexing of the scan.  At r = min(P, d) the displayed estimator
+    (technical summary, section 2, Reconstructie en Selectie) reduces to the
+    exact page LSE, so on a shuffled block table, with two sequences (one
+    ragged), two KV heads, three query heads per group, a distinct query per
+    head and per-page centroid offsets, scan_pool must return exact_pool's
+    values per head and per group.  exact_pool is pinned above against scipy
+    over tokens gathered through the block table with head h in group h // G,
+    so a wrong head -> group map, a head's output written to another head's
+    row, or a unit read from the wrong physical block fails here by orders
+    of magnitude more than the fp32 rounding of the summaries."""
+    lens = [16 * 21 + 5, 16 * 13]
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=lens, batch=2, num_q_heads=6,
+                                     num_kv_heads=2, carriers=2, page_offset_std=1.0)
+    P, d, G = spec.page_size, spec.head_dim, spec.group
+    r = min(P, d)
+    K = layer.k_f32()
+    assert G == 3
+    # the layout is really shuffled: physical block != logical position
+    assert np.count_nonzero(layer.block_table[0, :lens[0] // P] != np.arange(lens[0] // P)) > 10
+    mu, basis, coef = orc.build_pool(lay, r, K, spec.num_blocks)
+    head, page = orc.scan_pool(lay, r, layer.q, mu, basis, coef)
+    ehead, epage = orc.exact_pool(lay, layer.q, K)
+    for b in range(2):
+        f = lens[b] // P
+        np.testing.assert_allclose(head[b, :, :f], ehead[b, :, :f], rtol=0, atol=1e-6)
+        np.testing.assert_allclose(page[b, :, :f], epage[b, :, :f], rtol=0, atol=1e-6)
+        assert np.all(head[b, :, f:] == -np.inf) and np.all(page[b, :, f:] == -np.inf)
+    # the inputs separate every alternative map: heads, groups and pages differ
+    f0 = lens[0] // P
+    for h in range(1, 6):
+        assert np.abs(ehead[0, 0, :f0] - ehead[0, h, :f0]).max() > 1e-2
+    assert np.abs(epage[0, 0, :f0] - epage[0, 1, :f0]).max() > 1e-2
+    assert np.abs(np.diff(epage[0, 0, :f0])).min() > 1e-6
+
+
+def test_mean_share_reads_each_groups_own_heads(orc):
+    """Head -> group map of the mean-of-share scores (technical summary,
+    section 2, Group-Shared Selection), on a case with a known answer.  Each
+    query head h puts all of its estimated mass, in equal parts, on its own
+    set S_h of pages (the sets are disjoint), plus an arbitrary per-head
+    shift that the share removes.  The share of head h is then 1/|S_h| on S_h
+    and 0 elsewhere, so group g's mean share is 1 / (G |S_h|) on the pages of
+    its own heads h (h // G == g) and 0 (log: -inf) on every other page.  A
+    second case compares random per-head estimates with a numpy mean share
+    built over the heads h with h // G == g."""
+    B, Hq, Hkv, P, MP = 2, 6, 2, 16, 40
+    G = Hq // Hkv
+    lens = [16 * 40, 16 * 37 + 9]
+    lay = _share_layout(orc, B, Hq, Hkv, P, lens, MP)
+    g_rng = np.random.default_rng(21)
+    hm = np.full((B, Hq, MP), -np.inf)
+    expect = np.full((B, Hkv, MP), -np.inf)
+    for b in range(B):
+        f = lens[b] // P
+        owner = g_rng.permutation(np.arange(f) % Hq)  # page -> the head that owns it
+        for h in range(Hq):
+            S = np.flatnonzero(owner == h)
+            hm[b, h, S] = 4.0 * h - 7.0  # equal parts, then a per-head shift
+            expect[b, h // G, S] = -math.log(G * S.size)
+    sh = orc.share_pool(lay, hm)
+    np.testing.assert_array_equal(np.isneginf(sh), np.isneginf(expect))
+    fin = np.isfinite(expect)
+    np.testing.assert_allclose(sh[fin], expect[fin], rtol=0, atol=1e-12)
+
+    hm = _random_heads(B, Hq, MP, lens, P, 22) + g_rng.normal(0, 3, (B, Hq, 1))
+    ref = np.full((B, Hkv, MP), -np.inf)
+    for b in range(B):
+        f = lens[b] // P
+        for g in range(Hkv):
+            heads = [h for h in range(Hq) if h // G == g]
+            shares = [np.exp(hm[b, h, :f] - logsumexp(hm[b, h, :f])) for h in heads]
+            ref[b, g, :f] = np.log(np.mean(shares, axis=0))
+    sh = orc.share_pool(lay, hm)
+    np.testing.assert_array_equal(np.isneginf(sh), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    np.testing.assert_allclose(sh[fin], ref[fin], rtol=0, atol=1e-12)
+
+
 def _share_layout(orc, B, Hq, Hkv, P, lens, MP):
     bt = np.arange(B * MP, dtype=np.int32).reshape(B, MP)
     return orc.Layout(Hq, Hkv, 8, P, bt, np.asarray(lens, np.int32))
@@ -423,6 +502,11 @@ def test_sparse_attend_uses_only_listed_pages(wl, orc):
     Kt = np.concatenate([K[layer.block_table[0, j], 0, :min(P, 1000 - j * P)] for j in pages])
     Vt = np.concatenate([V[layer.block_table[0, j], 0, :min(P, 1000 - j * P)] for j in pages])
     np.testing.assert_allclose(out[0, 0], _sdpa_ref(layer.q[0, 0], Kt, Vt), atol=1e-12)
+    # entries that are not full pages (the partial page 62 itself, an index
+    # past the sequence, -1) are ignored: the partial page is attended once
+    sel2 = np.array([[[2, 17, 40, 62, 75, -1, 62]]], np.int32)
+    out2, _ = orc.attend_pool(lay, layer.q, layer.k_f32(), layer.v_f32(), sel2)
+    np.testing.assert_allclose(out2[0, 0], _sdpa_ref(layer.q[0, 0], Kt, Vt), atol=1e-12)
 
 
 # ---------------------------------------------------------------- planted mistakes
@@ -617,6 +701,26 @@ def test_sketch_is_exact_when_pages_share_one_subspace(orc):
     _, est = orc.scan_pool(lay, m, q, mu, rep, coef)
     _, exact = orc.exact_pool(lay, q, K)
     np.testing.assert_allclose(est[0, 0, :NB], exact[0, 0, :NB], atol=1e-4)
+
+
+def test_sketch_full_basis_is_exact_on_shuffled_layout(wl, orc):
+    """Paged indexing of the sketch: with a shared basis of full rank d every
+    page's centred keys are kept exactly, so on a shuffled block table (two
+    sequences, two KV heads) the sketch's masses equal exact_pool's (pinned
+    against scipy through the block table), per head and per group."""
+    lens = [16 * 11 + 7, 16 * 9]
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=lens, batch=2, num_q_heads=4,
+                                     num_kv_heads=2, carriers=1, page_offset_std=1.0)
+    K, d, P = layer.k_f32(), spec.head_dim, spec.page_size
+    assert np.count_nonzero(layer.block_table[0, :lens[0] // P] != np.arange(lens[0] // P)) > 5
+    sb, _ = orc.shared_basis(lay, d, K)
+    head, page = orc.scan_pool(lay, d, layer.q, *orc.sketch_pool(lay, d, K, sb, spec.num_blocks))
+    ehead, epage = orc.exact_pool(lay, layer.q, K)
+    for b in range(2):
+        f = lens[b] // P
+        np.testing.assert_allclose(head[b, :, :f], ehead[b, :, :f], rtol=0, atol=1e-5)
+        np.testing.assert_allclose(page[b, :, :f], epage[b, :, :f], rtol=0, atol=1e-5)
+    assert np.abs(epage[0, 0, :lens[0] // P] - epage[0, 1, :lens[0] // P]).max() > 1e-2
 
 
 def test_sketch_is_blind_where_page_summaries_are_exact(orc):
