@@ -13,7 +13,15 @@
 //     Rotation angles follow the symmetric 2x2 Schur decomposition; sweeps
 //     stop once no pair of the matrix couples any more (checked over the
 //     whole matrix after each sweep, which spares the last, idle sweep) or
-//     after kMaxSweeps.  A is kept in position space, where a round's pairs
+//     after kMaxSweeps.  One polishing sweep follows with a much tighter
+//     tolerance and no absolute floor beyond what keeps the angle finite: the
+//     stopping rule's floor (2e-7 of the trace) lets couplings of ~1e-5
+//     between the small eigenvalues stand, which turns the rank-r subspace
+//     by ~1e-4 whenever the eigenvalues on either side of the cut lie close;
+//     one more sweep, converging quadratically, removes them (the polished
+//     basis reconstructs logits to ~1e-5 of the double-precision summary on
+//     the 128-dimensional pages of the workloads, against ~3e-4 without).
+//     A is kept in position space, where a round's pairs
 //     are always adjacent positions and a fixed permutation moves every
 //     index between rounds, so each thread owns one 2x2 block with read and
 //     write slots fixed for the whole kernel (a round is a few loads, eight
@@ -23,9 +31,18 @@
 //     during the sweeps, and Kc is read again afterwards.
 //  4. Eigenvalues (diag A) ranked descending, ties by index; for the top r:
 //     basis_k = Kc^T u / sqrt(lambda), re-orthonormalised by modified
-//     Gram-Schmidt; coefficients are the coordinates coef[i][k] =
-//     basis_k . (k_i - mu).  lambda <= 3e-5 lambda_max (or <= 0) is
-//     numerically null and gives a zero basis row and coefficient column.
+//     Gram-Schmidt.  lambda <= 3e-6 lambda_max (or <= 0) is numerically null
+//     and gives a zero basis row and coefficient column.
+//  5. Two steps of subspace iteration on the top r rows, applied through Kc
+//     itself: Y = Kc V^T (P x r), then V^T <- Kc^T Y, re-orthonormalised.  The
+//     Gram squares the conditioning: its fp32 rounding (~1e-7 lambda_max)
+//     moves the rank-r subspace by that over lambda_r - lambda_{r+1}, which
+//     is large when the page's small eigenvalues are small in absolute terms
+//     (pages with little noise).  Products with Kc carry rounding of only
+//     ~1e-7 sigma_1 sigma_k, and each step also shrinks the components
+//     outside the subspace by lambda_{r+1} / lambda_r, so the subspace ends
+//     near the accuracy of an SVD of Kc.
+//  6. Coefficients are the coordinates coef[i][k] = basis_k . (k_i - mu).
 #include "device_common.hpp"
 #include "launchers.hpp"
 #include "quant.hpp"
@@ -37,7 +54,10 @@ namespace {
 constexpr int kMaxSweeps = 20;
 constexpr float kRelTol = 1e-6f;   // |a_pq| <= kRelTol sqrt(a_pp a_qq): already orthogonal
 constexpr float kAbsTol = 2e-7f;   // |a_pq| <= kAbsTol trace(A): negligible coupling
-constexpr float kNullTol = 3e-5f;  // lambda <= kNullTol lambda_max: numerically null
+constexpr float kPolishRelTol = 1e-7f;  // the polishing sweep's relative tolerance
+constexpr float kPolishAbsTol = 1e-12f; // and its floor (keeps zeta finite, see jacobi_angle)
+constexpr float kNullTol = 3e-6f;  // lambda <= kNullTol lambda_max: numerically null
+constexpr int kRefineSteps = 2;    // subspace-iteration steps through Kc
 
 // Waves: 0 (rotations, diagonal blocks), 1..NOFFW (off-diagonal blocks of
 // A), then the U waves (eight row updates per lane and round at P = 64).
@@ -85,10 +105,11 @@ __device__ constexpr int sigma(int pos) {
                             : pos + 2;
 }
 
-// Pair (p, q) still couples: |a_pq| above kRelTol sqrt(|a_pp a_qq|) (compared
-// squared) and above the absolute floor.
-__device__ __forceinline__ bool couples(float app, float aqq, float apq, float abs_tol) {
-    return apq * apq > (kRelTol * kRelTol) * fabsf(app * aqq) && fabsf(apq) > abs_tol;
+// Pair (p, q) still couples: |a_pq| above rel_tol sqrt(|a_pp a_qq|) (compared
+// squared, rel2 = rel_tol^2) and above the absolute floor.
+__device__ __forceinline__ bool couples(float app, float aqq, float apq, float abs_tol,
+                                        float rel2 = kRelTol * kRelTol) {
+    return apq * apq > rel2 * fabsf(app * aqq) && fabsf(apq) > abs_tol;
 }
 
 // Rotation (cos, sin) that zeroes a_pq of the symmetric 2x2 block: with
@@ -228,6 +249,7 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
     }
     __syncthreads();
     const float abs_tol = fmaxf(kAbsTol * trace_s, 1e-30f);
+    const float polish_abs_tol = fmaxf(kPolishAbsTol * trace_s, 1e-30f);
 
     // 3. Jacobi sweeps in position space (pair i at positions 2i, 2i+1),
     //    ping-ponging between two buffers.  Every thread's read and write
@@ -286,7 +308,11 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
     };
     __syncthreads();
     int rounds = 0;
-    for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+    // rotation test of the current sweep: the stopping rule's, then the
+    // polishing sweep's
+    float rot_abs = abs_tol, rot_rel2 = kRelTol * kRelTol;
+    bool polishing = false;
+    for (int sweep = 0;; ++sweep) {
         for (int rd = 0; rd < P - 1; ++rd, ++rounds) {
             const float* cur = jbuf + (rounds & 1) * (P * S);
             float* nxt = jbuf + ((rounds + 1) & 1) * (P * S);
@@ -296,7 +322,7 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
                 const float app = cur[r0 * S + r0], aqq = cur[r1 * S + r1];
                 const float apq = cur[r0 * S + r1];
                 float cs = 1.f, sn = 0.f, tn = 0.f;
-                const bool rot = couples(app, aqq, apq, abs_tol);
+                const bool rot = couples(app, aqq, apq, rot_abs, rot_rel2);
                 if (rot) jacobi_angle(app, aqq, apq, cs, sn, tn);
                 ring[rounds & 1][t] = f32x2{cs, sn};
                 nxt[s0 * S + s0] = app - tn * apq;
@@ -322,8 +348,10 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
             }
             __syncthreads();
         }
+        if (polishing) break;  // the polishing sweep is the last
         // Converged when no pair of the matrix couples any more: the next
-        // sweep would rotate nothing, so it is not run.
+        // sweep would rotate nothing by the stopping rule; the polishing
+        // sweep runs instead.
         const float* fin = jbuf + (rounds & 1) * (P * S);
         bool coupled = false;
         for (int e = t; e < P * P; e += NT) {
@@ -332,7 +360,11 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
         }
         if (coupled) more[sweep & 1] = 1;
         __syncthreads();
-        if (more[sweep & 1] == 0) break;  // same value for every thread
+        if (more[sweep & 1] == 0 || sweep + 1 >= kMaxSweeps) {  // same for every thread
+            polishing = true;
+            rot_abs = polish_abs_tol;
+            rot_rel2 = kPolishRelTol * kPolishRelTol;
+        }
     }
     if (uthr && rounds > 0) rotate_u(rounds - 1);  // the last round's rotations
     // sweeps end with the layout back at pos0: eigenvalue of index x
@@ -383,36 +415,65 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
     // Re-orthonormalise the rows (modified Gram-Schmidt, two passes, largest
     // eigenvalue first): the fp32 Gram squares the conditioning, so rows of
     // small-eigenvalue directions are orthonormal only to ~1e-4 otherwise.
-    if (t < kWave) {
-        constexpr int DL = D / kWave;  // dims per lane
-        for (int k = 0; k < r; ++k) {
-            float x[DL];
-            float nrm2 = 0.f;
+    auto orthonormalise_rows = [&]() {
+        if (t < kWave) {
+            constexpr int DL = D / kWave;  // dims per lane
+            for (int k = 0; k < r; ++k) {
+                float x[DL];
+                float nrm2 = 0.f;
 #pragma unroll
-            for (int e = 0; e < DL; ++e) {
-                x[e] = vs[k][t + kWave * e];
-                nrm2 += x[e] * x[e];
-            }
-            if (wave_sum(nrm2) == 0.f) continue;  // null direction stays zero
-            for (int pass = 0; pass < 2; ++pass) {
-                for (int jr = 0; jr < k; ++jr) {
-                    float dp = 0.f;
-#pragma unroll
-                    for (int e = 0; e < DL; ++e) dp += x[e] * vs[jr][t + kWave * e];
-                    dp = wave_sum(dp);
-#pragma unroll
-                    for (int e = 0; e < DL; ++e) x[e] -= dp * vs[jr][t + kWave * e];
+                for (int e = 0; e < DL; ++e) {
+                    x[e] = vs[k][t + kWave * e];
+                    nrm2 += x[e] * x[e];
                 }
+                if (wave_sum(nrm2) == 0.f) continue;  // null direction stays zero
+                for (int pass = 0; pass < 2; ++pass) {
+                    for (int jr = 0; jr < k; ++jr) {
+                        float dp = 0.f;
+#pragma unroll
+                        for (int e = 0; e < DL; ++e) dp += x[e] * vs[jr][t + kWave * e];
+                        dp = wave_sum(dp);
+#pragma unroll
+                        for (int e = 0; e < DL; ++e) x[e] -= dp * vs[jr][t + kWave * e];
+                    }
+                }
+                nrm2 = 0.f;
+#pragma unroll
+                for (int e = 0; e < DL; ++e) nrm2 += x[e] * x[e];
+                const float inv = 1.f / sqrtf(wave_sum(nrm2));
+#pragma unroll
+                for (int e = 0; e < DL; ++e) vs[k][t + kWave * e] = x[e] * inv;
             }
-            nrm2 = 0.f;
-#pragma unroll
-            for (int e = 0; e < DL; ++e) nrm2 += x[e] * x[e];
-            const float inv = 1.f / sqrtf(wave_sum(nrm2));
-#pragma unroll
-            for (int e = 0; e < DL; ++e) vs[k][t + kWave * e] = x[e] * inv;
+        }
+        __syncthreads();
+    };
+    orthonormalise_rows();
+    // 5. subspace iteration through Kc: Y = Kc V^T, V^T <- Kc^T Y, orthonormalised
+    {
+        float (*const ys)[16] = reinterpret_cast<float (*)[16]>(jbuf + P * UP + 16 * D);  // [P][r]
+        for (int step = 0; step < kRefineSteps; ++step) {
+            for (int i = t; i < P * r; i += NT) {
+                const int k = i / P, tok = i % P;  // a wave shares one basis row
+                float s = 0.f;
+#pragma unroll 8
+                for (int d = 0; d < D; d += 4) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(&kc[tok][d]);
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(&vs[k][d]);
+                    s += x[0] * v[0] + x[1] * v[1] + x[2] * v[2] + x[3] * v[3];
+                }
+                ys[tok][k] = s;
+            }
+            __syncthreads();
+            for (int i = t; i < r * D; i += NT) {
+                const int k = i / D, d = i % D;
+                float s = 0.f;
+                for (int tok = 0; tok < P; ++tok) s += kc[tok][d] * ys[tok][k];
+                vs[k][d] = s;
+            }
+            __syncthreads();
+            orthonormalise_rows();
         }
     }
-    __syncthreads();
     // outputs: centroid, basis, coefficients = coordinates Kc V^T, stored as
     // fp32, rounded to bf16 (nearest even), or as int8 / int4 codes
     if (a.out_dtype == kSummQ8Q4) {

@@ -9,8 +9,12 @@ that are unique (double-precision checks in the harness):
       centred keys in the basis);
   (c) captured energy ||C||_F^2 equals the oracle's sum of the top-r sigma^2
       (eigenvalues are well conditioned even when eigenvectors are not);
-and, on pages whose spectral gap (sigma_r - sigma_{r+1}) / sigma_1 >= 1e-2,
-the reconstructed logits equal the oracle's (normwise 1e-4)."""
+and, on pages whose spectral gap (sigma_r - sigma_{r+1}) / sigma_1 >= 1e-3,
+the reconstructed logits equal the oracle's (normwise 1e-4).  Below that gap
+the rank-r subspace is not well defined at fp32 precision (a Gram error of
+~1e-7 ||Kc||^2 over the gap exceeds 1e-4), so those pages are counted and
+their largest logit difference is printed, not gated.  Every case must
+check the logits on some pages, and the low-noise cases on almost all."""
 import math
 
 import numpy as np
@@ -36,7 +40,7 @@ def _build_gpu(case, rank=None, page_begin=None, dtype=torch.float32):
     return summ
 
 
-def _check_units(case, summ, units, r, gap_min=1e-2):
+def _check_units(case, summ, units, r, gap_min=1e-3):
     s = case.spec
     mu_g = summ.mu.cpu().numpy().astype(np.float64)
     basis_g = summ.basis.cpu().numpy().astype(np.float64)
@@ -44,6 +48,7 @@ def _check_units(case, summ, units, r, gap_min=1e-2):
     mu_o, basis_o, coef_o, sigma_o = oracle.build_units(case.lay, r, case.k_f32, units)
     scale = 1.0 / math.sqrt(s.head_dim)
     n_gapped = 0
+    worst_gapped = worst_small_gap = 0.0
     for n, (b, g, j) in enumerate(units):
         blk = case.layer.block_table[b, j]
         K = case.k_f32[blk, g].astype(np.float64)
@@ -62,15 +67,23 @@ def _check_units(case, summ, units, r, gap_min=1e-2):
         # reconstructed logits on well-separated pages
         sig = sigma_o[n]
         gap = (sig[r - 1] - sig[r]) / sig[0] if r < sig.size else 1.0
+        G = s.group
+        rel = 0.0
+        for hh in range(G):
+            qh = case.layer.q[b, g * G + hh].astype(np.float64)
+            lg = (qh @ mu + C @ (V @ qh)) * scale
+            lo = (qh @ mu_o[n] + coef_o[n] @ (basis_o[n] @ qh)) * scale
+            rel = max(rel, np.linalg.norm(lg - lo) / max(np.linalg.norm(lo),
+                                                         1e-6 * math.sqrt(s.page_size)))
         if gap >= gap_min:
             n_gapped += 1
-            G = s.group
-            for hh in range(G):
-                qh = case.layer.q[b, g * G + hh].astype(np.float64)
-                lg = (qh @ mu + C @ (V @ qh)) * scale
-                lo = (qh @ mu_o[n] + coef_o[n] @ (basis_o[n] @ qh)) * scale
-                assert np.linalg.norm(lg - lo) <= 1e-4 * max(np.linalg.norm(lo),
-                                                             1e-6 * math.sqrt(s.page_size))
+            worst_gapped = max(worst_gapped, rel)
+            assert rel <= 1e-4, (b, g, j, gap, rel)
+        else:
+            worst_small_gap = max(worst_small_gap, rel)
+    print(f"[build logits] {s.name} r={r}: {n_gapped}/{len(units)} pages with gap >= "
+          f"{gap_min:g} checked (worst {worst_gapped:.2e}); the other {len(units) - n_gapped} "
+          f"reported, worst {worst_small_gap:.2e}", flush=True)
     return n_gapped
 
 
@@ -81,8 +94,10 @@ def _check_units(case, summ, units, r, gap_min=1e-2):
     ("bf16-r8", lambda: bf16_small()),
     ("bf16-r2-offset", lambda: bf16_small(rank=2, page_offset_std=1.0)),
     ("bf16-r16-d64", lambda: bf16_small(rank=16, head_dim=64)),
+    ("bf16-r8-low-noise", lambda: bf16_small(noise_std=1e-3)),
+    ("bf16-r8-rank8-pages", lambda: bf16_small(noise_std=1e-3, subspace_rank=8)),
 ], ids=["tiny-r4", "tiny-r16-full-rank", "tiny-r4-offset-G2", "bf16-r8", "bf16-r2-offset",
-        "bf16-r16-d64"])
+        "bf16-r16-d64", "bf16-r8-low-noise", "bf16-r8-rank8-pages"])
 def test_build_matches_oracle(name, mk):
     case = Case(mk())
     s = case.spec
@@ -90,7 +105,10 @@ def test_build_matches_oracle(name, mk):
     summ = _build_gpu(case)
     units = np.array([[b, g, j] for b in range(s.batch) for g in range(s.num_kv_heads)
                       for j in range(s.seq_lens[b] // s.page_size)], np.int32)
-    _check_units(case, summ, units, s.rank)
+    n_gapped = _check_units(case, summ, units, s.rank)
+    assert n_gapped > 0, "no page had a spectral gap large enough for the logit check"
+    if "noise" in name or "rank8" in name:
+        assert n_gapped >= 0.9 * len(units), (n_gapped, len(units))
 
 
 def test_build_full_rank_end_to_end_exact():

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from gpu_cases import DEV, Case, bf16_small, say
 
 pytestmark = pytest.mark.gpu
@@ -57,6 +58,8 @@ def test_refresh_in_graph_tracks_page_crossing(agg):
     blocks = torch.from_numpy(_full_blocks(case).astype(np.int64)).to(DEV)
     for got, want in ((summ.mu, ref.mu), (summ.basis, ref.basis), (summ.coef, ref.coef)):
         assert torch.equal(got[blocks].view(torch.int32), want[blocks].view(torch.int32))
+    # the refreshed pages against the oracle's build of the new state
+    _check_refreshed_against_oracle(case, summ, [(0, 40), (1, 23)])
     # the step's outputs equal the eager calls on fully rebuilt summaries
     e = {key: torch.empty_like(v) for key, v in g.items()}
     lk.locks_select(case.q, ref, case.pages, s.budget_tokens, e["sel"], e["mass"], ws=e["ws"],
@@ -78,6 +81,25 @@ def test_refresh_in_graph_tracks_page_crossing(agg):
     for a, b in zip(before, (summ.mu, summ.basis, summ.coef)):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     graph.close()
+
+
+def _check_refreshed_against_oracle(case, summ, pages):
+    """The oracle's gap-independent checks (centroid, orthonormal basis,
+    coordinate residual, captured energy) and, where the spectral gap allows,
+    the reconstructed logits, on the refreshed (b, j) pages of every KV head,
+    with the sequence lengths the step left on the device."""
+    from test_gpu_build import _check_units
+    s = case.spec
+    lens = case.pages.seq_lens.cpu().numpy().astype(np.int32)
+    view = type("RefreshedCase", (), {})()
+    view.spec = s.with_(seq_lens=[int(x) for x in lens])
+    view.layer = case.layer
+    view.k_f32 = case.k_f32
+    view.lay = oracle.Layout(s.num_q_heads, s.num_kv_heads, s.head_dim, s.page_size,
+                             case.layer.block_table, lens)
+    units = np.array([[b, g, j] for b, j in pages for g in range(s.num_kv_heads)], np.int32)
+    say("refresh: refreshed pages against the oracle", units.tolist())
+    _check_units(view, summ, units, s.rank)
 
 
 def test_refresh_entry_builds_only_the_window():
@@ -103,3 +125,5 @@ def test_refresh_entry_builds_only_the_window():
             assert torch.equal(got.view(torch.int32), ref.basis[blk].view(torch.int32))
         else:
             assert torch.isnan(got).all()
+    _check_refreshed_against_oracle(case, summ, [(b, j) for b, lo in enumerate([5, 21])
+                                                 for j in range(lo, min(lo + 3, full[b]))])
