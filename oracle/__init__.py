@@ -61,7 +61,8 @@ def lib():
         L.orc_attend_tokens.argtypes = [c_int, c_int, _f64p, _f64p, _f64p, _f64p,
                                         ctypes.POINTER(c_double)]
         L.orc_attend_tokens.restype = None
-        L.orc_build_pool.argtypes = [lay, c_int, _f32p, _f32p, _f32p, _f32p, c_int]
+        L.orc_build_pool.argtypes = [lay, c_int, _f32p, _f32p, _f32p, _f32p, ctypes.c_void_p,
+                                     c_int]
         L.orc_build_units.argtypes = [lay, c_int, _f32p, c_int, _i32p, _i32p, _i32p, _f64p,
                                       _f64p, _f64p, _f64p, c_int]
         L.orc_scan_pool.argtypes = [lay, c_int, _f32p, _f32p, _f32p, _f32p, ctypes.c_void_p,
@@ -199,19 +200,24 @@ class Layout:
         return ctypes.byref(s), s
 
 
-def build_pool(L: Layout, r: int, k_pool, num_blocks: int, threads: int = 0):
+def build_pool(L: Layout, r: int, k_pool, num_blocks: int, threads: int = 0,
+               with_sigma: bool = False):
+    """fp32 summaries (mu, basis, coef) of every full page at its physical
+    block; with_sigma also returns the singular values [NB][Hkv][min(P,d)]
+    (double; zero for blocks that hold no full page)."""
     k_pool = _f32(k_pool)
     H, P, d = L.num_kv_heads, L.page_size, L.head_dim
     mu = np.zeros((num_blocks, H, d), np.float32)
     basis = np.zeros((num_blocks, H, max(r, 1), d), np.float32)[:, :, :r]
     basis = np.ascontiguousarray(basis)
     coef = np.zeros((num_blocks, H, P, r), np.float32)
+    sigma = np.zeros((num_blocks, H, min(P, d))) if with_sigma else None
     ref, _keep = L.c()
     _check(lib().orc_build_pool(ref, r, k_pool.reshape(-1), mu.reshape(-1),
                                 basis.reshape(-1) if basis.size else np.zeros(1, np.float32),
                                 coef.reshape(-1) if coef.size else np.zeros(1, np.float32),
-                                threads), "build_pool")
-    return mu, basis, coef
+                                _ptr(sigma), threads), "build_pool")
+    return (mu, basis, coef, sigma) if with_sigma else (mu, basis, coef)
 
 
 def build_units(L: Layout, r: int, k_pool, units, threads: int = 0):

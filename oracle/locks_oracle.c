@@ -276,7 +276,7 @@ int orc_build_units(const orc_layout* L, int r, const float* k_pool, int n, cons
 }
 
 int orc_build_pool(const orc_layout* L, int r, const float* k_pool, float* mu, float* basis,
-                   float* coef, int nthreads) {
+                   float* coef, double* sigma_out, int nthreads) {
     if (!layout_ok(L)) return -1;
     const int P = L->page_size, d = L->head_dim, H = L->num_kv_heads, nsv = P < d ? P : d;
     if (r < 0 || r > nsv) return -1;
@@ -303,6 +303,8 @@ int orc_build_pool(const orc_layout* L, int r, const float* k_pool, float* mu, f
             for (int e = 0; e < d; ++e) mu[unit * d + e] = (float)m[e];
             for (int e = 0; e < r * d; ++e) basis[unit * r * d + e] = (float)v[e];
             for (int e = 0; e < P * r; ++e) coef[unit * P * r + e] = (float)c[e];
+            if (sigma_out)
+                for (int e = 0; e < nsv; ++e) sigma_out[unit * nsv + e] = s[e];
         }
         free(keys);
         free(m);

@@ -97,9 +97,11 @@ typedef struct {
 } orc_layout;
 
 /* Summaries of every full page, written (rounded to float) at its physical
- * block; blocks of partial pages are left untouched. Returns 0 or -1. */
+ * block; blocks of partial pages are left untouched.  sigma_out (nullable,
+ * [NB][Hkv][min(P,d)] double) receives each unit's singular values of the
+ * centred keys, descending.  Returns 0 or -1. */
 int orc_build_pool(const orc_layout* L, int r, const float* k_pool, float* mu, float* basis,
-                   float* coef, int nthreads);
+                   float* coef, double* sigma_out, int nthreads);
 
 /* Double-precision summaries of n listed units (b, g, j) into dense arrays
  * mu [n][d], basis [n][r][d], coef [n][P][r], sigma [n][min(P,d)]. */

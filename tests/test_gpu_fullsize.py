@@ -236,48 +236,51 @@ def test_fullsize_agreement_with_exact_selection(full):
     compares with the selection that reads every key (the exact page LSE,
     aggregated over the group the same way): recall of the exact top-k, the
     share of the exact top-k's mass that the selection captures, carrier
-    recall, and the largest difference between sparse and dense outputs."""
+    recall, and the largest difference between sparse and dense outputs
+    (every sequence of the batch)."""
     import kv_cache_page_rank_amd as lk
     f, s = full, full.spec
-    if s.batch != 1:
-        pytest.skip("reported for the single-sequence 1M-token layers")
+    B = s.batch
     say("exact page masses (oracle, every key)", s.name)
     _, exact = oracle.exact_pool(oracle.Layout(s.num_q_heads, s.num_kv_heads, s.head_dim,
                                                s.page_size, f.layer.block_table, f.layer.seq_lens),
                                  f.layer.q, f.layer.k_f32(), threads=16)
-    nfull = s.seq_lens[0] // s.page_size
-    dout = torch.empty((1, s.num_q_heads, s.head_dim), dtype=torch.bfloat16, device=DEV)
-    dlse = torch.empty((1, s.num_q_heads), device=DEV)
-    dws = lk.workspace(lk.workspace_bytes(lk.OP_DENSE_ATTEND, 1, s.max_pages, s.num_q_heads,
+    dout = torch.empty((B, s.num_q_heads, s.head_dim), dtype=torch.bfloat16, device=DEV)
+    dlse = torch.empty((B, s.num_q_heads), device=DEV)
+    dws = lk.workspace(lk.workspace_bytes(lk.OP_DENSE_ATTEND, B, s.max_pages, s.num_q_heads,
                                           s.num_kv_heads, s.page_size, s.head_dim, s.rank, 0))
     lk.locks_dense_attend(f.q, f.kv, f.pages, dout, dlse, ws=dws)
     for budget in (s.budgets or [s.budget_tokens]):
         k = budget // s.page_size
-        sel = torch.empty((1, s.num_kv_heads, k), dtype=torch.int32, device=DEV)
-        mass = torch.empty((1, s.num_kv_heads, k), device=DEV)
-        ws = lk.workspace(lk.workspace_bytes(lk.OP_STEP, 1, s.max_pages, s.num_q_heads,
+        sel = torch.empty((B, s.num_kv_heads, k), dtype=torch.int32, device=DEV)
+        mass = torch.empty((B, s.num_kv_heads, k), device=DEV)
+        ws = lk.workspace(lk.workspace_bytes(lk.OP_STEP, B, s.max_pages, s.num_q_heads,
                                              s.num_kv_heads, s.page_size, s.head_dim, s.rank, k))
         say("agreement", s.name, budget)
         lk.locks_select(f.q, f.summ, f.pages, budget, sel, mass, ws=ws)
         out = torch.empty_like(dout)
         lse = torch.empty_like(dlse)
-        sel_b = lk.workspace_bytes(lk.OP_SELECT, 1, s.max_pages, s.num_q_heads, s.num_kv_heads,
+        sel_b = lk.workspace_bytes(lk.OP_SELECT, B, s.max_pages, s.num_q_heads, s.num_kv_heads,
                                    s.page_size, s.head_dim, s.rank, k)
         lk.locks_sparse_attend(f.q, f.kv, f.pages, sel, out, lse, ws=ws[sel_b:])
         torch.cuda.synchronize()
         sel_np = sel.cpu().numpy()
         recall, captured, carriers = [], [], 0
-        for g in range(s.num_kv_heads):
-            a = exact[0, g, :nfull]
-            best = _brute_topk(a.astype(np.float32), k)
-            got = sel_np[0, g][sel_np[0, g] >= 0]
-            recall.append(len(set(best.tolist()) & set(got.tolist())) / k)
-            captured.append(math.exp(_lse(a[got]) - _lse(a[best])))
-            carriers += len(set(f.layer.carrier_page[0, g].tolist()) & set(got.tolist()))
+        for b in range(B):
+            nfull = s.seq_lens[b] // s.page_size
+            kk = min(k, nfull)
+            for g in range(s.num_kv_heads):
+                a = exact[b, g, :nfull]
+                best = _brute_topk(a.astype(np.float32), kk)
+                got = sel_np[b, g][sel_np[b, g] >= 0]
+                recall.append(len(set(best.tolist()) & set(got.tolist())) / max(kk, 1))
+                captured.append(math.exp(_lse(a[got]) - _lse(a[best])))
+                carriers += len(set(f.layer.carrier_page[b, g].tolist()) & set(got.tolist()))
         diff = float((out.float() - dout.float()).abs().max())
         print(f"[agreement] {s.name} r={s.rank} budget {budget}: recall@k "
-              f"{np.mean(recall):.3f}, captured exact mass {np.mean(captured):.3f}, carriers "
-              f"{carriers}/{f.layer.carrier_page[0].size}, max|o_sparse - o_dense| {diff:.4f}",
+              f"{np.mean(recall):.3f} (min {np.min(recall):.3f}), captured exact mass "
+              f"{np.mean(captured):.3f} (min {np.min(captured):.3f}), carriers "
+              f"{carriers}/{f.layer.carrier_page.size}, max|o_sparse - o_dense| {diff:.4f}",
               flush=True)
         assert all(0.0 <= r <= 1.0 for r in recall)
         assert all(0.0 < c <= 1.0 + 1e-6 for c in captured)

@@ -382,12 +382,14 @@ def test_scan_full_rank_equals_exact(wl, orc):
 
 def test_build_pool_matches_units(wl, orc):
     spec, layer, lay = _small_layout(wl, orc, seq_lens=[200, 70], batch=2, carriers=1)
-    mu, basis, coef = orc.build_pool(lay, spec.rank, layer.k_f32(), spec.num_blocks)
+    mu, basis, coef, sig = orc.build_pool(lay, spec.rank, layer.k_f32(), spec.num_blocks,
+                                          with_sigma=True)
     units = np.array([[b, 0, j] for b in range(2) for j in range(spec.seq_lens[b] // 16)],
                      np.int32)
-    mu_u, basis_u, coef_u, _ = orc.build_units(lay, spec.rank, layer.k_f32(), units)
+    mu_u, basis_u, coef_u, sig_u = orc.build_units(lay, spec.rank, layer.k_f32(), units)
     for n, (b, g, j) in enumerate(units):
         blk = layer.block_table[b, j]
+        np.testing.assert_array_equal(sig[blk, g], sig_u[n])
         np.testing.assert_array_equal(mu[blk, g], mu_u[n].astype(np.float32))
         np.testing.assert_array_equal(basis[blk, g], basis_u[n].astype(np.float32))
         np.testing.assert_array_equal(coef[blk, g], coef_u[n].astype(np.float32))
