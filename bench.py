@@ -66,7 +66,8 @@ def cpu_threads():
 
 
 # Kernel sources whose HBM traffic the committed counter summary describes.
-SCAN_SOURCES = ["kv_cache_page_rank_amd/csrc/scan.hip", "kv_cache_page_rank_amd/csrc/device_common.hpp",
+SCAN_SOURCES = ["kv_cache_page_rank_amd/csrc/scan_kernel.hpp", "kv_cache_page_rank_amd/csrc/scan_f32.hip",
+                "kv_cache_page_rank_amd/csrc/device_common.hpp",
                 "kv_cache_page_rank_amd/csrc/launchers.hpp"]
 SCAN_COUNTERS = "profiles/scan_kernel_glm4-9b-layer-1m_hbm_counters.txt"
 
@@ -130,6 +131,33 @@ def time_events(fn, iters, torch):
     torch.cuda.synchronize()
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return statistics.mean(ms) * 1e3, statistics.median(ms) * 1e3, ms
+
+
+def dist(us, per=1):
+    """mean / median / p10 / p90 of a list of microseconds (each the mean
+    of `per` back-to-back calls)."""
+    import numpy as np
+    a = np.asarray(us, np.float64)
+    return {"samples": int(a.size), "calls_per_sample": per, "replays": int(a.size) * per,
+            "mean_us": round(float(a.mean()), 3), "median_us": round(float(np.median(a)), 3),
+            "p10_us": round(float(np.percentile(a, 10)), 3),
+            "p90_us": round(float(np.percentile(a, 90)), 3)}
+
+
+def time_samples(fn, samples, per, torch):
+    """`samples` timings, each the mean of `per` back-to-back calls between
+    two events on the current stream (events only between batches, so their
+    own cost is spread over `per` calls).  Returns the dist() record."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(samples + 1)]
+    ev[0].record()
+    n = 0
+    for s_ in range(samples):
+        for _ in range(per):
+            fn(n)
+            n += 1
+        ev[s_ + 1].record()
+    torch.cuda.synchronize()
+    return dist([ev[i].elapsed_time(ev[i + 1]) * 1e3 / per for i in range(samples)], per)
 
 
 def time_batch(fn, iters, torch):
@@ -243,6 +271,12 @@ def main():
     wall_s = time.perf_counter() - t0
     step_us = e0.elapsed_time(e1) * 1e3 / args.steps
     log(f"step: {step_us:.2f} us (graph replay, {L} layer copies), wall {wall_s * 1e6 / args.steps:.2f} us")
+    # the step's distribution: 50 samples, each the mean of 10 back-to-back
+    # replays (an event between samples only: one per replay would add its
+    # own few microseconds to every replay)
+    step_dist = time_samples(lambda i: graphs[i % L].launch(), 50, 10, torch)
+    log(f"step over {step_dist['replays']} replays: median {step_dist['median_us']:.2f} us, "
+        f"p10 {step_dist['p10_us']:.2f}, p90 {step_dist['p90_us']:.2f}")
 
     # --- dominant kernel: the summary scan alone, per-launch events on the launch stream
     pms = [torch.empty((B, Hkv, MP), device="cuda") for _ in range(L)]
@@ -256,8 +290,43 @@ def main():
                            args.steps, torch)
     scan_b = traffic.scan_bytes(B, Hq, Hkv, MP, full_total, d, P, r)
     scan_gbs = scan_b / (scan_mean * 1e-6) / 1e9
+    scan_dist = time_samples(lambda i: lk.locks_scan(q, summs[i % L], pages, pms[i % L]), 50,
+                             10, torch)
     log(f"scan: {scan_mean:.2f} us per launch back to back ({scan_ev_mean:.2f} mean, "
-        f"{scan_med:.2f} median with an event pair per launch), {scan_gbs:.0f} GB/s")
+        f"{scan_med:.2f} median with an event pair per launch; median of 10-launch means "
+        f"{scan_dist['median_us']:.2f}), {scan_gbs:.0f} GB/s")
+
+    # --- ceilings measured with the same build: a contiguous streaming read of
+    # 4 GiB, and the scan's own bytes read in its access pattern with none of
+    # its arithmetic (fp32 summaries at P 64, d 128, r 8)
+    ceilings = {}
+    sbuf = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+    sbuf.fill_(1.0)
+    sink = torch.empty(4 * 16384, dtype=torch.float32, device="cuda")
+    best = (0.0, 0)
+    for blocks in (1024, 2048, 4096, 8192, 16384):  # the best grid is the ceiling
+        sk = sink[:4 * blocks]
+        for _ in range(2):
+            lk.locks_probe_stream_read(sbuf, sk)
+        st_us = time_batch(lambda i: lk.locks_probe_stream_read(sbuf, sk), 10, torch)
+        gbs = sbuf.numel() * 4 / (st_us * 1e-6) / 1e9
+        log(f"ceiling: streaming read of 4 GiB, {blocks} workgroups: {st_us:.1f} us, "
+            f"{gbs:.0f} GB/s")
+        best = max(best, (gbs, blocks))
+    ceilings["stream_read_GBps"] = round(best[0], 1)
+    ceilings["stream_read_workgroups"] = best[1]
+    ceilings["stream_read_bytes"] = sbuf.numel() * 4
+    del sbuf
+    if (P, d, r) == (64, 128, 8):
+        for i in range(args.warmup):
+            lk.locks_probe_summary_read(q, summs[i % L], pages, pms[i % L])
+        pat_us = time_batch(lambda i: lk.locks_probe_summary_read(q, summs[i % L], pages,
+                                                                   pms[i % L]), args.steps, torch)
+        pat_gbs = scan_b / (pat_us * 1e-6) / 1e9
+        ceilings.update({"scan_pattern_read_us": round(pat_us, 3),
+                         "scan_pattern_read_GBps": round(pat_gbs, 1)})
+        log(f"ceiling: the scan's bytes in its access pattern {pat_us:.2f} us, {pat_gbs:.0f} GB/s")
+    torch.cuda.empty_cache()
 
     # --- select alone and sparse attention alone
     sel_ws = lk.workspace(lk.workspace_bytes(lk.OP_SELECT, B, MP, Hq, Hkv, P, d, r, k))
@@ -336,7 +405,7 @@ def main():
     log(f"mean-of-share aggregation: step {share_step:.2f} us")
 
     # --- dense baseline
-    dense_mean = None
+    dense_mean = dense_dist = None
     dense_b = traffic.dense_bytes(sum(-(-n // P) for n in spec.seq_lens), Hkv, d, P)
     if not args.no_dense:
         dws = lk.workspace(lk.workspace_bytes(lk.OP_DENSE_ATTEND, B, MP, Hq, Hkv, P, d, r, 0))
@@ -344,10 +413,12 @@ def main():
         dlse = torch.empty((B, Hq), device="cuda")
         for i in range(2):
             lk.locks_dense_attend(q, kvs[i % L], pages, dout, dlse, ws=dws)
-        dense_mean, _, _ = time_events(
-            lambda i: lk.locks_dense_attend(q, kvs[i % L], pages, dout, dlse, ws=dws),
-            max(5, args.steps // 5), torch)
-        log(f"dense: {dense_mean:.2f} us, {dense_b / (dense_mean * 1e-6) / 1e9:.0f} GB/s")
+        dense_dist = time_samples(
+            lambda i: lk.locks_dense_attend(q, kvs[i % L], pages, dout, dlse, ws=dws), 50, 4,
+            torch)
+        dense_mean = dense_dist["mean_us"]
+        log(f"dense: {dense_mean:.2f} us (median {dense_dist['median_us']:.2f}), "
+            f"{dense_b / (dense_mean * 1e-6) / 1e9:.0f} GB/s")
         for rp in (bf16_summ, q8q4_summ):
             if rp is not None:
                 rp["speedup_vs_dense"] = round(dense_mean / rp["step_us"], 3)
@@ -381,8 +452,13 @@ def main():
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
                      "traffic": counted_traffic(SCAN_COUNTERS, SCAN_SOURCES, spec.name),
                      "bytes_per_launch": scan_b, "avg_launch_us": round(scan_mean, 3),
-                     "avg_launch_us_event_pairs": round(scan_ev_mean, 3)},
+                     "avg_launch_us_event_pairs": round(scan_ev_mean, 3),
+                     "launch_dist": scan_dist, "ceilings": ceilings,
+                     "frac_of_stream_ceiling": round(scan_gbs / ceilings["stream_read_GBps"], 4),
+                     "frac_of_pattern_ceiling": None if "scan_pattern_read_GBps" not in ceilings
+                     else round(scan_gbs / ceilings["scan_pattern_read_GBps"], 4)},
         "cpu_baseline": cpu,
+        "step_dist": step_dist,
         "breakdown": {
             "scan_us": round(scan_mean, 3),
             "select_us": round(sel_mean, 3),
@@ -391,7 +467,10 @@ def main():
             "sparse_attend_bytes": sparse_b,
             "sparse_attend_GBps": round(sparse_b / (sparse_b2b * 1e-6) / 1e9, 1),
             "dense_attend_us": None if dense_mean is None else round(dense_mean, 3),
+            "dense_dist": dense_dist,
             "speedup_vs_dense": None if dense_mean is None else round(dense_mean / step_us, 3),
+            "speedup_vs_dense_medians": None if dense_dist is None else
+            round(dense_dist["median_us"] / step_dist["median_us"], 3),
             "step_bytes": step_b,
             "dense_bytes": dense_b,
             "byte_reduction": round(dense_b / step_b, 3),
@@ -412,14 +491,32 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(spec, layer, target_s, threads):
-    """Time the oracle's decode step on the host cores: scan + aggregation
-    over every full page, selection from those masses, and attention over
-    the pages it selected.  Nothing here comes from the GPU: the summaries are
+    """Time the oracle on the host cores, on the same layer.
+
+    The decode step: scan + aggregation over every full page, selection from
+    those masses, and attention over the pages it selected - with all
+    `threads` cores (repeated for about target_s seconds) and with one thread
+    (a few repeats).  Nothing here comes from the GPU: the summaries are
     seeded stand-ins of the layer's shapes (the oracle's cost does not depend
-    on their values).  The whole step is repeated until about target_s
-    seconds of CPU time have been spent (or, when one step alone is longer, a
-    prefix of the pages is scanned and scaled).  Returns the JSON record."""
+    on their values).  When one step alone is longer than target_s, a prefix
+    of the pages is scanned and the time scaled to all pages.
+
+    The summary build (the oracle's one-sided Jacobi SVD of every page), on a
+    prefix of the pages (all KV heads), with all cores and with one thread,
+    extrapolated per unit to every full page of the layer.  Returns the JSON
+    record."""
     import numpy as np
 
     import oracle
@@ -432,49 +529,80 @@ def cpu_baseline(spec, layer, target_s, threads):
     coef = g.standard_normal((NB, Hkv, P, r), dtype=np.float32)
     full_total = sum(n // P for n in spec.seq_lens)
     kf, vf = layer.k_f32(), layer.v_f32()  # widened once, outside the timed calls
+    lay_full = oracle.Layout(spec.num_q_heads, Hkv, d, P, layer.block_table, layer.seq_lens)
 
-    def step(npages):
+    def step(npages, nthreads):
         """Scan + selection over the first npages full pages of each sequence."""
         seq = np.array([min(n, npages * P) for n in spec.seq_lens], np.int32)
         lay = oracle.Layout(spec.num_q_heads, Hkv, d, P, layer.block_table, seq)
         t0 = time.perf_counter()
-        _, pm = oracle.scan_pool(lay, r, layer.q, mu, basis, coef, threads=threads, heads=False)
+        _, pm = oracle.scan_pool(lay, r, layer.q, mu, basis, coef, threads=nthreads, heads=False)
         t1 = time.perf_counter()
         sel, _ = oracle.select_pool(lay, spec.budget_tokens, pm.astype(np.float32), spec.k_pages)
         t2 = time.perf_counter()
         return t1 - t0, t2 - t1, int(sum(s // P for s in seq)), sel
 
-    lay_full = oracle.Layout(spec.num_q_heads, Hkv, d, P, layer.block_table, layer.seq_lens)
-    npages = max(full_total, 1)
-    scan_s, sel_s, done, sel = step(npages)
-    t0 = time.perf_counter()
-    oracle.attend_pool(lay_full, layer.q, kf, vf, sel, threads=threads)
-    att_s = time.perf_counter() - t0
-    reps = 1
-    if scan_s + sel_s + att_s > target_s:  # one step is already long: scan a prefix
-        npages = max(1, int(npages * target_s / (scan_s + sel_s + att_s)))
-        scan_s, sel_s, done, _ = step(npages)
-        scan_s *= full_total / max(done, 1)
-        sample = f"scan+aggregation+selection over the first {done} of {full_total} full pages " \
-                 f"(x{Hkv} KV heads), scaled to all pages; attention over the selected pages"
-    else:
-        reps = max(1, int(target_s / (scan_s + sel_s + att_s)))
+    def timed_step(nthreads, budget_s, max_reps):
+        npages = max(full_total, 1)
+        scan_s, sel_s, done, sel = step(npages, nthreads)
+        t0 = time.perf_counter()
+        oracle.attend_pool(lay_full, layer.q, kf, vf, sel, threads=nthreads)
+        att_s = time.perf_counter() - t0
+        if scan_s + sel_s + att_s > budget_s:  # one step is already long: scan a prefix
+            npages = max(1, int(npages * budget_s / (scan_s + sel_s + att_s)))
+            scan_s, sel_s, done, _ = step(npages, nthreads)
+            scan_s *= full_total / max(done, 1)
+            return scan_s, sel_s, att_s, (f"scan+aggregation+selection over the first {done} of "
+                                          f"{full_total} full pages (x{Hkv} KV heads), scaled "
+                                          f"to all pages; attention over the selected pages")
+        reps = max(1, min(max_reps, int(budget_s / (scan_s + sel_s + att_s))))
         tot_scan = tot_sel = tot_att = 0.0
         for _ in range(reps):
-            a, s_, _, sel = step(npages)
+            a, s_, _, sel = step(npages, nthreads)
             t0 = time.perf_counter()
-            oracle.attend_pool(lay_full, layer.q, kf, vf, sel, threads=threads)
+            oracle.attend_pool(lay_full, layer.q, kf, vf, sel, threads=nthreads)
             tot_att += time.perf_counter() - t0
             tot_scan += a
             tot_sel += s_
-        scan_s, sel_s, att_s = tot_scan / reps, tot_sel / reps, tot_att / reps
-        sample = f"the full step (scan+aggregation over all {full_total} full pages x{Hkv} KV " \
-                 f"heads, selection, attention over the selected pages), mean of {reps} repeats"
+        return (tot_scan / reps, tot_sel / reps, tot_att / reps,
+                f"the full step (scan+aggregation over all {full_total} full pages x{Hkv} KV "
+                f"heads, selection, attention over the selected pages), mean of {reps} repeats")
+
+    scan_s, sel_s, att_s, sample = timed_step(threads, 0.6 * target_s, 10 ** 6)
     step_s = scan_s + sel_s + att_s
     log(f"cpu oracle: scan {scan_s * 1e3:.1f} ms, select {sel_s * 1e3:.1f} ms, attend "
         f"{att_s * 1e3:.1f} ms -> {step_s * 1e6:.0f} us/step on {threads} threads ({sample})")
+    s1, se1, a1, sample1 = timed_step(1, 0.2 * target_s, 5)
+    step1_s = s1 + se1 + a1
+    log(f"cpu oracle, one thread: {step1_s * 1e6:.0f} us/step ({sample1})")
+
+    # summary build on a prefix of each sequence's pages, every KV head
+    def build_sample(nthreads, npages):
+        seq = np.array([min(n, npages * P) for n in spec.seq_lens], np.int32)
+        lay = oracle.Layout(spec.num_q_heads, Hkv, d, P, layer.block_table, seq)
+        units = int(sum(s_ // P for s_ in seq)) * Hkv
+        t0 = time.perf_counter()
+        oracle.build_pool(lay, r, kf, NB, threads=nthreads)
+        return time.perf_counter() - t0, units
+
+    ball_s, ball_u = build_sample(threads, max(1, 64 * threads // (Hkv * spec.batch)))
+    b1_s, b1_u = build_sample(1, max(1, 48 // (Hkv * spec.batch)))
+    all_units = full_total * Hkv
+    build_all_ms = ball_s / ball_u * all_units * 1e3
+    build_one_ms = b1_s / b1_u * all_units * 1e3
+    log(f"cpu oracle build: {ball_u} units in {ball_s:.2f} s on {threads} threads, {b1_u} units "
+        f"in {b1_s:.2f} s on one thread -> {all_units} units: {build_all_ms / 1e3:.1f} s / "
+        f"{build_one_ms / 1e3:.1f} s (extrapolated per unit)")
     return {"value": round(step_s * 1e6, 1), "unit": "µs/step", "cores": threads,
-            "kind": "oracle", "sample": sample}
+            "kind": "oracle", "sample": sample, "cpu_model": cpu_model(),
+            "one_thread": {"value": round(step1_s * 1e6, 1), "unit": "µs/step", "cores": 1,
+                           "sample": sample1},
+            "build": {"all_cores_ms_extrapolated": round(build_all_ms, 1),
+                      "one_thread_ms_extrapolated": round(build_one_ms, 1),
+                      "units": all_units,
+                      "sample": f"oracle build of {ball_u} units on {threads} threads and "
+                                f"{b1_u} units on one thread (the first pages of each "
+                                f"sequence, every KV head), scaled per unit"}}
 
 
 if __name__ == "__main__":

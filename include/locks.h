@@ -161,7 +161,10 @@ size_t locks_workspace_bytes(int32_t op, int32_t batch, int32_t max_pages, int32
  * coefficients).  Per (page, KV head): mu = mean key; Kc = K - 1 mu^T;
  * the top-r eigenpairs (lambda_k, u_k) of the P x P Gram Kc Kc^T;
  * basis_k = Kc^T u_k / sqrt(lambda_k); coef[i][k] = sqrt(lambda_k) u_k[i].
- * Eigenvalues below 3e-5 * lambda_max give zero basis/coef (numerically null).
+ * Eigenvalues below 3e-6 * lambda_max give zero basis/coef (numerically null).
+ * The top-r rows are then refined by two steps of subspace iteration applied
+ * through Kc (V^T <- Kc^T (Kc V^T), re-orthonormalised), which brings the
+ * rank-r subspace close to the accuracy of an SVD of Kc in fp32.
  * page_begin: device [B] or NULL (= all full pages).  Summaries of other
  * blocks are left untouched.  summaries->rank is r.  Computed in fp32 and
  * stored in out->dtype (bf16: rounded to nearest even; Q8Q4: the fp32
@@ -348,6 +351,33 @@ typedef struct locks_step_graph locks_step_graph;
 locks_status locks_step_graph_create(const locks_step_args* args, locks_step_graph** graph);
 locks_status locks_step_graph_launch(locks_step_graph* graph, void* stream);
 void locks_step_graph_destroy(locks_step_graph* graph);
+
+/*
+ * Measurement probes, not part of the decode step.  They give the summary
+ * scan's HBM roofline two ceilings measured on the same device with the
+ * same build: what a plain streaming read reaches, and what reading exactly
+ * the scan's bytes in the scan's access pattern reaches.
+ *
+ * locks_probe_stream_read: reads the device buffer buf (bytes, a multiple of
+ * 16) once, contiguously, with sink_floats / 4 workgroups of 256 threads
+ * (sink_floats a multiple of 4, 4 .. 262144); writes sink_floats floats of
+ * checksum to the device array sink.
+ *
+ * locks_probe_summary_read: reads what locks_scan reads for fp32 summaries at
+ * P 64, d 128, r 8 (every full page's centroid, basis and coefficients, the
+ * queries, the block table and sequence lengths), with the scan's mapping of
+ * waves to runs of 16 pages of one (b, g) and its load widths and order,
+ * but does none of the scan's arithmetic; writes one float per page to
+ * page_out [B][H_kv][max_pages] (-inf for runs with no full page).  Pages of
+ * a partly full run that are not full read block 0 instead.  Other dtypes or
+ * shapes: LOCKS_ERR_UNSUPPORTED.
+ */
+locks_status locks_probe_stream_read(const void* buf, size_t bytes, float* sink,
+                                     int32_t sink_floats, void* stream);
+locks_status locks_probe_summary_read(const float* q, int32_t num_q_heads,
+                                      const locks_summaries* summaries,
+                                      const locks_page_table* pages, float* page_out,
+                                      void* stream);
 
 const char* locks_status_string(int32_t status);
 int32_t locks_last_hip_error(void);

@@ -32,7 +32,8 @@ EXPORTED = ("locks_workspace_bytes", "locks_build_summaries", "locks_select", "l
             "locks_dense_attend",
             "locks_step_graph_create",
             "locks_step_graph_launch", "locks_step_graph_destroy", "locks_status_string",
-            "locks_last_hip_error", "locks_version")
+            "locks_last_hip_error", "locks_version", "locks_probe_stream_read",
+            "locks_probe_summary_read")
 
 
 class LocksError(RuntimeError):
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.locks_sparse_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, i32, vp, vp,
                                           vp, sz, vp]
         L.locks_dense_attend.argtypes = [vp, i32, P(CKVCache), P(CPageTable), vp, vp, vp, sz, vp]
+        L.locks_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
+        L.locks_probe_summary_read.argtypes = [vp, i32, P(CSummaries), P(CPageTable), vp, vp]
         L.locks_step_graph_create.argtypes = [P(CStepArgs), P(vp)]
         L.locks_step_graph_launch.argtypes = [vp, vp]
         L.locks_step_graph_destroy.argtypes = [vp]
@@ -115,7 +118,8 @@ def lib() -> ctypes.CDLL:
                    "locks_mean_share", "locks_refresh_summaries", "locks_quantize_summaries",
                    "locks_build_sketch_summaries",
                    "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
-                   "locks_step_graph_launch"):
+                   "locks_step_graph_launch", "locks_probe_stream_read",
+                   "locks_probe_summary_read"):
             getattr(L, fn).restype = i32
         _lib = L
     return _lib
@@ -304,6 +308,24 @@ def locks_sparse_attend(q, cache: PagedKV, pages: PageTable, sel_pages, out, out
                                      _ptr(sel_pages), k, _ptr(out), _ptr(out_lse), _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream(stream)),
            "locks_sparse_attend")
+
+
+def locks_probe_stream_read(buf, sink, stream=None):
+    """Measurement probe: one contiguous read of the device tensor buf
+    (its bytes a multiple of 16); sink: float32 device tensor of 4 * blocks
+    checksums (blocks = workgroups of 256 threads)."""
+    assert sink.dtype == torch.float32
+    _check(lib().locks_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                         sink.numel(), _stream(stream)), "locks_probe_stream_read")
+
+
+def locks_probe_summary_read(q, summaries: Summaries, pages: PageTable, page_out, stream=None):
+    """Measurement probe: the fp32 summary scan's reads, in its access
+    pattern, without its arithmetic (page_out [B][H_kv][max_pages] float32)."""
+    sc, pc = summaries.c(), pages.c()
+    _check(lib().locks_probe_summary_read(_ptr(q), q.shape[1], ctypes.byref(sc),
+                                          ctypes.byref(pc), _ptr(page_out), _stream(stream)),
+           "locks_probe_summary_read")
 
 
 def locks_dense_attend(q, cache: PagedKV, pages: PageTable, out, out_lse=None, ws=None,

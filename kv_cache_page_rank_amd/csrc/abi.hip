@@ -519,6 +519,45 @@ void locks_step_graph_destroy(locks_step_graph* graph) {
     delete graph;
 }
 
+locks_status locks_probe_stream_read(const void* buf, size_t bytes, float* sink,
+                                     int32_t sink_floats, void* stream) {
+    if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || sink_floats < 4 ||
+        sink_floats % 4 != 0 || sink_floats / 4 > 65536)
+        return LOCKS_ERR_INVALID_ARG;
+    const hipError_t e = locks::launch_probe_stream(buf, bytes, sink, sink_floats / 4,
+                                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
+locks_status locks_probe_summary_read(const float* q, int32_t num_q_heads,
+                                      const locks_summaries* summaries,
+                                      const locks_page_table* pages, float* page_out,
+                                      void* stream) {
+    locks_status st = check_summaries(summaries, true);
+    if (st != LOCKS_OK) return st;
+    if ((st = check_page_table(pages)) != LOCKS_OK) return st;
+    if (!q || !page_out || !head_dims_ok(num_q_heads, summaries->num_kv_heads))
+        return LOCKS_ERR_INVALID_ARG;
+    if (summaries->dtype != LOCKS_F32 ||
+        !locks::probe_scan_supported(summaries->page_size, summaries->head_dim, summaries->rank))
+        return LOCKS_ERR_UNSUPPORTED;
+    locks::ProbeScanParams p{};
+    p.q = q;
+    p.mu = summaries->mu;
+    p.basis = summaries->basis;
+    p.coef = summaries->coef;
+    p.block_table = pages->block_table;
+    p.seq_lens = pages->seq_lens;
+    p.batch = pages->batch;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = summaries->num_kv_heads;
+    p.max_pages = pages->max_pages;
+    p.num_blocks = summaries->num_blocks;
+    p.page_out = page_out;
+    const hipError_t e = locks::launch_probe_scan(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
+}
+
 const char* locks_status_string(int32_t status) {
     switch (status) {
         case LOCKS_OK:

@@ -117,4 +117,21 @@ struct QuantParams {
 };
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 
+// Measurement probes (not part of the decode step): a streaming read, and a
+// read of the fp32 summary scan's bytes in the scan's access pattern.
+struct ProbeScanParams {
+    const float* q;            // [B][Hq][D]
+    const void* mu;            // fp32 summaries, as ScanParams
+    const void* basis;
+    const void* coef;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int32_t batch, num_q_heads, num_kv_heads, max_pages, num_blocks;
+    float* page_out;           // [B][Hkv][max_pages], one value per page
+};
+hipError_t launch_probe_stream(const void* buf, size_t bytes, float* sink, int32_t blocks,
+                               hipStream_t s);
+hipError_t launch_probe_scan(const ProbeScanParams& p, hipStream_t s);
+bool probe_scan_supported(int page_size, int head_dim, int rank);
+
 }  // namespace locks

@@ -1,0 +1,871 @@
+// Kernel templates of the summary scan, instantiated once per stored
+// summary type by scan_f32.hip, scan_bf16.hip and scan_q8q4.hip (one
+// translation unit each, so they compile in parallel); scan.hip dispatches.
+//
+// Summary scan: per-page estimated attention mass from the resident summary
+// alone (gist.science technical summary, section 2, Reconstructie en
+// Selectie, displayed estimator), aggregated over each GQA group by
+// log-sum-exp (section 2, Group-Shared Selection, read as the sum of the
+// heads' unnormalised masses).
+//
+// For page j of (b, g) and head h of the group, in log2 units with q
+// pre-scaled by log2(e)/sqrt(d):
+//   T[k][h]   = basis_k . q_h                       (MFMA 16x16x4 fp32)
+//   beta[h]   = mu . q_h                            (MFMA, 16 pages per tile)
+//   L[i][h]   = sum_k coef[i][k] T[k][h]            (MFMA 16x16x4 fp32)
+//   s2[h]     = beta[h] + log2 sum_i 2^L[i][h]      (VALU: max, exp2, sum)
+//   a2        = log2 sum_h 2^s2[h]                  (VALU, 16-lane row)
+// and the outputs are s2 * ln 2 and a2 * ln 2.  bf16 and integer-code
+// summaries run the same products on the bf16 matrix cores (below).
+//
+// One wave scans 16 consecutive logical pages of one (b, g).  Its query
+// fragment (16 heads x d; heads >= G load head 0 and scale it by 0) stays in
+// registers.  All loads
+// are 16-byte vector loads; each MFMA operand is taken straight from the
+// loaded registers thanks to the free choice of contraction order:
+// MFMA step s of a tile contracts d = 16*(s/4) + 4*(l/16) + s%4, so lane l
+// loads d-chunks [16t + 4*(l/16), +4) of its row (64 contiguous bytes per
+// row per load instruction).
+// When asked, the wave also writes the largest page mass of its 16 pages
+// (the run maximum the top-k uses to skip runs that cannot hold a winner).
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace locks {
+
+namespace {
+
+constexpr int kBatch = kRunPages;  // pages per wave (one run)
+constexpr int kPrefetch = 1;       // basis tiles in flight ahead of the one computed
+constexpr int kChains = 2;         // independent accumulator chains of an fp32 d contraction
+
+// State of one wave's batch, shared by the two specialisations below.
+template <int D>
+struct WaveCtx {
+    int b, g, j0, G, Hkv, r, lane, w, c;
+    bool head_ok;
+    int my_phys;  // block of page j0 + c (-1: absent)
+    float* out_page;
+    float qf[D / 4];  // query words as loaded (head c, or head 0 for padding heads)
+    float qs;         // scale to log2 units, 0 for padding heads
+};
+
+// Summary element types: fp32, bf16 bit patterns (uint16_t), or int8 / int4
+// codes (int8_t).  E = elements per lane and 32-wide d chunk of the query
+// fragment (16-byte loads for fp32 and bf16; the codes reuse bf16's layout).
+template <typename TS>
+struct Summ {
+    static constexpr int E = 16 / (int)sizeof(TS);
+};
+template <>
+struct Summ<int8_t> {
+    static constexpr int E = 8;
+};
+
+// Address of element `off` of `base`.  kOff32: every summary array is below
+// 4 GiB, so the byte offset is a 32-bit value added to the uniform base (one
+// VALU op per address instead of 64-bit arithmetic).
+template <typename TS, bool kOff32>
+__device__ __forceinline__ const char* elem_addr(const void* base, size_t off) {
+    if constexpr (kOff32)
+        return static_cast<const char*>(base) + (uint32_t)((uint32_t)off * (uint32_t)sizeof(TS));
+    else
+        return static_cast<const char*>(base) + off * sizeof(TS);
+}
+
+// N (1, 2 or 4) consecutive fp32 summary elements starting at element `off`.
+template <bool kOff32, int N>
+__device__ __forceinline__ void load_f32(const void* base, size_t off, float* out) {
+    const char* ptr = elem_addr<float, kOff32>(base, off);
+    if constexpr (N == 1) {
+        out[0] = *reinterpret_cast<const float*>(ptr);
+    } else if constexpr (N == 2) {
+        const f32x2 v = *reinterpret_cast<const f32x2*>(ptr);
+        out[0] = v[0];
+        out[1] = v[1];
+    } else {
+        static_assert(N == 4, "loads of 1, 2 or 4 elements");
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ptr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = v[e];
+    }
+}
+
+// Per-page tail shared by both summary types: lane (w, c) holds the logits of
+// tokens 16 mt + 4w + v for head c (log2 units, beta not yet added) in
+// L[mt][v].  Forms the head's LSE, adds beta, aggregates the group and
+// writes page pb of the batch (row w = pb / 4 holds the right beta).
+template <int D, int MT, bool kHeads, bool kMasked>
+__device__ __forceinline__ void page_mass(const ScanParams& a, const WaveCtx<D>& x,
+                                          const f32x4* L, int pb, const f32x4& beta,
+                                          float& run_mx) {
+    const int w = x.w, c = x.c, g = x.g;
+    const int j = x.j0 + pb;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, L[mt][v]);
+    mx = max_over_rows(mx);
+    float sum = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sum += fast_exp2(L[mt][v] - mx);
+    sum = sum_over_rows(sum);
+    // head h's mass is sum * 2^(mx + beta); beta of page pb sits in row
+    // pb/4, element pb%4, so only that row's values are right
+    const float top = mx + beta[pb & 3];
+    float a2, s2 = 0.0f;
+    if constexpr (kHeads) {
+        s2 = top + fast_log2(sum);
+        const float xv = x.head_ok ? s2 : -INFINITY;
+        const float gm = max_in_row(xv);
+        a2 = gm + fast_log2(sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f));
+    } else {  // the group sum without each head's log: sum_h sum_h 2^(top_h - max top)
+        const float gm = max_in_row(x.head_ok ? top : -INFINITY);
+        a2 = gm + fast_log2(sum_in_row(x.head_ok ? sum * fast_exp2(top - gm) : 0.0f));
+    }
+    if (w == (pb >> 2) && j < a.max_pages) {
+        const bool ok = !kMasked || __builtin_amdgcn_readlane(x.my_phys, pb) >= 0;
+        const float mass = ok ? a2 * kLn2 : -INFINITY;
+        run_mx = fmaxf(run_mx, mass);
+        if (c == 0) x.out_page[j] = mass;
+        if constexpr (kHeads) {
+            if (x.head_ok)
+                a.head_logmass[((size_t)x.b * a.num_q_heads + g * x.G + c) * a.max_pages + j] =
+                    ok ? s2 * kLn2 : -INFINITY;
+        }
+    }
+}
+
+// The query words, passed through empty asm statements that clobber memory:
+// they stay after every load issued before them, and the query's arithmetic
+// stays after them, so a wave's first summary loads go out before it waits
+// for its query.
+template <int N>
+__device__ __forceinline__ void query_after_loads(const float* qf, float* qv) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        qv[i] = qf[i];
+        asm volatile("" : "+v"(qv[i])::"memory");
+    }
+}
+// The same for loaded summary words that are used before the first tile.
+template <typename T>
+__device__ __forceinline__ void after_loads(T& v) {
+    asm volatile("" : "+v"(v)::"memory");
+}
+
+// One wave's batch of kBatch pages.  kMasked: some page of the batch is
+// absent or the rank is padded, so loads are zeroed per row; otherwise no
+// masking code is emitted.  kHeads: per-head masses are written too.
+// fp32 summaries: the word layout keeps the fp32 loads 64 contiguous bytes
+// per row; the contraction order of the MFMA steps is chosen to match it.
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
+__device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCtx<D>& x) {
+    using TS = float;
+    constexpr int PPT = 16 / RR;          // pages per basis tile (16 rows = PPT pages x RR rows)
+    constexpr int NTILE = kBatch / PPT;   // basis tiles per batch
+    constexpr int KS2 = RR / 4;           // K-steps of the coefficient product
+    constexpr int MT = P / 16;            // token tiles per page
+    constexpr int DS = D / 4;             // words of a row held per lane
+    constexpr int E = Summ<TS>::E;        // elements per 16-byte load
+    constexpr int NCH = D / (4 * E);      // 16-byte loads per row and lane
+    constexpr int PF = kPrefetch;
+    using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
+    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
+    const int my_phys = x.my_phys;
+    auto phys_at = [&](int pb) { return __shfl(my_phys, pb, kWave); };
+    auto phys_uniform = [&](int pb) { return __builtin_amdgcn_readlane(my_phys, pb); };
+
+    // The query in fp32, word s of lane (w, c) at d = 16 (s/4) + 4w + s%4
+    // (the fp32 load layout): MFMA step s contracts these 4 d's.  Scaled once
+    // the first tile's and the centroids' loads are issued (scaling waits for
+    // the query's loads; the summary loads need not).
+    float qv[DS];
+    auto prepare_q = [&]() {
+        query_after_loads<DS>(x.qf, qv);
+#pragma unroll
+        for (int i = 0; i < DS; ++i) qv[i] *= x.qs;
+    };
+    // (rows of A) . q for the lane's DS words: 16x16x4 fp32 steps in
+    // kChains independent accumulator chains
+    auto dot_q = [&](const uint32_t* words) {
+        f32x4 acc[kChains];
+#pragma unroll
+        for (int i = 0; i < kChains; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < DS; ++st)
+            acc[st % kChains] = mfma_16x16x4_f32(__uint_as_float(words[st]), qv[st], acc[st % kChains]);
+        f32x4 T = acc[0];
+#pragma unroll
+        for (int i = 1; i < kChains; ++i) T += acc[i];
+        return T;
+    };
+
+    // Basis-tile row assignment for the loading lane (row m = c):
+    //   page-in-tile p = (m%4) / KS2, k-step ks = (m%4) % KS2, basis row kk = KS2*(m/4) + ks.
+    // After the MFMA, lane (w, c) element v holds T[page v/KS2][KS2*w + v%KS2][head c],
+    // which is exactly its B operand for k-step v%KS2 of page v/KS2.
+    const int a_pin = (c & 3) / KS2;
+    const int a_kk = KS2 * (c >> 2) + ((c & 3) % KS2);
+
+    // A tile keeps the loaded words as they are and reinterprets them where
+    // the MFMAs consume them, so the waits for a tile's loads fall at its use.
+    constexpr int CFW = KS2;  // words per coefficient chunk
+    struct Tile {
+        uint32_t v[DS];
+        uint32_t cf[PPT][MT][CFW];
+    };
+    auto widen = [](const uint32_t* words, int i) -> float { return __uint_as_float(words[i]); };
+    // Loads are unconditional (absent rows read a clamped, valid address and
+    // are zeroed afterwards) so that the next tile's loads stay in flight
+    // while the current tile is computed.
+    auto load_tile = [&](int tt, Tile& T) {
+        const int pj = phys_at(tt * PPT + a_pin);
+        const bool row_ok = !kMasked || (pj >= 0 && a_kk < r);
+        const Off src = (((Off)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
+                         (kMasked && a_kk >= r ? r - 1 : a_kk)) * D + E * w;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(elem_addr<TS, kOff32>(a.basis, src + 4 * E * t));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) T.v[4 * t + e] = row_ok ? v[e] : 0u;
+        }
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int pp = phys_uniform(tt * PPT + p);
+            const bool ok = !kMasked || pp >= 0;
+            const Off csrc = ((Off)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const Off row = csrc + (Off)(16 * mt + c) * r;
+                if (kExact || KS2 == 1) {
+                    // KS2 consecutive elements k = KS2 w .. (rank not padded), or the
+                    // single element k = w clamped to the rank and zeroed past it
+                    const int k0 = kExact ? KS2 * w : (w < r ? w : r - 1);
+                    const bool kok = kExact || w < r;
+                    const char* ptr = elem_addr<TS, kOff32>(a.coef, row + k0);
+                    if constexpr (CFW == 1) {
+                        const uint32_t word = *reinterpret_cast<const uint32_t*>(ptr);
+                        T.cf[p][mt][0] = (ok && kok) ? word : 0u;
+                    } else if constexpr (CFW == 2) {
+                        const u32x2 v = *reinterpret_cast<const u32x2*>(ptr);
+                        T.cf[p][mt][0] = ok ? v[0] : 0u;
+                        T.cf[p][mt][1] = ok ? v[1] : 0u;
+                    } else {
+                        const u32x4 v = *reinterpret_cast<const u32x4*>(ptr);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) T.cf[p][mt][e] = ok ? v[e] : 0u;
+                    }
+                } else {
+                    // padded rank with KS2 > 1: element by element, clamped and
+                    // zeroed past the rank
+#pragma unroll
+                    for (int e = 0; e < CFW; ++e) T.cf[p][mt][e] = 0u;
+#pragma unroll
+                    for (int ks = 0; ks < KS2; ++ks) {
+                        const int kk = KS2 * w + ks;
+                        const char* ptr = elem_addr<TS, kOff32>(a.coef, row + (kk < r ? kk : r - 1));
+                        const uint32_t word = *reinterpret_cast<const uint32_t*>(ptr);
+                        T.cf[p][mt][ks] = (ok && kk < r) ? word : 0u;
+                    }
+                }
+            }
+        }
+    };
+    // coefficient element ks of chunk (p, mt)
+    auto coef_el = [&](const Tile& tl, int p, int mt, int ks) -> float {
+        return widen(tl.cf[p][mt], ks);
+    };
+
+    // ring of tiles: the loads of tiles tt+1 .. tt+PF are in flight while
+    // tile tt is computed
+    Tile ring[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF && i < NTILE; ++i) load_tile(i, ring[i]);
+
+    // beta tile: A row m = page j0 + m (lane column c supplies row c).
+    f32x4 beta;
+    {
+        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + E * w;
+        uint32_t mv[DS];
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            float v[E];
+            load_f32<kOff32, E>(a.mu, src + 4 * E * t, v);
+#pragma unroll
+            for (int e = 0; e < E; ++e) mv[E * t + e] = __float_as_uint(v[e]);
+        }
+#pragma unroll
+        for (int i = 0; i < DS; ++i) {
+            after_loads(mv[i]);
+            mv[i] = (!kMasked || my_phys >= 0) ? mv[i] : 0u;
+        }
+        prepare_q();
+        beta = dot_q(mv);
+    }
+    // lane (w, c) now holds beta[page j0 + 4w + v][head c] in element v.
+
+    float run_mx = -INFINITY;  // max of the written page masses (row w holds pages 4w..4w+3)
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) {
+        if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
+        const Tile& cur = ring[tt % (PF + 1)];
+        const f32x4 Tcur = dot_q(cur.v);
+        // coefficient product in fp32 (8 accumulating 16x16x4 steps per page at
+        // rank 8): lane (w, c) element v holds T[page v/KS2][KS2 w + v%KS2][head c],
+        // its B operand for k-step v%KS2 of page v/KS2
+        f32x4 L[PPT][MT];
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                L[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS2; ++ks)
+                    L[p][mt] = mfma_16x16x4_f32(coef_el(cur, p, mt, ks), Tcur[p * KS2 + ks], L[p][mt]);
+            }
+
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], tt * PPT + p, beta, run_mx);
+    }
+    if (a.run_max) {
+        run_mx = max_over_rows(run_mx);
+        const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
+        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
+    }
+}
+
+// bf16 summaries on the bf16 matrix cores, to fp32 accuracy: the stored
+// values are bf16 already, and each fp32 multiplicand (q, and the basis
+// product T) is split into three bf16 parts hi + mid + lo whose sum is the
+// value (24 significant bits); every product is exact and accumulates in
+// fp32.  Per tile of 16 basis rows (row m = basis row m % RR of page m / RR):
+//   T (16 rows x 16 heads)   = basis rows . q^T   v_mfma_f32_16x16x32_bf16 x 3 parts per 32 d
+//   L (16 tokens x 16 heads) = coef . T           v_mfma_f32_16x16x16_bf16 x 3 parts
+// The coefficient operand of page p is zero outside p's rows of the tile.
+__device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
+    h = (__bf16)x;
+    float rest = x - (float)h;
+    m = (__bf16)rest;
+    rest -= (float)m;
+    l = (__bf16)rest;
+}
+
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
+__device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveCtx<D>& x) {
+    using TS = uint16_t;
+    constexpr int PPT = 16 / RR;          // pages per tile
+    constexpr int NTILE = kBatch / PPT;
+    constexpr int MT = P / 16;            // token tiles per page
+    constexpr int NCH = D / 32;           // 32-wide d chunks (one 16-byte load per lane each)
+    constexpr int WPP = RR / 4;           // lane groups per page in the coefficient operand
+    constexpr int PF = kPrefetch;
+    using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
+    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
+    const int my_phys = x.my_phys;
+
+    // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e.
+    // Split after the first tile's and the centroids' loads are issued.
+    bf16x8 qp[3][NCH];
+    auto split_q = [&]() {
+        float qv[D / 4];
+        query_after_loads<D / 4>(x.qf, qv);
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 h, m, l;
+                split3(qv[8 * t + e] * x.qs, h, m, l);
+                qp[0][t][e] = h;
+                qp[1][t][e] = m;
+                qp[2][t][e] = l;
+            }
+    };
+
+    const int a_pin = c / RR, a_k = c % RR;   // basis row loaded by this lane
+    const int c_pin = w / WPP;                // page whose coefficients this lane supplies
+    const int c_k0 = 4 * (w % WPP);           // its first coefficient index
+    struct Tile {
+        u32x4 v[NCH];
+        u32x2 cf[MT];
+    };
+    auto load_tile = [&](int tt, Tile& T) {
+        const int pj = __shfl(my_phys, tt * PPT + a_pin, kWave);
+        const bool row_ok = !kMasked || (pj >= 0 && a_k < r);
+        const Off src = (((Off)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
+                         (kMasked && a_k >= r ? r - 1 : a_k)) * D + 8 * w;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(elem_addr<TS, kOff32>(a.basis, src + 32 * t));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) T.v[t][e] = row_ok ? v[e] : 0u;
+        }
+        const int pp = __shfl(my_phys, tt * PPT + c_pin, kWave);
+        const bool ok = !kMasked || pp >= 0;
+        const Off csrc = ((Off)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const Off row = csrc + (Off)(16 * mt + c) * r;
+            if constexpr (kExact) {
+                const u32x2 v = *reinterpret_cast<const u32x2*>(elem_addr<TS, kOff32>(a.coef, row + c_k0));
+                T.cf[mt][0] = ok ? v[0] : 0u;
+                T.cf[mt][1] = ok ? v[1] : 0u;
+            } else {  // padded rank: element by element, clamped and zeroed past it
+                uint32_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kk = c_k0 + e;
+                    const uint32_t h = *reinterpret_cast<const uint16_t*>(
+                        elem_addr<TS, kOff32>(a.coef, row + (kk < r ? kk : r - 1)));
+                    hv[e] = (ok && kk < r) ? h : 0u;
+                }
+                T.cf[mt][0] = hv[0] | (hv[1] << 16);
+                T.cf[mt][1] = hv[2] | (hv[3] << 16);
+            }
+        }
+    };
+
+    Tile ring[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF && i < NTILE; ++i) load_tile(i, ring[i]);
+
+    // beta tile: A row m = page j0 + m (lane column c supplies row c).
+    f32x4 beta;
+    {
+        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + 8 * w;
+        f32x4 bacc[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) bacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 mv[NCH];
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            mv[t] = *reinterpret_cast<const u32x4*>(elem_addr<TS, kOff32>(a.mu, src + 32 * t));
+        }
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            after_loads(mv[t]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mv[t][e] = (!kMasked || my_phys >= 0) ? mv[t][e] : 0u;
+        }
+        split_q();
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) bacc[i] = mfma_16x16x32_bf16(as_bf16x8(mv[t]), qp[i][t], bacc[i]);
+        beta = bacc[0] + bacc[1] + bacc[2];
+    }
+
+    float run_mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) {
+        if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
+        const Tile& cur = ring[tt % (PF + 1)];
+        f32x4 tacc[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) tacc[i] = mfma_16x16x32_bf16(as_bf16x8(cur.v[t]), qp[i][t], tacc[i]);
+        const f32x4 T = tacc[0] + tacc[1] + tacc[2];
+        // lane (w, c) holds T[tile row 4w + v][head c]: its B operand rows of the
+        // coefficient product, split into three bf16 parts
+        bf16x4 tp[3];
+        {
+            __bf16 hv[4], mv[4], lv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) split3(T[v], hv[v], mv[v], lv[v]);
+            typedef __bf16 bf16v4 __attribute__((ext_vector_type(4)));
+            tp[0] = __builtin_bit_cast(bf16x4, bf16v4{hv[0], hv[1], hv[2], hv[3]});
+            tp[1] = __builtin_bit_cast(bf16x4, bf16v4{mv[0], mv[1], mv[2], mv[3]});
+            tp[2] = __builtin_bit_cast(bf16x4, bf16v4{lv[0], lv[1], lv[2], lv[3]});
+        }
+        f32x4 L[PPT][MT];
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const bool mine = c_pin == p;
+                const u32x2 av = {mine ? cur.cf[mt][0] : 0u, mine ? cur.cf[mt][1] : 0u};
+                const bf16x4 A = as_bf16x4(av);
+                f32x4 acc = mfma_16x16x16_bf16(A, tp[0], f32x4{0.f, 0.f, 0.f, 0.f});
+                acc = mfma_16x16x16_bf16(A, tp[1], acc);
+                L[p][mt] = mfma_16x16x16_bf16(A, tp[2], acc);
+            }
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], tt * PPT + p, beta, run_mx);
+    }
+    if (a.run_max) {
+        run_mx = max_over_rows(run_mx);
+        const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
+        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
+    }
+}
+
+// Integer codes widened to bf16: small integers are exact in bf16, so the
+// bf16 MFMA products of the codes with the split query stay exact; the
+// scales are applied in fp32 to the accumulated sums.  The codes are read
+// as unsigned fields with the sign bit flipped (excess-8 / excess-128) and
+// the bias subtracted in float, which is exact: a sign-extending field
+// extract followed by an int-to-float convert is folded by this compiler into
+// an unsigned convert of the sign-extended value, wrong for negative codes.
+// 8 int4 codes (element e in bits 4e..4e+3) -> 8 bf16, pairs packed low first.
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+__device__ __forceinline__ u32x4 widen_i4x8(uint32_t w) {
+    const uint32_t u = w ^ 0x88888888u;  // two's complement -> excess-8
+    u32x4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float lo = (float)((u >> (8 * p)) & 15u) - 8.f;
+        const float hi = (float)((u >> (8 * p + 4)) & 15u) - 8.f;
+        o[p] = bf16_pair(lo, hi);
+    }
+    return o;
+}
+// 4 int8 codes (element e in byte e) -> 4 bf16.
+__device__ __forceinline__ u32x2 widen_i8x4(uint32_t w) {
+    const uint32_t u = w ^ 0x80808080u;  // two's complement -> excess-128
+    u32x2 o;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const float lo = (float)((u >> (16 * p)) & 255u) - 128.f;
+        const float hi = (float)((u >> (16 * p + 8)) & 255u) - 128.f;
+        o[p] = bf16_pair(lo, hi);
+    }
+    return o;
+}
+
+// One batch of kBatch pages with int8 / int4 summaries: the bf16 scan's
+// operand layout and MFMAs on the widened codes.  With codes m (centroid),
+// v (basis), c (coefficients) and scales s_mu, s_v[k], s_c[k]:
+//   beta = s_mu (m . q),   t_k = s_v[k] s_c[k] (v_k . q),   logit_i = beta + sum_k c_ik t_k,
+// the same estimator on the dequantised summary (scale * code).
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
+__device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<D>& x) {
+    constexpr int PPT = 16 / RR;          // pages per tile
+    constexpr int NTILE = kBatch / PPT;
+    constexpr int MT = P / 16;            // token tiles per page
+    constexpr int NCH = D / 32;           // 32-wide d chunks
+    constexpr int WPP = RR / 4;           // lane groups per page in the coefficient operand
+    constexpr int PF = kPrefetch;
+    using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
+    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
+    const int my_phys = x.my_phys;
+    const int SC = 1 + 2 * r;             // scales per unit
+    const uint8_t* const mu_q = static_cast<const uint8_t*>(a.mu);
+    const uint8_t* const basis_q = static_cast<const uint8_t*>(a.basis);
+    const uint8_t* const coef_q = static_cast<const uint8_t*>(a.coef);
+
+    // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e.
+    // Split after the first tile's and the centroids' loads are issued.
+    bf16x8 qp[3][NCH];
+    auto split_q = [&]() {
+        float qv[D / 4];
+        query_after_loads<D / 4>(x.qf, qv);
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 h, m, l;
+                split3(qv[8 * t + e] * x.qs, h, m, l);
+                qp[0][t][e] = h;
+                qp[1][t][e] = m;
+                qp[2][t][e] = l;
+            }
+    };
+
+    const int a_pin = c / RR, a_k = c % RR;   // basis row loaded by this lane
+    const int c_pin = w / WPP;                // page whose coefficients this lane supplies
+    const int c_k0 = 4 * (w % WPP);           // its first coefficient index
+    const int s_pin = (4 * w) / RR;           // page of the T rows 4w..4w+3 this lane holds
+    const int s_k0 = (4 * w) % RR;            // their first basis index
+    struct Tile {
+        uint32_t v[NCH];   // 8 int4 codes per chunk
+        uint32_t cf[MT];   // 4 int8 codes per token tile
+        float sc[4];       // s_v[k] s_c[k] of the lane's four T rows
+    };
+    auto load_tile = [&](int tt, Tile& T) {
+        const int pj = __shfl(my_phys, tt * PPT + a_pin, kWave);
+        const bool row_ok = !kMasked || (pj >= 0 && a_k < r);
+        const Off src = (((Off)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
+                         (kMasked && a_k >= r ? r - 1 : a_k)) * (D / 2) + 4 * w;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(basis_q + src + 16 * t);
+            T.v[t] = row_ok ? v : 0u;
+        }
+        const int pp = __shfl(my_phys, tt * PPT + c_pin, kWave);
+        const bool ok = !kMasked || pp >= 0;
+        const Off csrc = ((Off)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const Off row = csrc + (Off)(16 * mt + c) * r;
+            if constexpr (kExact) {
+                const uint32_t v = *reinterpret_cast<const uint32_t*>(coef_q + row + c_k0);
+                T.cf[mt] = ok ? v : 0u;
+            } else {  // padded rank: byte by byte, clamped and zeroed past it
+                uint32_t hv = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kk = c_k0 + e;
+                    const uint32_t b = coef_q[row + (kk < r ? kk : r - 1)];
+                    hv |= ((ok && kk < r) ? b : 0u) << (8 * e);
+                }
+                T.cf[mt] = hv;
+            }
+        }
+        const int ps = __shfl(my_phys, tt * PPT + s_pin, kWave);
+        const float* sp = a.scales + ((size_t)(kMasked && ps < 0 ? 0 : ps) * Hkv + g) * SC;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int k = s_k0 + v;
+            const bool kok = (!kMasked || ps >= 0) && (kExact || k < r);
+            const int kc = kExact || k < r ? k : r - 1;
+            T.sc[v] = kok ? sp[1 + kc] * sp[1 + r + kc] : 0.f;
+        }
+    };
+
+    Tile ring[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF && i < NTILE; ++i) load_tile(i, ring[i]);
+
+    // beta tile: A row m = page j0 + m (lane column c supplies row c).
+    f32x4 beta;
+    {
+        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + 8 * w;
+        f32x4 bacc[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) bacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x2 m8[NCH];
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            m8[t] = *reinterpret_cast<const u32x2*>(mu_q + src + 32 * t);
+        }
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            after_loads(m8[t]);
+            if (kMasked && my_phys < 0) m8[t] = u32x2{0u, 0u};
+        }
+        split_q();
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const u32x2 lo = widen_i8x4(m8[t][0]), hi = widen_i8x4(m8[t][1]);
+            const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int i = 0; i < 3; ++i) bacc[i] = mfma_16x16x32_bf16(as_bf16x8(v), qp[i][t], bacc[i]);
+        }
+        beta = bacc[0] + bacc[1] + bacc[2];
+        // rows 4w + v are pages j0 + 4w + v: their centroid scales
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int pv = __shfl(my_phys, 4 * w + v, kWave);
+            const float sm = a.scales[((size_t)(pv < 0 ? 0 : pv) * Hkv + g) * SC];
+            beta[v] *= pv < 0 ? 0.f : sm;
+        }
+    }
+
+    float run_mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) {
+        if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
+        const Tile& cur = ring[tt % (PF + 1)];
+        f32x4 tacc[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const bf16x8 vb = as_bf16x8(widen_i4x8(cur.v[t]));
+#pragma unroll
+            for (int i = 0; i < 3; ++i) tacc[i] = mfma_16x16x32_bf16(vb, qp[i][t], tacc[i]);
+        }
+        f32x4 T = tacc[0] + tacc[1] + tacc[2];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) T[v] *= cur.sc[v];
+        // lane (w, c) holds T[tile row 4w + v][head c]: its B operand rows of the
+        // coefficient product, split into three bf16 parts
+        bf16x4 tp[3];
+        {
+            __bf16 hv[4], mv[4], lv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) split3(T[v], hv[v], mv[v], lv[v]);
+            typedef __bf16 bf16v4 __attribute__((ext_vector_type(4)));
+            tp[0] = __builtin_bit_cast(bf16x4, bf16v4{hv[0], hv[1], hv[2], hv[3]});
+            tp[1] = __builtin_bit_cast(bf16x4, bf16v4{mv[0], mv[1], mv[2], mv[3]});
+            tp[2] = __builtin_bit_cast(bf16x4, bf16v4{lv[0], lv[1], lv[2], lv[3]});
+        }
+        f32x4 L[PPT][MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const bf16x4 cw = as_bf16x4(widen_i8x4(cur.cf[mt]));
+#pragma unroll
+            for (int p = 0; p < PPT; ++p) {
+                const bf16x4 A = c_pin == p ? cw : bf16x4{0, 0, 0, 0};
+                f32x4 acc = mfma_16x16x16_bf16(A, tp[0], f32x4{0.f, 0.f, 0.f, 0.f});
+                acc = mfma_16x16x16_bf16(A, tp[1], acc);
+                L[p][mt] = mfma_16x16x16_bf16(A, tp[2], acc);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], tt * PPT + p, beta, run_mx);
+    }
+    if (a.run_max) {
+        run_mx = max_over_rows(run_mx);
+        const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
+        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
+    }
+}
+
+template <typename TS, int P, int D, int RR, bool kExact, bool kHeads, bool kOff32>
+__global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
+    static_assert(P % 16 == 0 && D % 32 == 0, "P a multiple of 16, d of 32");
+    static_assert(RR == 4 || RR == 8 || RR == 16, "padded rank");
+    constexpr int E = Summ<TS>::E;
+    constexpr int NCH = D / (4 * E);
+
+    WaveCtx<D> x;
+    x.lane = threadIdx.x & 63;
+    x.w = x.lane >> 4;
+    x.c = x.lane & 15;
+    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nbatch = (a.max_pages + kBatch - 1) / kBatch;
+    if (wave >= a.batch * a.num_kv_heads * nbatch) return;
+    const int jb = wave % nbatch;
+    x.g = (wave / nbatch) % a.num_kv_heads;
+    x.b = wave / (nbatch * a.num_kv_heads);
+    x.Hkv = a.num_kv_heads;
+    x.G = a.num_q_heads / x.Hkv;
+    x.r = a.rank;
+    x.head_ok = x.c < x.G;
+    x.j0 = jb * kBatch;
+    const int c = x.c, w = x.w;
+
+    // The block-table entry of page j0 + c is read together with the
+    // sequence length (clamped index, kept only if the page is full), so the
+    // two loads overlap instead of following each other.
+    const int jc = x.j0 + (c < kBatch ? c : 0);
+    const int p_spec =
+        a.block_table[(size_t)x.b * a.max_pages + (jc < a.max_pages ? jc : a.max_pages - 1)];
+    int full = a.seq_lens[x.b] / P;
+    full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
+    x.out_page = a.page_logmass + ((size_t)x.b * x.Hkv + x.g) * a.max_pages;
+    if (x.j0 >= full) {  // whole batch past the full pages
+        if (a.run_max && x.lane == 0)
+            a.run_max[((size_t)x.b * x.Hkv + x.g) * nbatch + jb] = -INFINITY;
+        if (w == 0 && c < kBatch && x.j0 + c < a.max_pages) {
+            x.out_page[x.j0 + c] = -INFINITY;
+            if constexpr (kHeads)
+                for (int hh = 0; hh < x.G; ++hh)
+                    a.head_logmass[((size_t)x.b * a.num_q_heads + x.g * x.G + hh) * a.max_pages +
+                                   x.j0 + c] = -INFINITY;
+        }
+        return;
+    }
+    x.my_phys =
+        (c < kBatch && x.j0 + c < full && p_spec >= 0 && p_spec < a.num_blocks) ? p_spec : -1;
+
+    // Query fragment, in the contraction order of the summary loads:
+    // qf[E t + e] = q[h][4E t + E w + e] for head h = c, as loaded; the batch
+    // functions scale it to log2 units (qs, 0 for padding heads) when they
+    // split it, after their first summary loads are issued.
+    x.qs = x.head_ok ? kLog2e / sqrtf((float)D) : 0.0f;
+    {
+        const float* qp =
+            a.q + ((size_t)x.b * a.num_q_heads + x.g * x.G + (x.head_ok ? c : 0)) * D;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int h4 = 0; h4 < E / 4; ++h4) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(qp + 4 * E * t + E * w + 4 * h4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x.qf[E * t + 4 * h4 + e] = v[e];
+            }
+    }
+
+    // every page of the batch present and the rank not padded: no masking
+    if constexpr (kExact) {
+        if (x.j0 + kBatch <= full && __ballot(c < kBatch && x.my_phys < 0) == 0ull) {
+            if constexpr (sizeof(TS) == 1)
+                scan_batch_q<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
+            else if constexpr (sizeof(TS) == 2)
+                scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
+            else
+                scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
+            return;
+        }
+    }
+    if constexpr (sizeof(TS) == 1)
+        scan_batch_q<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
+    else if constexpr (sizeof(TS) == 2)
+        scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
+    else
+        scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
+}
+
+template <typename TS, int P, int D, int RR, bool kHeads, bool kOff32>
+hipError_t launch4(const ScanParams& p, hipStream_t s, unsigned blocks) {
+    if (p.rank == RR)
+        hipLaunchKernelGGL((scan_kernel<TS, P, D, RR, true, kHeads, kOff32>), dim3(blocks),
+                           dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((scan_kernel<TS, P, D, RR, false, kHeads, kOff32>), dim3(blocks),
+                           dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename TS, int P, int D, int RR>
+hipError_t launch_ts(const ScanParams& p, hipStream_t s, unsigned blocks) {
+    // largest summary array (basis or coefficients) in bytes
+    size_t per_unit = (size_t)p.rank * (D > P ? D : P) * sizeof(TS);
+    if (sizeof(TS) == 1) {  // codes: centroid D, basis r D/2, coefficients P r bytes
+        per_unit = (size_t)p.rank * (D / 2 > P ? D / 2 : P);
+        per_unit = per_unit > (size_t)D ? per_unit : (size_t)D;
+    }
+    const bool off32 = (size_t)p.num_blocks * p.num_kv_heads * per_unit < (size_t(1) << 32);
+    if (p.head_logmass != nullptr)
+        return off32 ? launch4<TS, P, D, RR, true, true>(p, s, blocks)
+                     : launch4<TS, P, D, RR, true, false>(p, s, blocks);
+    return off32 ? launch4<TS, P, D, RR, false, true>(p, s, blocks)
+                 : launch4<TS, P, D, RR, false, false>(p, s, blocks);
+}
+
+
+template <typename TS, int P, int D, int RR>
+hipError_t launch_typed(const ScanParams& p, hipStream_t s) {
+    const long waves = (long)p.batch * p.num_kv_heads * ((p.max_pages + kBatch - 1) / kBatch);
+    const unsigned blocks = (unsigned)((waves + 3) / 4);
+    if (blocks == 0) return hipSuccess;
+    return launch_ts<TS, P, D, RR>(p, s, blocks);
+}
+
+template <typename TS, int P, int D>
+hipError_t launch_rr(const ScanParams& p, hipStream_t s) {
+    if (p.rank <= 4) return launch_typed<TS, P, D, 4>(p, s);
+    if (p.rank <= 8) return launch_typed<TS, P, D, 8>(p, s);
+    return launch_typed<TS, P, D, 16>(p, s);
+}
+
+// Every supported (page size, head dim) for one stored summary type.
+template <typename TS>
+hipError_t launch_scan_of(const ScanParams& p, hipStream_t s) {
+    if (p.page_size == 16 && p.head_dim == 64) return launch_rr<TS, 16, 64>(p, s);
+    if (p.page_size == 16 && p.head_dim == 128) return launch_rr<TS, 16, 128>(p, s);
+    if (p.page_size == 64 && p.head_dim == 64) return launch_rr<TS, 64, 64>(p, s);
+    return launch_rr<TS, 64, 128>(p, s);
+}
+
+}  // namespace
+
+}  // namespace locks

@@ -149,6 +149,18 @@ def test_host_validation_rejects_without_launch(lk):
     # sparse attend with pages requested but no list
     assert lib.locks_sparse_attend(p, 32, by(kv), by(pt), None, 4, p, None, p, 1 << 30, None) == \
         lk.LOCKS_ERR_INVALID_ARG
+    # measurement probes: sizes and shapes checked on the host
+    assert lib.locks_probe_stream_read(p, 1000, p, 64, None) == lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_probe_stream_read(p, 1024, p, 6, None) == lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_probe_stream_read(p, 1024, p, 4 * 65537, None) == lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_probe_stream_read(None, 1024, p, 64, None) == lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_probe_summary_read(p, 32, by(sm_bf), by(pt), p, None) == \
+        lk.LOCKS_ERR_UNSUPPORTED
+    _, sm_r4, _, _ = _fake(lk, r=4)
+    assert lib.locks_probe_summary_read(p, 32, by(sm_r4), by(pt), p, None) == \
+        lk.LOCKS_ERR_UNSUPPORTED
+    assert lib.locks_probe_summary_read(p, 32, by(sm), by(pt), None, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
     # graph creation validates before capturing
     h = ctypes.c_void_p()
     assert lib.locks_step_graph_create(None, by(h)) == lk.LOCKS_ERR_INVALID_ARG
