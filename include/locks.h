@@ -248,6 +248,28 @@ locks_status locks_select(const float* q, int32_t num_q_heads, const locks_summa
                           size_t ws_bytes, void* stream);
 
 /*
+ * locks_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and rules as
+ * locks_select; the selection workspace (page masses unless page_logmass is
+ * given, run maxima, per-head estimates and totals) lives in a static device
+ * array of 16 MiB that the library holds on each device it runs on until the
+ * process ends.  Shapes whose workspace,
+ * locks_workspace_bytes(LOCKS_OP_SELECT, ...), exceeds 16 MiB return
+ * LOCKS_ERR_WORKSPACE and launch nothing (for example B * max_pages *
+ * (H_kv + H_q) floats above ~4M).  Allocates nothing: no hipMalloc, no
+ * hipFree.  The first call on a device looks up that device's array
+ * (hipGetSymbolAddress); make it before any stream capture.  Every call on
+ * one device shares that device's array, which keeps the last call's
+ * contents: calls that overlap on one device (concurrent streams, or
+ * threads) race and give undefined results.
+ */
+locks_status locks_select_noalloc(const float* q, int32_t num_q_heads,
+                                  const locks_summaries* summaries, const locks_page_table* pages,
+                                  int32_t budget_tokens, int32_t agg, int32_t* sel_pages,
+                                  float* sel_logmass, float* page_logmass, void* stream);
+
+/*
  * Step 2 alone: the page masses without selection (same definitions as
  * locks_select).  page_logmass [B][H_kv][max_pages] is required;
  * head_logmass [B][H_q][max_pages] (per-head s_hat) is optional.

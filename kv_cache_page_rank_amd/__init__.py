@@ -33,7 +33,7 @@ EXPORTED = ("locks_workspace_bytes", "locks_build_summaries", "locks_select", "l
             "locks_step_graph_create",
             "locks_step_graph_launch", "locks_step_graph_destroy", "locks_status_string",
             "locks_last_hip_error", "locks_version", "locks_probe_stream_read",
-            "locks_probe_summary_read")
+            "locks_probe_summary_read", "locks_select_noalloc")
 
 
 class LocksError(RuntimeError):
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
                                             vp]
         L.locks_select.argtypes = [vp, i32, P(CSummaries), P(CPageTable), i32, i32, vp, vp, vp,
                                    vp, sz, vp]
+        L.locks_select_noalloc.argtypes = [vp, i32, P(CSummaries), P(CPageTable), i32, i32, vp,
+                                           vp, vp, vp]
         L.locks_mean_share.argtypes = [vp, i32, i32, P(CPageTable), i32, vp, vp, vp, sz, vp]
         L.locks_refresh_summaries.argtypes = [P(CKVCache), P(CPageTable), vp, i32, P(CSummaries),
                                               vp]
@@ -119,7 +121,7 @@ def lib() -> ctypes.CDLL:
                    "locks_build_sketch_summaries",
                    "locks_sparse_attend", "locks_dense_attend", "locks_step_graph_create",
                    "locks_step_graph_launch", "locks_probe_stream_read",
-                   "locks_probe_summary_read"):
+                   "locks_probe_summary_read", "locks_select_noalloc"):
             getattr(L, fn).restype = i32
         _lib = L
     return _lib
@@ -262,6 +264,18 @@ def locks_select(q, summaries: Summaries, pages: PageTable, budget_tokens, sel_p
                               budget_tokens, agg, _ptr(sel_pages), _ptr(sel_logmass),
                               _ptr(page_logmass), _ptr(ws), 0 if ws is None else ws.numel(),
                               _stream(stream)), "locks_select")
+
+
+def locks_select_noalloc(q, summaries: Summaries, pages: PageTable, budget_tokens, sel_pages,
+                         sel_logmass, page_logmass=None, stream=None, agg=AGG_LSE):
+    """locks_select with the library's static per-device scratch instead of a
+    workspace (for callers that cannot allocate; calls on one device must not
+    overlap)."""
+    sc, pc = summaries.c(), pages.c()
+    _check(lib().locks_select_noalloc(_ptr(q), q.shape[1], ctypes.byref(sc), ctypes.byref(pc),
+                                      budget_tokens, agg, _ptr(sel_pages), _ptr(sel_logmass),
+                                      _ptr(page_logmass), _stream(stream)),
+           "locks_select_noalloc")
 
 
 def locks_refresh_summaries(cache: PagedKV, pages: PageTable, page_begin, max_new_pages,

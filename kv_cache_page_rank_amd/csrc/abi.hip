@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <new>
 
 #include "../../include/locks.h"
@@ -427,6 +428,62 @@ locks_status locks_mean_share(const float* head_logmass, int32_t num_q_heads,
     return share_common(head_logmass, num_q_heads, num_kv_heads, pages, page_size,
                         static_cast<float*>(ws), page_logmass, run_max,
                         static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// Scratch of locks_select_noalloc: the selection workspace (page masses, run
+// maxima, per-head estimates and totals) in a static device array, so that
+// entry point never allocates.  Each device holds its own copy; its address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and kept.  In host code `scratch` itself is only a stand-in for
+// the symbol: kernels get the looked-up address, never the name.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+locks_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return LOCKS_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LOCKS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+locks_status locks_select_noalloc(const float* q, int32_t num_q_heads,
+                                  const locks_summaries* summaries, const locks_page_table* pages,
+                                  int32_t budget_tokens, int32_t agg, int32_t* sel_pages,
+                                  float* sel_logmass, float* page_logmass, void* stream) {
+    locks_status st = check_summaries(summaries, true);
+    if (st != LOCKS_OK) return st;
+    if ((st = check_page_table(pages)) != LOCKS_OK) return st;
+    if (!q || budget_tokens < 0 || !head_dims_ok(num_q_heads, summaries->num_kv_heads))
+        return LOCKS_ERR_INVALID_ARG;
+    const size_t need =
+        select_ws(pages->batch, pages->max_pages, num_q_heads, summaries->num_kv_heads);
+    if (need > kNoAllocScratchBytes) return LOCKS_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != LOCKS_OK) return st;
+    return locks_select(q, num_q_heads, summaries, pages, budget_tokens, agg, sel_pages,
+                        sel_logmass, page_logmass, ws, need, stream);
 }
 
 locks_status locks_sparse_attend(const float* q, int32_t num_q_heads, const locks_kv_cache* cache,

@@ -161,6 +161,15 @@ def test_host_validation_rejects_without_launch(lk):
         lk.LOCKS_ERR_UNSUPPORTED
     assert lib.locks_probe_summary_read(p, 32, by(sm), by(pt), None, None) == \
         lk.LOCKS_ERR_INVALID_ARG
+    # the allocation-free selection refuses shapes whose workspace exceeds its
+    # 16 MiB scratch, and bad arguments, on the host
+    _, _, pt_wide, _ = _fake(lk, B=64, MP=32768)
+    assert lib.locks_select_noalloc(p, 32, by(sm), by(pt_wide), 2048, 0, p, p, None, None) == \
+        lk.LOCKS_ERR_WORKSPACE
+    assert lib.locks_select_noalloc(None, 32, by(sm), by(pt), 2048, 0, p, p, None, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
+    assert lib.locks_select_noalloc(p, 32, by(sm), by(pt), -5, 0, p, p, None, None) == \
+        lk.LOCKS_ERR_INVALID_ARG
     # graph creation validates before capturing
     h = ctypes.c_void_p()
     assert lib.locks_step_graph_create(None, by(h)) == lk.LOCKS_ERR_INVALID_ARG
