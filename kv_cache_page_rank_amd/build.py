@@ -24,9 +24,18 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
          "-I" + os.path.join(os.path.dirname(HERE), "include")]
 
 
+# Extra flags of the summary-scan translation units: MFMA results in ordinary
+# VGPRs (the kernel fits two waves per SIMD either way, and the VALU reads the
+# results without accumulator-register moves), and no IEEE NaN handling (the
+# scan's max/exp chains then need no canonicalising moves; the scan never
+# reads NaN: rows of absent pages are zeroed by their bit patterns).
+SCAN_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]
+EXTRA_FLAGS = {"scan_f32.hip": SCAN_FLAGS, "scan_bf16.hip": SCAN_FLAGS, "scan_q8q4.hip": SCAN_FLAGS}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

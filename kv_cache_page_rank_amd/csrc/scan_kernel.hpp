@@ -39,8 +39,11 @@ namespace locks {
 
 namespace {
 
-constexpr int kBatch = kRunPages;  // pages per wave (one run)
-constexpr int kPrefetch = 1;       // basis tiles in flight ahead of the one computed
+// A wave scans NP consecutive pages (NP a multiple of kRunPages: whole runs)
+// with PF basis tiles in flight ahead of the one computed; the launcher picks
+// them per workload.  The bf16 and integer-code paths use one run, one tile.
+constexpr int kBatch = kRunPages;  // pages per wave of the bf16 / code paths
+constexpr int kPrefetch = 1;       // their tiles in flight ahead
 constexpr int kChains = 2;         // independent accumulator chains of an fp32 d contraction
 
 // State of one wave's batch, shared by the two specialisations below.
@@ -48,7 +51,7 @@ template <int D>
 struct WaveCtx {
     int b, g, j0, G, Hkv, r, lane, w, c;
     bool head_ok;
-    int my_phys;  // block of page j0 + c (-1: absent)
+    int my_phys;  // lane l: block of page j0 + l % NP (-1: absent)
     float* out_page;
     float qf[D / 4];  // query words as loaded (head c, or head 0 for padding heads)
     float qs;         // scale to log2 units, 0 for padding heads
@@ -98,7 +101,8 @@ __device__ __forceinline__ void load_f32(const void* base, size_t off, float* ou
 // Per-page tail shared by both summary types: lane (w, c) holds the logits of
 // tokens 16 mt + 4w + v for head c (log2 units, beta not yet added) in
 // L[mt][v].  Forms the head's LSE, adds beta, aggregates the group and
-// writes page pb of the batch (row w = pb / 4 holds the right beta).
+// writes page pb of the batch.  beta is the centroid tile of pb's run of 16
+// pages: its row w = (pb % 16) / 4 holds the right beta.
 template <int D, int MT, bool kHeads, bool kMasked>
 __device__ __forceinline__ void page_mass(const ScanParams& a, const WaveCtx<D>& x,
                                           const f32x4* L, int pb, const f32x4& beta,
@@ -130,7 +134,7 @@ __device__ __forceinline__ void page_mass(const ScanParams& a, const WaveCtx<D>&
         const float gm = max_in_row(x.head_ok ? top : -INFINITY);
         a2 = gm + fast_log2(sum_in_row(x.head_ok ? sum * fast_exp2(top - gm) : 0.0f));
     }
-    if (w == (pb >> 2) && j < a.max_pages) {
+    if (w == ((pb & 15) >> 2) && j < a.max_pages) {
         const bool ok = !kMasked || __builtin_amdgcn_readlane(x.my_phys, pb) >= 0;
         const float mass = ok ? a2 * kLn2 : -INFINITY;
         run_mx = fmaxf(run_mx, mass);
@@ -161,24 +165,29 @@ __device__ __forceinline__ void after_loads(T& v) {
     asm volatile("" : "+v"(v)::"memory");
 }
 
-// One wave's batch of kBatch pages.  kMasked: some page of the batch is
-// absent or the rank is padded, so loads are zeroed per row; otherwise no
-// masking code is emitted.  kHeads: per-head masses are written too.
-// fp32 summaries: the word layout keeps the fp32 loads 64 contiguous bytes
-// per row; the contraction order of the MFMA steps is chosen to match it.
-template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
+// One wave's batch of NP pages (NP / 16 runs).  kMasked: some page of the
+// batch is absent or the rank is padded, so loads are zeroed per row;
+// otherwise no masking code is emitted.  kHeads: per-head masses are written
+// too.  fp32 summaries: the word layout keeps the fp32 loads 64 contiguous
+// bytes per row; the contraction order of the MFMA steps is chosen to match
+// it.  PF basis tiles are in flight ahead of the one computed, across run
+// boundaries.
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked, int NP,
+          int PF>
 __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCtx<D>& x) {
     using TS = float;
     constexpr int PPT = 16 / RR;          // pages per basis tile (16 rows = PPT pages x RR rows)
-    constexpr int NTILE = kBatch / PPT;   // basis tiles per batch
+    constexpr int NTILE = NP / PPT;       // basis tiles per batch
+    constexpr int NRUN = NP / kRunPages;  // runs per batch
     constexpr int KS2 = RR / 4;           // K-steps of the coefficient product
     constexpr int MT = P / 16;            // token tiles per page
     constexpr int DS = D / 4;             // words of a row held per lane
     constexpr int E = Summ<TS>::E;        // elements per 16-byte load
     constexpr int NCH = D / (4 * E);      // 16-byte loads per row and lane
-    constexpr int PF = kPrefetch;
+    static_assert(NP % kRunPages == 0 && NP <= kWave && PF >= 1, "whole runs per wave");
     using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
-    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
+    // the exact path's rank is the compile-time RR (address products become shifts)
+    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = kExact ? RR : x.r;
     const int my_phys = x.my_phys;
     auto phys_at = [&](int pb) { return __shfl(my_phys, pb, kWave); };
     auto phys_uniform = [&](int pb) { return __builtin_amdgcn_readlane(my_phys, pb); };
@@ -290,32 +299,44 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
 #pragma unroll
     for (int i = 0; i < PF && i < NTILE; ++i) load_tile(i, ring[i]);
 
-    // beta tile: A row m = page j0 + m (lane column c supplies row c).
-    f32x4 beta;
+    // beta tiles, one per run: A row m = page j0 + 16 n + m (lane column c
+    // supplies row c).  All runs' centroid loads go out before the first product.
+    f32x4 beta[NRUN];
     {
-        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + E * w;
-        uint32_t mv[DS];
+        uint32_t mv[NRUN][DS];
 #pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-            float v[E];
-            load_f32<kOff32, E>(a.mu, src + 4 * E * t, v);
+        for (int n = 0; n < NRUN; ++n) {
+            const int pm = phys_at(16 * n + c);
+            const Off src = ((Off)(pm < 0 ? 0 : pm) * Hkv + g) * D + E * w;
 #pragma unroll
-            for (int e = 0; e < E; ++e) mv[E * t + e] = __float_as_uint(v[e]);
-        }
+            for (int t = 0; t < NCH; ++t) {
+                float v[E];
+                load_f32<kOff32, E>(a.mu, src + 4 * E * t, v);
 #pragma unroll
-        for (int i = 0; i < DS; ++i) {
-            after_loads(mv[i]);
-            mv[i] = (!kMasked || my_phys >= 0) ? mv[i] : 0u;
+                for (int e = 0; e < E; ++e) mv[n][E * t + e] = __float_as_uint(v[e]);
+            }
         }
         prepare_q();
-        beta = dot_q(mv);
+#pragma unroll
+        for (int n = 0; n < NRUN; ++n) {
+            const int pm = phys_at(16 * n + c);
+#pragma unroll
+            for (int i = 0; i < DS; ++i) {
+                after_loads(mv[n][i]);
+                mv[n][i] = (!kMasked || pm >= 0) ? mv[n][i] : 0u;
+            }
+            beta[n] = dot_q(mv[n]);
+        }
     }
-    // lane (w, c) now holds beta[page j0 + 4w + v][head c] in element v.
+    // lane (w, c) now holds beta[page j0 + 16 n + 4w + v][head c] in element v of beta[n].
 
-    float run_mx = -INFINITY;  // max of the written page masses (row w holds pages 4w..4w+3)
+    float run_mx = -INFINITY;  // max of the written page masses of the current run
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
         if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
+        // keep the next tile's loads ahead of this tile's waits (the scheduler
+        // would otherwise sink them below them, leaving nothing in flight)
+        __builtin_amdgcn_sched_barrier(0);
         const Tile& cur = ring[tt % (PF + 1)];
         const f32x4 Tcur = dot_q(cur.v);
         // coefficient product in fp32 (8 accumulating 16x16x4 steps per page at
@@ -333,13 +354,21 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
             }
 
 #pragma unroll
-        for (int p = 0; p < PPT; ++p)
-            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], tt * PPT + p, beta, run_mx);
-    }
-    if (a.run_max) {
-        run_mx = max_over_rows(run_mx);
-        const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
-        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
+        for (int p = 0; p < PPT; ++p) {
+            const int pb = tt * PPT + p;
+            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], pb, beta[pb / kRunPages], run_mx);
+        }
+        // a run ends with this tile: its maximum (row w holds pages 4w..4w+3)
+        if ((tt + 1) * PPT % kRunPages == 0) {
+            if (a.run_max) {
+                const float rm = max_over_rows(run_mx);
+                const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
+                const int run = (x.j0 + tt * PPT) / kRunPages;
+                if (x.lane == 0 && run < nruns)
+                    a.run_max[((size_t)x.b * Hkv + g) * nruns + run] = rm;
+            }
+            run_mx = -INFINITY;
+        }
     }
 }
 
@@ -369,7 +398,8 @@ __device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveC
     constexpr int WPP = RR / 4;           // lane groups per page in the coefficient operand
     constexpr int PF = kPrefetch;
     using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
-    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
+    // the exact path's rank is the compile-time RR (address products become shifts)
+    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = kExact ? RR : x.r;
     const int my_phys = x.my_phys;
 
     // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e.
@@ -467,6 +497,9 @@ __device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveC
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
         if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
+        // keep the next tile's loads ahead of this tile's waits (the scheduler
+        // would otherwise sink them below them, leaving nothing in flight)
+        __builtin_amdgcn_sched_barrier(0);
         const Tile& cur = ring[tt % (PF + 1)];
         f32x4 tacc[3];
 #pragma unroll
@@ -560,7 +593,8 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
     constexpr int WPP = RR / 4;           // lane groups per page in the coefficient operand
     constexpr int PF = kPrefetch;
     using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
-    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = x.r;
+    // the exact path's rank is the compile-time RR (address products become shifts)
+    const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = kExact ? RR : x.r;
     const int my_phys = x.my_phys;
     const int SC = 1 + 2 * r;             // scales per unit
     const uint8_t* const mu_q = static_cast<const uint8_t*>(a.mu);
@@ -727,10 +761,14 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
     }
 }
 
-template <typename TS, int P, int D, int RR, bool kExact, bool kHeads, bool kOff32>
+template <typename TS, int P, int D, int RR, bool kExact, bool kHeads, bool kOff32,
+          int NP = kBatch, int PF = kPrefetch>
 __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     static_assert(P % 16 == 0 && D % 32 == 0, "P a multiple of 16, d of 32");
     static_assert(RR == 4 || RR == 8 || RR == 16, "padded rank");
+    static_assert(NP % kRunPages == 0 && NP <= kWave, "whole runs per wave");
+    static_assert(sizeof(TS) == 4 || (NP == kBatch && PF == kPrefetch),
+                  "the bf16 and code paths scan one run per wave");
     constexpr int E = Summ<TS>::E;
     constexpr int NCH = D / (4 * E);
 
@@ -739,7 +777,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     x.w = x.lane >> 4;
     x.c = x.lane & 15;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int nbatch = (a.max_pages + kBatch - 1) / kBatch;
+    const int nbatch = (a.max_pages + NP - 1) / NP;
     if (wave >= a.batch * a.num_kv_heads * nbatch) return;
     const int jb = wave % nbatch;
     x.g = (wave / nbatch) % a.num_kv_heads;
@@ -748,32 +786,34 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     x.G = a.num_q_heads / x.Hkv;
     x.r = a.rank;
     x.head_ok = x.c < x.G;
-    x.j0 = jb * kBatch;
+    x.j0 = jb * NP;
     const int c = x.c, w = x.w;
 
-    // The block-table entry of page j0 + c is read together with the
-    // sequence length (clamped index, kept only if the page is full), so the
-    // two loads overlap instead of following each other.
-    const int jc = x.j0 + (c < kBatch ? c : 0);
+    // Lane l looks after page j0 + l % NP.  Its block-table entry is read
+    // together with the sequence length (clamped index, kept only if the page
+    // is full), so the two loads overlap instead of following each other.
+    const int pl = x.lane % NP;
+    const int jc = x.j0 + pl;
     const int p_spec =
         a.block_table[(size_t)x.b * a.max_pages + (jc < a.max_pages ? jc : a.max_pages - 1)];
     int full = a.seq_lens[x.b] / P;
     full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
     x.out_page = a.page_logmass + ((size_t)x.b * x.Hkv + x.g) * a.max_pages;
     if (x.j0 >= full) {  // whole batch past the full pages
-        if (a.run_max && x.lane == 0)
-            a.run_max[((size_t)x.b * x.Hkv + x.g) * nbatch + jb] = -INFINITY;
-        if (w == 0 && c < kBatch && x.j0 + c < a.max_pages) {
-            x.out_page[x.j0 + c] = -INFINITY;
+        const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
+        const int run = x.j0 / kRunPages + x.lane;
+        if (a.run_max && x.lane < NP / kRunPages && run < nruns)
+            a.run_max[((size_t)x.b * x.Hkv + x.g) * nruns + run] = -INFINITY;
+        if (x.lane < NP && x.j0 + x.lane < a.max_pages) {
+            x.out_page[x.j0 + x.lane] = -INFINITY;
             if constexpr (kHeads)
                 for (int hh = 0; hh < x.G; ++hh)
                     a.head_logmass[((size_t)x.b * a.num_q_heads + x.g * x.G + hh) * a.max_pages +
-                                   x.j0 + c] = -INFINITY;
+                                   x.j0 + x.lane] = -INFINITY;
         }
         return;
     }
-    x.my_phys =
-        (c < kBatch && x.j0 + c < full && p_spec >= 0 && p_spec < a.num_blocks) ? p_spec : -1;
+    x.my_phys = (jc < full && p_spec >= 0 && p_spec < a.num_blocks) ? p_spec : -1;
 
     // Query fragment, in the contraction order of the summary loads:
     // qf[E t + e] = q[h][4E t + E w + e] for head h = c, as loaded; the batch
@@ -796,13 +836,13 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
 
     // every page of the batch present and the rank not padded: no masking
     if constexpr (kExact) {
-        if (x.j0 + kBatch <= full && __ballot(c < kBatch && x.my_phys < 0) == 0ull) {
+        if (x.j0 + NP <= full && __ballot(x.lane < NP && x.my_phys < 0) == 0ull) {
             if constexpr (sizeof(TS) == 1)
                 scan_batch_q<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
             else if constexpr (sizeof(TS) == 2)
                 scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
             else
-                scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
+                scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, false, NP, PF>(a, x);
             return;
         }
     }
@@ -811,22 +851,25 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     else if constexpr (sizeof(TS) == 2)
         scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
     else
-        scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
+        scan_batch_f32<P, D, RR, kExact, kHeads, kOff32, true, NP, PF>(a, x);
 }
 
-template <typename TS, int P, int D, int RR, bool kHeads, bool kOff32>
-hipError_t launch4(const ScanParams& p, hipStream_t s, unsigned blocks) {
+template <typename TS, int P, int D, int RR, bool kHeads, bool kOff32, int NP, int PF>
+hipError_t launch4(const ScanParams& p, hipStream_t s) {
+    const long waves = (long)p.batch * p.num_kv_heads * ((p.max_pages + NP - 1) / NP);
+    const unsigned blocks = (unsigned)((waves + 3) / 4);
+    if (blocks == 0) return hipSuccess;
     if (p.rank == RR)
-        hipLaunchKernelGGL((scan_kernel<TS, P, D, RR, true, kHeads, kOff32>), dim3(blocks),
-                           dim3(256), 0, s, p);
+        hipLaunchKernelGGL((scan_kernel<TS, P, D, RR, true, kHeads, kOff32, NP, PF>),
+                           dim3(blocks), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((scan_kernel<TS, P, D, RR, false, kHeads, kOff32>), dim3(blocks),
-                           dim3(256), 0, s, p);
+        hipLaunchKernelGGL((scan_kernel<TS, P, D, RR, false, kHeads, kOff32, NP, PF>),
+                           dim3(blocks), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
-template <typename TS, int P, int D, int RR>
-hipError_t launch_ts(const ScanParams& p, hipStream_t s, unsigned blocks) {
+template <typename TS, int P, int D, int RR, int NP = kBatch, int PF = kPrefetch>
+hipError_t launch_ts(const ScanParams& p, hipStream_t s) {
     // largest summary array (basis or coefficients) in bytes
     size_t per_unit = (size_t)p.rank * (D > P ? D : P) * sizeof(TS);
     if (sizeof(TS) == 1) {  // codes: centroid D, basis r D/2, coefficients P r bytes
@@ -835,19 +878,15 @@ hipError_t launch_ts(const ScanParams& p, hipStream_t s, unsigned blocks) {
     }
     const bool off32 = (size_t)p.num_blocks * p.num_kv_heads * per_unit < (size_t(1) << 32);
     if (p.head_logmass != nullptr)
-        return off32 ? launch4<TS, P, D, RR, true, true>(p, s, blocks)
-                     : launch4<TS, P, D, RR, true, false>(p, s, blocks);
-    return off32 ? launch4<TS, P, D, RR, false, true>(p, s, blocks)
-                 : launch4<TS, P, D, RR, false, false>(p, s, blocks);
+        return off32 ? launch4<TS, P, D, RR, true, true, NP, PF>(p, s)
+                     : launch4<TS, P, D, RR, true, false, NP, PF>(p, s);
+    return off32 ? launch4<TS, P, D, RR, false, true, NP, PF>(p, s)
+                 : launch4<TS, P, D, RR, false, false, NP, PF>(p, s);
 }
-
 
 template <typename TS, int P, int D, int RR>
 hipError_t launch_typed(const ScanParams& p, hipStream_t s) {
-    const long waves = (long)p.batch * p.num_kv_heads * ((p.max_pages + kBatch - 1) / kBatch);
-    const unsigned blocks = (unsigned)((waves + 3) / 4);
-    if (blocks == 0) return hipSuccess;
-    return launch_ts<TS, P, D, RR>(p, s, blocks);
+    return launch_ts<TS, P, D, RR>(p, s);
 }
 
 template <typename TS, int P, int D>
