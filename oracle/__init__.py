@@ -37,7 +37,8 @@ class _Layout(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
-                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("summarized", ctypes.c_void_p)]
 
 
 def lib():
@@ -169,17 +170,22 @@ def attend_tokens(q, keys, vals):
 
 @dataclass
 class Layout:
-    """Paged layout: block_table [B][max_pages] int32, seq_lens [B] int32."""
+    """Paged layout: block_table [B][max_pages] int32, seq_lens [B] int32;
+    summarized [B] int32 or None: the leading pages of each sequence whose
+    summaries exist (None: every full page)."""
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
     page_size: int
     block_table: np.ndarray
     seq_lens: np.ndarray
+    summarized: np.ndarray | None = None
 
     def __post_init__(self):
         self.block_table = _i32(self.block_table)
         self.seq_lens = _i32(self.seq_lens)
+        if self.summarized is not None:
+            self.summarized = _i32(self.summarized)
 
     @property
     def batch(self):
@@ -196,7 +202,8 @@ class Layout:
     def c(self):
         s = _Layout(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
                     self.page_size, self.max_pages, self.block_table.ctypes.data,
-                    self.seq_lens.ctypes.data)
+                    self.seq_lens.ctypes.data,
+                    None if self.summarized is None else self.summarized.ctypes.data)
         return ctypes.byref(s), s
 
 

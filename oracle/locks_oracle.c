@@ -236,6 +236,15 @@ static int layout_ok(const orc_layout* L) {
 
 static int full_pages(const orc_layout* L, int b) { return L->seq_lens[b] / L->page_size; }
 
+/* Pages of sequence b that compete for the budget: the full pages whose
+ * summaries exist (all full pages when no count is given). */
+static int candidate_pages(const orc_layout* L, int b) {
+    const int full = full_pages(L, b);
+    if (!L->summarized) return full;
+    const int s = L->summarized[b] < 0 ? 0 : L->summarized[b];
+    return s < full ? s : full;
+}
+
 static int all_pages(const orc_layout* L, int b) {
     return (L->seq_lens[b] + L->page_size - 1) / L->page_size;
 }
@@ -355,7 +364,7 @@ int orc_scan_units(const orc_layout* L, int r, const float* q, const float* mu,
     const int G = L->num_q_heads / L->num_kv_heads;
     for (int u = 0; u < n; ++u) {
         if (ub[u] < 0 || ub[u] >= L->batch || ug[u] < 0 || ug[u] >= L->num_kv_heads ||
-            uj[u] < 0 || uj[u] >= full_pages(L, ub[u]))
+            uj[u] < 0 || uj[u] >= candidate_pages(L, ub[u]))
             return -1;
         const double a = scan_unit(L, r, q, mu, basis, coef, ub[u], ug[u], uj[u],
                                    head_mass ? head_mass + (size_t)u * G : NULL);
@@ -375,7 +384,7 @@ int orc_scan_pool(const orc_layout* L, int r, const float* q, const float* mu,
         const int j = (int)(u % MP), g = (int)((u / MP) % H), b = (int)(u / ((int64_t)MP * H));
         double est[1024];
         double a = -INFINITY;
-        if (j < full_pages(L, b)) {
+        if (j < candidate_pages(L, b)) {
             a = scan_unit(L, r, q, mu, basis, coef, b, g, j, est);
         } else {
             for (int hh = 0; hh < G; ++hh) est[hh] = -INFINITY;
@@ -399,8 +408,8 @@ int orc_share_pool(const orc_layout* L, const double* head_mass, double* page_sh
         return -1;
     }
     for (int b = 0; b < L->batch; ++b) {
-        const int full = full_pages(L, b);
-        /* each head's total estimated mass over the sequence's full pages */
+        const int full = candidate_pages(L, b);
+        /* each head's total estimated mass over the sequence's candidate pages */
         for (int h = 0; h < Hq; ++h) z[h] = orc_lse(full, head_mass + ((size_t)b * Hq + h) * MP);
         for (int g = 0; g < H; ++g)
             for (int j = 0; j < MP; ++j) {
@@ -459,7 +468,7 @@ int orc_select_pool(const orc_layout* L, int budget_tokens, const float* page_ma
     for (int b = 0; b < L->batch; ++b)
         for (int g = 0; g < H; ++g) {
             const size_t row = (size_t)b * H + g;
-            orc_select_topk(full_pages(L, b), page_mass + row * MP, k, width,
+            orc_select_topk(candidate_pages(L, b), page_mass + row * MP, k, width,
                             sel_pages + row * width, sel_mass ? sel_mass + row * width : NULL);
         }
     return 0;
@@ -467,7 +476,8 @@ int orc_select_pool(const orc_layout* L, int budget_tokens, const float* page_ma
 
 /* Reading for the partial last page: it has no summary yet (summaries are
  * made when a page is final, section 2), so it is never a candidate and is
- * always attended. */
+ * always attended; so is every full page whose summary does not exist yet
+ * (pages from candidate_pages(b) on). */
 int orc_attend_pool(const orc_layout* L, const float* q, const float* k_pool,
                     const float* v_pool, const int32_t* sel_pages, int width, double* out,
                     double* lse, int nthreads) {
@@ -478,15 +488,16 @@ int orc_attend_pool(const orc_layout* L, const float* q, const float* k_pool,
 #pragma omp parallel for schedule(dynamic, 1) num_threads(NTHREADS(nthreads))
     for (int64_t bh = 0; bh < rows; ++bh) {
         const int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h / G;
-        const int full = full_pages(L, b), np = all_pages(L, b);
-        /* the attended pages, in ascending order */
-        int32_t* pages = (int32_t*)malloc(sizeof(int32_t) * (size_t)(np > 0 ? np : 1));
+        const int cand = candidate_pages(L, b), np = all_pages(L, b);
+        /* the attended pages: the listed candidates, then every page without a
+         * summary (unsummarised full pages and the partial last page) */
+        int32_t* pages = (int32_t*)malloc(sizeof(int32_t) * (size_t)(np + width > 0 ? np + width : 1));
         int n_pages = 0;
         if (sel_pages) {
             const int32_t* s = sel_pages + ((size_t)b * H + g) * width;
             for (int t = 0; t < width; ++t)
-                if (s[t] >= 0 && s[t] < full) pages[n_pages++] = s[t];
-            if (np > full) pages[n_pages++] = full; /* partial last page */
+                if (s[t] >= 0 && s[t] < cand) pages[n_pages++] = s[t];
+            for (int j = cand; j < np; ++j) pages[n_pages++] = j;
         } else {
             for (int j = 0; j < np; ++j) pages[n_pages++] = j;
         }

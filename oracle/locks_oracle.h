@@ -94,6 +94,13 @@ typedef struct {
     int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages;
     const int32_t* block_table;
     const int32_t* seq_lens;
+    /* Nullable [B]: the leading pages of each sequence whose summaries exist.
+     * Reading (technical summary, section 2: a page's summary is made once
+     * the page is final, off the attention's critical path): only pages
+     * j < min(summarized[b], seq_lens[b] / P) are candidates for selection;
+     * full pages from there on have no summary yet and are attended like
+     * the partial last page, outside the budget.  NULL: every full page. */
+    const int32_t* summarized;
 } orc_layout;
 
 /* Summaries of every full page, written (rounded to float) at its physical

@@ -86,13 +86,23 @@ MUTANTS = [
      "const int k = budget_tokens / L->page_size;",
      "const int k = (budget_tokens + L->page_size - 1) / L->page_size;"),
     ("attend: partial last page left out",
-     "if (np > full) pages[n_pages++] = full; /* partial last page */", ""),
+     "            for (int j = cand; j < np; ++j) pages[n_pages++] = j;",
+     "            for (int j = cand; j < full_pages(L, b); ++j) pages[n_pages++] = j;"),
     ("attend: head -> group by h % H",
      "const int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h / G;",
      "const int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h % H;"),
-    ("attend: list entries that are not full pages accepted",
-     "if (s[t] >= 0 && s[t] < full) pages[n_pages++] = s[t];",
-     "if (s[t] >= 0 && s[t] <= full) pages[n_pages++] = s[t];"),
+    ("attend: list entries that are not candidates accepted",
+     "if (s[t] >= 0 && s[t] < cand) pages[n_pages++] = s[t];",
+     "if (s[t] >= 0 && s[t] <= cand) pages[n_pages++] = s[t];"),
+    ("select: pages without a summary compete",
+     "            orc_select_topk(candidate_pages(L, b), page_mass + row * MP, k, width,",
+     "            orc_select_topk(full_pages(L, b), page_mass + row * MP, k, width,"),
+    ("scan: pages without a summary scanned",
+     "        if (j < candidate_pages(L, b)) {\n            a = scan_unit(",
+     "        if (j < full_pages(L, b)) {\n            a = scan_unit("),
+    ("attend: full pages without a summary left out",
+     "            for (int j = cand; j < np; ++j) pages[n_pages++] = j;",
+     "            for (int j = full_pages(L, b); j < np; ++j) pages[n_pages++] = j;"),
     ("quantise: ties rounded away from zero",
      "const float y = rintf(x[(size_t)i * stride] / s);",
      "const float y = roundf(x[(size_t)i * stride] / s);"),

@@ -511,6 +511,61 @@ def test_sparse_attend_uses_only_listed_pages(wl, orc):
     np.testing.assert_allclose(out2[0, 0], _sdpa_ref(layer.q[0, 0], Kt, Vt), atol=1e-12)
 
 
+def test_unsummarised_pages_are_attended_outside_the_budget(wl, orc):
+    """Pages compete for the budget once their summary exists (technical
+    summary, section 2: a page's summary is made when the page is final, off
+    the attention's critical path).  With a count s_b of summarised pages per
+    sequence: pages j >= s_b are not scanned (-inf) and never selected, the
+    selection is the brute-force top-k of the masses over j < s_b, and the
+    attention covers exactly the selected pages plus every page from s_b to
+    the end (plain softmax with scipy over those tokens).  A count at or above
+    the full pages changes nothing; selecting every candidate is dense
+    attention whatever the count."""
+    from scipy.special import softmax
+    lens = [16 * 30 + 7, 16 * 20, 16 * 12 + 3]
+    spec, layer, lay = _small_layout(wl, orc, seq_lens=lens, batch=3, num_q_heads=4,
+                                     num_kv_heads=2, carriers=1)
+    P, d, G, r = spec.page_size, spec.head_dim, spec.group, spec.rank
+    K, V = layer.k_f32(), layer.v_f32()
+    counts = np.array([27, 25, 0], np.int32)  # 3 pending + partial; all summarised; none
+    lay_s = orc.Layout(spec.num_q_heads, spec.num_kv_heads, d, P, layer.block_table,
+                       layer.seq_lens, summarized=counts)
+    mu, basis, coef = orc.build_pool(lay, r, K, spec.num_blocks)
+    _, page_all = orc.scan_pool(lay, r, layer.q, mu, basis, coef)
+    _, page = orc.scan_pool(lay_s, r, layer.q, mu, basis, coef)
+    k = spec.k_pages
+    sel, _ = orc.select_pool(lay_s, spec.budget_tokens, page.astype(np.float32), k)
+    out, lse = orc.attend_pool(lay_s, layer.q, K, V, sel)
+    for b in range(3):
+        full, n_all = lens[b] // P, -(-lens[b] // P)
+        s_b = min(int(counts[b]), full)
+        np.testing.assert_array_equal(page[b, :, :s_b], page_all[b, :, :s_b])
+        assert np.all(np.isneginf(page[b, :, s_b:]))
+        for g in range(2):
+            want = _brute_topk(page_all[b, g, :s_b].astype(np.float32), min(k, s_b))
+            assert list(sel[b, g][sel[b, g] >= 0]) == want
+            pages = want + list(range(s_b, n_all))
+            toks = np.concatenate([K[layer.block_table[b, j], g, :min(P, lens[b] - j * P)]
+                                   for j in pages]).astype(np.float64)
+            vals = np.concatenate([V[layer.block_table[b, j], g, :min(P, lens[b] - j * P)]
+                                   for j in pages]).astype(np.float64)
+            for h in range(g * G, (g + 1) * G):
+                sc = toks @ layer.q[b, h].astype(np.float64) / math.sqrt(d)
+                assert abs(lse[b, h] - logsumexp(sc)) < 1e-12
+                np.testing.assert_allclose(out[b, h], softmax(sc) @ vals, rtol=0, atol=1e-12)
+    # a count at or above the full pages is no count at all
+    lay_f = orc.Layout(spec.num_q_heads, spec.num_kv_heads, d, P, layer.block_table,
+                       layer.seq_lens, summarized=np.array([40, 20, 13], np.int32))
+    _, page_f = orc.scan_pool(lay_f, r, layer.q, mu, basis, coef)
+    np.testing.assert_array_equal(page_f, page_all)
+    # select every candidate: dense attention, whatever the count
+    sel_all, _ = orc.select_pool(lay_s, 10 ** 6, page.astype(np.float32), spec.max_pages)
+    o_s, l_s = orc.attend_pool(lay_s, layer.q, K, V, sel_all)
+    o_d, l_d = orc.attend_pool(lay, layer.q, K, V, None)
+    np.testing.assert_allclose(o_s, o_d, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l_s, l_d, rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def test_pins_catch_planted_mistakes(orc):
