@@ -278,6 +278,32 @@ def main():
     log(f"step over {step_dist['replays']} replays: median {step_dist['median_us']:.2f} us, "
         f"p10 {step_dist['p10_us']:.2f}, p90 {step_dist['p90_us']:.2f}")
 
+    # --- the page-crossing refresh off the step's path: 10 step replays on the
+    # launch stream while a one-page refresh (B x H_kv units) runs on a side
+    # stream, against 10 replays alone (same graphs; the refresh rewrites the
+    # same values, so the overlap only shares the machine)
+    side = torch.cuda.Stream()
+    n_ov = 10
+
+    def replays(with_refresh):
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        if with_refresh:
+            side.wait_stream(torch.cuda.current_stream())
+            lk.locks_refresh_summaries(kvs[0], pages, last, 1, summs[0], stream=side)
+        for i in range(n_ov):
+            graphs[i % L].launch()
+        a1.record()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) * 1e3 / n_ov
+
+    replays(True)
+    alone_us = min(replays(False) for _ in range(3))
+    overlap_us = min(replays(True) for _ in range(3))
+    log(f"step beside a concurrent one-page refresh: {overlap_us:.2f} us per step over {n_ov} "
+        f"replays ({alone_us:.2f} alone; the refresh itself takes {refresh_us:.1f} us)")
+
     # --- dominant kernel: the summary scan alone, per-launch events on the launch stream
     pms = [torch.empty((B, Hkv, MP), device="cuda") for _ in range(L)]
     for i in range(args.warmup):
@@ -488,6 +514,8 @@ def main():
             "build_ms": round(build_ms, 3),
             "build_pages_per_s": round(full_total * Hkv / (build_ms * 1e-3), 1),
             "refresh_one_page_us": round(refresh_us, 1),
+            "step_beside_refresh_us": round(overlap_us, 3),
+            "step_alone_same_window_us": round(alone_us, 3),
             "bf16_summaries": bf16_summ,
             "q8q4_summaries": q8q4_summ,
             "mean_share_step_us": round(share_step, 3),

@@ -38,8 +38,12 @@
  *  - Page indices returned by selection are LOGICAL page numbers j within a
  *    sequence (page j holds tokens [jP, jP + P)); the block table maps them
  *    to physical blocks.
- *  - Only full pages (j < seq_len / P) have summaries and compete for the
- *    budget; a partial last page is always attended, outside the budget.
+ *  - Only full pages (j < seq_len / P) whose summaries exist compete for the
+ *    budget: all of them, or the first summarized[b] when the page table
+ *    carries that count.  The partial last page, and any full page whose
+ *    summary is still being built, is always attended, outside the budget
+ *    (technical summary, section 2: summaries are made once a page is final,
+ *    off the attention's critical path).
  *
  * Layouts (row-major, innermost last)
  *   q            [B][H_q][d]             float32, one decode query per head
@@ -138,12 +142,17 @@ typedef struct {
     float* scales; /* LOCKS_Q8Q4: [NB][H_kv][1 + 2r]; otherwise unused */
 } locks_summaries;
 
-/* Block table of a batch of sequences. */
+/* Block table of a batch of sequences.  summarized (nullable, device [B]):
+ * how many leading pages of each sequence have their summaries built; pages
+ * j < min(summarized[b], seq_lens[b] / P) compete for the budget, pages from
+ * there to the end are attended outside it.  NULL: every full page has its
+ * summary.  locks_refresh_summaries advances it. */
 typedef struct {
     int32_t batch;
     int32_t max_pages;
     const int32_t* block_table; /* [B][max_pages] */
     const int32_t* seq_lens;    /* [B] */
+    int32_t* summarized;        /* [B] or NULL */
 } locks_page_table;
 
 /* Bytes of workspace an operation needs for these shapes (0 if none).
@@ -181,9 +190,15 @@ locks_status locks_build_summaries(const locks_kv_cache* cache, const locks_page
  * attention's critical path): the same summaries as locks_build_summaries,
  * for the pages page_begin[b] <= j < min(page_begin[b] + max_new_pages,
  * seq_lens[b] / P) only, with a launch sized by max_new_pages (not by
- * max_pages).  page_begin: device [B], required.  In a decode loop the
- * caller sets page_begin[b] to the previous step's count of full pages, so a
- * step whose new token completes a page refreshes exactly that page.
+ * max_pages).  page_begin: device [B], required.  When pages->summarized is
+ * set, a second launch on the same stream then advances summarized[b] to the
+ * end of that range (when summarized[b] >= page_begin[b], i.e. no gap).
+ * Intended use: run it on a side stream once a step's token completes a
+ * page, with page_begin[b] = summarized[b]; steps launched meanwhile attend
+ * the new page outside the budget, and later steps see it as a candidate.
+ * A step that reads summarized[b] while this call runs sees the old or the
+ * new count; either is a valid state (the count advances only after the
+ * summaries are written).
  */
 locks_status locks_refresh_summaries(const locks_kv_cache* cache, const locks_page_table* pages,
                                      const int32_t* page_begin, int32_t max_new_pages,
@@ -355,16 +370,14 @@ typedef struct {
     float* out_lse;       /* optional [B][H_q] */
     void* ws;             /* locks_workspace_bytes(LOCKS_OP_STEP, ...) */
     size_t ws_bytes;
-    const int32_t* refresh_begin; /* optional device [B]: refresh node first (see */
-    int32_t refresh_pages;        /* locks_refresh_summaries); NULL / 0: none     */
 } locks_step_args;
 
 typedef struct locks_step_graph locks_step_graph;
 
 /*
- * Capture one decode step (locks_refresh_summaries when refresh_begin is
- * set, then locks_select and locks_sparse_attend, with the argument
- * pointers given) into an instantiated HIP graph (technical
+ * Capture one decode step (locks_select and locks_sparse_attend, with the
+ * argument pointers given; summaries of newly final pages are built outside
+ * it, see locks_refresh_summaries) into an instantiated HIP graph (technical
  * summary, section 2, Implementatie: scoring, selection and sparse attention
  * run inside full graphs).  The pointers are baked in: replay reads the
  * current contents of the same buffers.  *graph receives a handle owned by

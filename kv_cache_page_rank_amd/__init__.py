@@ -61,7 +61,8 @@ class CSummaries(ctypes.Structure):
 
 class CPageTable(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32),
-                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("summarized", ctypes.c_void_p)]
 
 
 class CStepArgs(ctypes.Structure):
@@ -71,8 +72,7 @@ class CStepArgs(ctypes.Structure):
                 ("cache", CKVCache), ("pages", CPageTable), ("sel_pages", ctypes.c_void_p),
                 ("sel_logmass", ctypes.c_void_p), ("page_logmass", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("out_lse", ctypes.c_void_p), ("ws", ctypes.c_void_p),
-                ("ws_bytes", ctypes.c_size_t), ("refresh_begin", ctypes.c_void_p),
-                ("refresh_pages", ctypes.c_int32)]
+                ("ws_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -164,12 +164,16 @@ class PagedKV:
 class PageTable:
     block_table: torch.Tensor  # [B][max_pages] int32
     seq_lens: torch.Tensor     # [B] int32
+    summarized: torch.Tensor | None = None  # [B] int32: leading pages with summaries
 
     def c(self) -> CPageTable:
         assert self.block_table.dtype == torch.int32 and self.seq_lens.dtype == torch.int32
         assert self.block_table.is_contiguous() and self.seq_lens.is_contiguous()
+        if self.summarized is not None:
+            assert self.summarized.dtype == torch.int32 and self.summarized.is_contiguous()
         B, MP = self.block_table.shape
-        return CPageTable(B, MP, self.block_table.data_ptr(), self.seq_lens.data_ptr())
+        return CPageTable(B, MP, self.block_table.data_ptr(), self.seq_lens.data_ptr(),
+                          None if self.summarized is None else self.summarized.data_ptr())
 
 
 @dataclass
@@ -356,15 +360,14 @@ class StepGraph:
 
     def __init__(self, q, summaries: Summaries, cache: PagedKV, pages: PageTable, budget_tokens,
                  sel_pages, sel_logmass, out, out_lse=None, page_logmass=None, ws=None,
-                 agg=AGG_LSE, refresh_begin=None, refresh_pages=0):
+                 agg=AGG_LSE):
         self._keep = (q, summaries, cache, pages, sel_pages, sel_logmass, out, out_lse,
-                      page_logmass, ws, refresh_begin)
+                      page_logmass, ws)
         a = CStepArgs(q.data_ptr(), q.shape[1], budget_tokens, agg, summaries.c(), cache.c(),
                       pages.c(), sel_pages.data_ptr(), sel_logmass.data_ptr(),
                       None if page_logmass is None else page_logmass.data_ptr(), out.data_ptr(),
                       None if out_lse is None else out_lse.data_ptr(),
-                      None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
-                      None if refresh_begin is None else refresh_begin.data_ptr(), refresh_pages)
+                      None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel())
         h = ctypes.c_void_p()
         _check(lib().locks_step_graph_create(ctypes.byref(a), ctypes.byref(h)),
                "locks_step_graph_create")

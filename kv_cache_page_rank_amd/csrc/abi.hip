@@ -109,6 +109,7 @@ locks_status attend_common(const float* q, int32_t hq, const locks_kv_cache* kv,
     p.bf16 = kv->dtype == LOCKS_BF16;
     p.block_table = pt->block_table;
     p.seq_lens = pt->seq_lens;
+    p.summarized = pt->summarized;
     p.sel_pages = sel;
     p.batch = pt->batch;
     p.num_q_heads = hq;
@@ -141,6 +142,7 @@ locks_status scan_common(const float* q, int32_t hq, const locks_summaries* s,
     p.scales = s->scales;
     p.block_table = pt->block_table;
     p.seq_lens = pt->seq_lens;
+    p.summarized = pt->summarized;
     p.batch = pt->batch;
     p.num_q_heads = hq;
     p.num_kv_heads = s->num_kv_heads;
@@ -162,6 +164,7 @@ locks_status topk_common(const float* page_logmass, const locks_page_table* pt, 
     locks::TopkParams p{};
     p.page_logmass = page_logmass;
     p.seq_lens = pt->seq_lens;
+    p.summarized = pt->summarized;
     p.batch = pt->batch;
     p.num_kv_heads = hkv;
     p.max_pages = pt->max_pages;
@@ -182,6 +185,7 @@ locks_status share_common(const float* head_logmass, int32_t hq, int32_t hkv,
     locks::ShareParams p{};
     p.head_logmass = head_logmass;
     p.seq_lens = pt->seq_lens;
+    p.summarized = pt->summarized;
     p.batch = pt->batch;
     p.num_q_heads = hq;
     p.num_kv_heads = hkv;
@@ -312,8 +316,15 @@ locks_status locks_refresh_summaries(const locks_kv_cache* cache, const locks_pa
                                      const int32_t* page_begin, int32_t max_new_pages,
                                      const locks_summaries* out, void* stream) {
     if (!page_begin || max_new_pages <= 0) return LOCKS_ERR_INVALID_ARG;
-    return build_common(cache, pages, page_begin, max_new_pages, out,
-                        static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const locks_status st = build_common(cache, pages, page_begin, max_new_pages, out, s);
+    if (st != LOCKS_OK || !pages->summarized) return st;
+    // the new summaries exist once the build above is done (stream order):
+    // the count advances after it
+    const hipError_t e = locks::launch_advance_summarized(
+        pages->seq_lens, page_begin, pages->summarized, pages->batch, cache->page_size,
+        pages->max_pages, max_new_pages, s);
+    return e == hipSuccess ? LOCKS_OK : hip_fail(e);
 }
 
 locks_status locks_quantize_summaries(const locks_summaries* src, const locks_summaries* dst,
@@ -530,14 +541,9 @@ locks_status locks_step_graph_create(const locks_step_args* a, locks_step_graph*
         (void)hipStreamDestroy(s);
         return hip_fail(e);
     }
-    locks_status st = LOCKS_OK;
-    if (a->refresh_begin && a->refresh_pages > 0)
-        st = locks_refresh_summaries(&a->cache, &a->pages, a->refresh_begin, a->refresh_pages,
-                                     &a->summaries, s);
-    if (st == LOCKS_OK)
-        st = locks_select(a->q, a->num_q_heads, &a->summaries, &a->pages, a->budget_tokens,
-                          a->agg, a->sel_pages, a->sel_logmass, a->page_logmass, a->ws,
-                          a->ws_bytes, s);
+    locks_status st = locks_select(a->q, a->num_q_heads, &a->summaries, &a->pages,
+                                   a->budget_tokens, a->agg, a->sel_pages, a->sel_logmass,
+                                   a->page_logmass, a->ws, a->ws_bytes, s);
     if (st == LOCKS_OK) {
         void* attn_ws = static_cast<char*>(a->ws) + sel_bytes;
         st = locks_sparse_attend(a->q, a->num_q_heads, &a->cache, &a->pages, a->sel_pages, k, a->out,

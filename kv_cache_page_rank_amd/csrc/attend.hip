@@ -1,9 +1,12 @@
 // Split-K paged flash-decode over a page list, and the log-sum-exp merge.
 //
-// Sparse: for each (b, g) one split per selected page plus one split for the
-// sequence's partial last page (abstract: only the top pages are attended;
-// the partial page has no summary yet and is always attended).  Dense: each
-// split is a run of consecutive pages (the dense-attention baseline).
+// Sparse: for each (b, g) one split per selected page plus one tail split for
+// every page without a summary (abstract: only the top pages are attended; a
+// page's summary is made once the page is final, so the partial last page,
+// and full pages whose summaries are still being built, are always
+// attended): pages [cand, n_all), where cand = min(summarised pages, full
+// pages) - normally just the partial page.  Dense: each split is a run of
+// consecutive pages (the dense-attention baseline).
 // A split emits, per query head, the running max m and sum l (log2 units)
 // and the unnormalised output o; the merge combines the splits of a head in
 // split order: M = max m_s, L = sum l_s 2^(m_s - M), out = sum o_s 2^(m_s - M) / L,
@@ -22,18 +25,25 @@ namespace locks {
 namespace {
 
 struct SplitPages {
-    int first, count;  // consecutive logical pages [first, first + count) (count 0 or 1 for sparse)
+    int first, count;  // consecutive logical pages [first, first + count)
 };
 
+// Candidates of sequence b (full pages with summaries; attention needs the
+// count to know which pages the tail split covers).
+__device__ __forceinline__ int attn_candidates(const AttnParams& a, int b, int seq_raw) {
+    return candidate_pages(seq_raw, a.summarized ? a.summarized[b] : 0, a.summarized != nullptr,
+                           a.page_size, a.max_pages);
+}
+
 __device__ __forceinline__ SplitPages split_pages(const AttnParams& a, bool sparse, int b, int g,
-                                                  int s, int full, int n_all) {
+                                                  int s, int cand, int n_all) {
     SplitPages r{0, 0};
     if (sparse) {
         if (s < a.k_sel) {
             const int j = a.sel_pages[((size_t)b * a.num_kv_heads + g) * a.k_sel + s];
-            if (j >= 0 && j < full) r = {j, 1};
-        } else if (n_all > full) {
-            r = {full, 1};  // partial last page
+            if (j >= 0 && j < cand) r = {j, 1};
+        } else if (n_all > cand) {
+            r = {cand, n_all - cand};  // pages without a summary (the tail)
         }
     } else {
         const int lo = s * a.pages_per_split;
@@ -330,6 +340,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     const int hq = g * G + (head_ok ? c : 0);
 
     const int seq_raw = a.seq_lens[b];
+    const int summ_raw = a.summarized ? a.summarized[b] : 0;
     // sparse: this lane's list entry (slot s * pages_per_split + lane; a run
     // has at most 16 slots), read together with the sequence length; the
     // list is a readable device array even when k_sel = 0
@@ -337,12 +348,13 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
     if constexpr (kSparse) {
         const int slot = s * a.pages_per_split + lane;
         j_list0 = a.sel_pages[((size_t)b * Hkv + g) * a.k_sel + (slot < a.k_sel ? slot : 0)];
-        asm volatile("" ::"s"(seq_raw), "v"(j_list0));
+        asm volatile("" ::"s"(seq_raw), "s"(summ_raw), "v"(j_list0));
     }
     const int seq = seq_raw < 0 ? 0 : seq_raw;
-    int full = seq / P, n_all = (seq + P - 1) / P;
-    full = full > a.max_pages ? a.max_pages : full;
+    int n_all = (seq + P - 1) / P;
     n_all = n_all > a.max_pages ? a.max_pages : n_all;
+    // candidates (full pages with summaries); pages [cand, n_all) form the tail
+    const int cand = candidate_pages(seq_raw, summ_raw, a.summarized != nullptr, P, a.max_pages);
     // dense: consecutive pages [first, first + count); sparse: slots
     // [first, first + count) of the selected list (pages_per_split per wave)
     SplitPages sp{0, 0};
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
             const int hi = lo + a.pages_per_split < slots ? lo + a.pages_per_split : slots;
             sp = {lo, hi > lo ? hi - lo : 0};
         } else {
-            sp = split_pages(a, false, b, g, s, full, n_all);
+            sp = split_pages(a, false, b, g, s, cand, n_all);
         }
     }
 
@@ -421,18 +433,22 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
 
     if constexpr (kSparse) {
         // A sparse run is one chunk (at most 16 slots).  Lane l's page is
-        // slot sp.first + l, whose list entry was read up front.  Its
+        // slot sp.first + l, whose list entry was read up front; the slots
+        // from k_sel on are the tail, pages cand, cand + 1, .. (normally just
+        // the partial page), one per lane up to the wave's 64 lanes.  The
         // block-table read is unconditional (clamped to entry 0: the table
         // has at least one column) and goes out before the query's loads;
         // the page is checked once those are issued, and the query is split
         // only after the first page's loads are out.
         const int slot = sp.first + lane;
+        const int tail = n_all - cand;  // pages without a summary
+        // the wave whose slots include k_sel takes the tail (lanes from k_sel on)
+        const bool tail_wave = s < S && sp.first <= a.k_sel && a.k_sel < sp.first + sp.count;
         int jc = -1;
         if (slot < a.k_sel)
-            jc = (j_list0 >= 0 && j_list0 < full) ? j_list0 : -1;
-        else if (slot == a.k_sel && n_all > full)
-            jc = full;  // partial last page
-        jc = lane < sp.count ? jc : -1;
+            jc = (lane < sp.count && j_list0 >= 0 && j_list0 < cand) ? j_list0 : -1;
+        else if (tail_wave && slot - a.k_sel < tail)
+            jc = cand + (slot - a.k_sel);
         const int ph_raw = bt[jc >= 0 ? jc : 0];
         f32x4 xa[KS], xb[KS];
         load_q_raw<D>(a, b, hq, w, xa, xb);
@@ -442,7 +458,24 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const AttnParams a) {
         const bool ok = jc >= 0 && ph_raw >= 0 && ph_raw < a.num_blocks;
         const int jl = ok ? jc : -1, pl = ok ? ph_raw : -1;
         const uint64_t todo = __ballot(ok);
-        if (todo != 0) walk(todo, jl, pl, [&] { split_q<D>(xa, xb, head_ok, qp); });
+        bool split = false;
+        if (todo != 0) walk(todo, jl, pl, [&] { split_q<D>(xa, xb, head_ok, qp); split = true; });
+        // a tail longer than the lanes left for it: the rest, 64 pages a round
+        const int in_wave = sp.first + kWave - a.k_sel;  // tail pages the first round took
+        if (tail_wave) {
+            for (int base = in_wave; base < tail; base += kWave) {
+                const int t = base + lane;
+                const int jt = t < tail ? cand + t : -1;
+                const int pt = bt[jt >= 0 ? jt : 0];
+                const bool okt = jt >= 0 && pt >= 0 && pt < a.num_blocks;
+                const uint64_t todo2 = __ballot(okt);
+                if (todo2 != 0)
+                    walk(todo2, okt ? jt : -1, okt ? pt : -1, [&] {
+                        if (!split) split_q<D>(xa, xb, head_ok, qp);
+                        split = true;
+                    });
+            }
+        }
     } else {
         {
             f32x4 xa[KS], xb[KS];
@@ -500,21 +533,33 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
     // (sel_pages is always a readable device array: with k_sel = 0 it is a
     // marker that is read but never used)
     const int seq_raw = a.seq_lens[b];
+    const int summ_raw = a.summarized ? a.summarized[b] : 0;
     const int j_list = a.sel_pages[((size_t)b * Hkv + g) * a.k_sel + (s < a.k_sel ? s : 0)];
-    // both values are consumed here, so both reads issue before one wait
+    // the values are consumed here, so all reads issue before one wait
     // (otherwise the list read is sunk into the branch that uses it)
-    asm volatile("" ::"s"(seq_raw), "s"(j_list));
+    asm volatile("" ::"s"(seq_raw), "s"(summ_raw), "s"(j_list));
     const int seq = seq_raw < 0 ? 0 : seq_raw;
-    int full = seq / P, n_all = (seq + P - 1) / P;
-    full = full > a.max_pages ? a.max_pages : full;
+    int n_all = (seq + P - 1) / P;
     n_all = n_all > a.max_pages ? a.max_pages : n_all;
+    const int cand =
+        candidate_pages(seq_raw, summ_raw, a.summarized != nullptr, P, a.max_pages);
     SplitPages sp{0, 0};
     if (s < a.k_sel) {
-        if (j_list >= 0 && j_list < full) sp = {j_list, 1};
-    } else if (n_all > full) {
-        sp = {full, 1};  // partial last page
+        if (j_list >= 0 && j_list < cand) sp = {j_list, 1};
+    } else if (n_all > cand) {
+        sp = {cand, n_all - cand};  // pages without a summary (normally the partial page)
     }
-    int phys = sp.count ? a.block_table[(size_t)b * a.max_pages + sp.first] : -1;
+
+    QParts<KS> qp;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // one page (pi = 0: also the query's loads and split); the tail split
+    // walks its pages one after the other with the running max rescaled
+    for (int pi = 0; pi < (sp.count > 0 ? sp.count : 1); ++pi) {
+    const int jpg = sp.first + pi;
+    int phys = sp.count ? a.block_table[(size_t)b * a.max_pages + jpg] : -1;
     const bool page_ok = sp.count && phys >= 0 && phys < a.num_blocks;
     phys = page_ok ? phys : 0;
 
@@ -533,19 +578,14 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
             vraw[md] = *reinterpret_cast<const u32x2*>(vp + (size_t)(16 * md + c) * P);
     }
 
-    QParts<KS> qp;
-    {
+    if (pi == 0) {
         f32x4 xa[KS], xb[KS];
         load_q_raw<D>(a, b, hq, w, xa, xb);
         split_q<D>(xa, xb, head_ok, qp);
     }
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 acc[MD];
-#pragma unroll
-    for (int md = 0; md < MD; ++md) acc[md] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (page_ok) {
-        const int nv = seq - sp.first * P < P ? seq - sp.first * P : P;
+        const int nv = seq - jpg * P < P ? seq - jpg * P : P;
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -558,8 +598,16 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
 #pragma unroll
             for (int v = 0; v < 4; ++v) sc[v] = tok0 + 4 * w + v < nv ? sc[v] : -INFINITY;
         }
-        const float mx = max_over_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        const float mx_page = max_over_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        const float mx = fmaxf(m_run, mx_page);
         if (mx != -INFINITY) {
+            // earlier pages of the tail: rescale to the new running max
+            if (m_run != -INFINITY && m_run != mx) {
+                const float al = fast_exp2(m_run - mx);
+                l_run *= al;
+#pragma unroll
+                for (int md = 0; md < MD; ++md) acc[md] *= al;
+            }
             uint32_t ph[2], pl[2];
             float psum = 0.f;
 #pragma unroll
@@ -574,7 +622,7 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
                 pl[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
             }
             m_run = mx;
-            l_run = psum;
+            l_run += psum;
             const bf16x4 bhi = as_bf16x4(u32x2{ph[0], ph[1]});
             const bf16x4 blo = as_bf16x4(u32x2{pl[0], pl[1]});
 #pragma unroll
@@ -593,6 +641,7 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
             }
         }
     }
+    }  // pages of the split
     const float l_tot = sum_over_rows(l_run);
     if (w == 0) {
         sm_m[wv][c] = m_run;
@@ -623,10 +672,10 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const AttnParams a) {
     const int G = a.num_q_heads / Hkv;
     const int t = threadIdx.x;
     const int seq = a.seq_lens[b] < 0 ? 0 : a.seq_lens[b];
-    int full = seq / P, n_all = (seq + P - 1) / P;
-    full = full > a.max_pages ? a.max_pages : full;
+    int n_all = (seq + P - 1) / P;
     n_all = n_all > a.max_pages ? a.max_pages : n_all;
-    const SplitPages sp = split_pages(a, kSparse, b, g, s, full, n_all);
+    const int cand = attn_candidates(a, b, seq);
+    const SplitPages sp = split_pages(a, kSparse, b, g, s, cand, n_all);
 
     const float qscale = kLog2e / sqrtf((float)D);
     for (int i = t; i < G * D; i += 256) {

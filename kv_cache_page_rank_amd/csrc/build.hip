@@ -509,6 +509,20 @@ __global__ __launch_bounds__(build_threads<P>()) void build_kernel(const BuildPa
     }
 }
 
+// The summarised-page count after a refresh: one thread per sequence.
+__global__ void advance_summarized_kernel(const int32_t* seq_lens, const int32_t* page_begin,
+                                          int32_t* summarized, int batch, int page_size,
+                                          int max_pages, int max_new_pages) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= batch) return;
+    int full = seq_lens[b] / page_size;
+    full = full < 0 ? 0 : (full > max_pages ? max_pages : full);
+    const int lo = page_begin[b];
+    const int hi = lo + max_new_pages < full ? lo + max_new_pages : full;
+    const int cur = summarized[b];
+    if (cur >= lo && hi > cur) summarized[b] = hi;
+}
+
 template <int P, int D>
 hipError_t launch_pd(const BuildParams& p, hipStream_t s) {
     const long units =
@@ -528,6 +542,15 @@ hipError_t launch_pd(const BuildParams& p, hipStream_t s) {
 bool build_supported(int page_size, int head_dim, int rank) {
     return (page_size == 16 || page_size == 64) && (head_dim == 64 || head_dim == 128) &&
            rank >= 1 && rank <= 16 && rank <= page_size && rank <= head_dim;
+}
+
+hipError_t launch_advance_summarized(const int32_t* seq_lens, const int32_t* page_begin,
+                                     int32_t* summarized, int32_t batch, int32_t page_size,
+                                     int32_t max_pages, int32_t max_new_pages, hipStream_t s) {
+    hipLaunchKernelGGL(advance_summarized_kernel, dim3((batch + 255) / 256), dim3(256), 0, s,
+                       seq_lens, page_begin, summarized, batch, page_size, max_pages,
+                       max_new_pages);
+    return hipGetLastError();
 }
 
 hipError_t launch_build(const BuildParams& p, hipStream_t s) {

@@ -135,6 +135,18 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x4 as_bf16x4(u32x2 v) { return __builtin_bit_cast(bf16x4, v); }
 
+// Pages of a sequence that compete for the budget: its full pages (seq / P,
+// clamped to [0, max_pages]) whose summaries exist (the first `summ` pages;
+// summ_valid false: all of them).  Pages from there to the end are attended
+// outside the budget.
+__device__ __forceinline__ int candidate_pages(int seq_raw, int summ, bool summ_valid, int P,
+                                               int max_pages) {
+    int full = seq_raw / P;
+    full = full < 0 ? 0 : (full > max_pages ? max_pages : full);
+    if (summ_valid) full = summ < 0 ? 0 : (summ < full ? summ : full);
+    return full;
+}
+
 // Monotone map of a float's bits to uint32 (ascending floats -> ascending
 // keys; -0 is first folded onto +0).  NaN inputs are not ordered.
 __device__ __forceinline__ uint32_t orderable_bits(float f) {

@@ -25,6 +25,7 @@ struct ScanParams {
     int32_t summ_dtype;
     const int32_t* block_table;
     const int32_t* seq_lens;
+    const int32_t* summarized;  // [B] or null: leading pages with summaries (candidates)
     int32_t batch, num_q_heads, num_kv_heads, max_pages, num_blocks;
     int32_t page_size, head_dim, rank;
     float* page_logmass;   // [B][Hkv][max_pages]
@@ -38,6 +39,7 @@ bool scan_supported(int page_size, int head_dim, int rank);
 struct ShareParams {
     const float* head_logmass;  // [B][Hq][max_pages]
     const int32_t* seq_lens;
+    const int32_t* summarized;  // [B] or null: leading pages with summaries (candidates)
     int32_t batch, num_q_heads, num_kv_heads, max_pages, page_size;
     float* head_total;          // [B][Hq] workspace
     float* page_logmass;        // [B][Hkv][max_pages]
@@ -48,6 +50,7 @@ hipError_t launch_share(const ShareParams& p, hipStream_t s);
 struct TopkParams {
     const float* page_logmass;  // [B][Hkv][max_pages]
     const int32_t* seq_lens;
+    const int32_t* summarized;  // [B] or null: leading pages with summaries (candidates)
     int32_t batch, num_kv_heads, max_pages, page_size, k_req, width;
     int32_t* sel_pages;         // [B][Hkv][width]
     float* sel_logmass;         // [B][Hkv][width] or null
@@ -63,6 +66,7 @@ struct AttnParams {
     int32_t bf16;              // cache dtype
     const int32_t* block_table;
     const int32_t* seq_lens;
+    const int32_t* summarized;  // [B] or null: leading pages with summaries (candidates)
     const int32_t* sel_pages;  // [B][Hkv][k_sel] (sparse) or null (dense)
     int32_t batch, num_q_heads, num_kv_heads, max_pages, num_blocks;
     int32_t page_size, head_dim;
@@ -95,6 +99,12 @@ struct BuildParams {
     int32_t out_dtype;     // SummDtype
 };
 hipError_t launch_build(const BuildParams& p, hipStream_t s);
+// After a refresh of pages [page_begin[b], min(page_begin[b] + max_new_pages,
+// full pages)): summarized[b] advances to the end of that range when it
+// reached at least page_begin[b] (no gap).  One thread per sequence.
+hipError_t launch_advance_summarized(const int32_t* seq_lens, const int32_t* page_begin,
+                                     int32_t* summarized, int32_t batch, int32_t page_size,
+                                     int32_t max_pages, int32_t max_new_pages, hipStream_t s);
 bool build_supported(int page_size, int head_dim, int rank);
 
 // Shared-basis sketch (ablation baseline): the centroid of every full page

@@ -796,8 +796,11 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     const int jc = x.j0 + pl;
     const int p_spec =
         a.block_table[(size_t)x.b * a.max_pages + (jc < a.max_pages ? jc : a.max_pages - 1)];
-    int full = a.seq_lens[x.b] / P;
-    full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
+    // the pages that compete: full pages whose summaries exist (the count is
+    // read beside the length; pages past it are not scanned and get -inf)
+    const int summ_raw = a.summarized ? a.summarized[x.b] : 0;
+    const int full =
+        candidate_pages(a.seq_lens[x.b], summ_raw, a.summarized != nullptr, P, a.max_pages);
     x.out_page = a.page_logmass + ((size_t)x.b * x.Hkv + x.g) * a.max_pages;
     if (x.j0 >= full) {  // whole batch past the full pages
         const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;

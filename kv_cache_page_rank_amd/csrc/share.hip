@@ -26,8 +26,8 @@ __global__ __launch_bounds__(kShareThreads) void head_total_kernel(const SharePa
     const int bh = blockIdx.x;
     const int b = bh / a.num_q_heads;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    int full = a.seq_lens[b] / a.page_size;
-    full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
+    const int full = candidate_pages(a.seq_lens[b], a.summarized ? a.summarized[b] : 0,
+                                     a.summarized != nullptr, a.page_size, a.max_pages);
     const float* row = a.head_logmass + (size_t)bh * a.max_pages;
     float m = -INFINITY, sum = 0.f;
     for (int base = 0; base < full; base += kShareThreads * kShareVals) {
@@ -76,8 +76,8 @@ __global__ __launch_bounds__(kShareThreads) void share_kernel(const ShareParams 
     const int bg = blockIdx.x / nchunk;
     const int b = bg / Hkv, g = bg % Hkv;
     const int j = (blockIdx.x % nchunk) * kShareThreads + threadIdx.x;
-    int full = a.seq_lens[b] / a.page_size;
-    full = full < 0 ? 0 : (full > a.max_pages ? a.max_pages : full);
+    const int full = candidate_pages(a.seq_lens[b], a.summarized ? a.summarized[b] : 0,
+                                     a.summarized != nullptr, a.page_size, a.max_pages);
     float score = -INFINITY;
     if (j < full) {
         const float* hm = a.head_logmass + ((size_t)b * a.num_q_heads + g * G) * a.max_pages + j;

@@ -229,6 +229,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
     // of them hold full pages is decided once the length is in.
     const int nruns_all = (a.max_pages + kRunPages - 1) / kRunPages;
     const int seq_raw = a.seq_lens[b];
+    const int summ_raw = a.summarized ? a.summarized[b] : 0;
     float rmv[kRunPer];
 #pragma unroll
     for (int i = 0; i < kRunPer; ++i) rmv[i] = 0.f;
@@ -242,9 +243,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
     }
     // both reads issue before one wait (the run-maxima reads would otherwise
     // be sunk below the branches on the length)
-    asm volatile("" ::"s"(seq_raw), "v"(rmv[0]), "v"(rmv[kRunPer - 1]));
-    int n = seq_raw / a.page_size;
-    n = n < 0 ? 0 : (n > a.max_pages ? a.max_pages : n);
+    asm volatile("" ::"s"(seq_raw), "s"(summ_raw), "v"(rmv[0]), "v"(rmv[kRunPer - 1]));
+    // candidates: the full pages whose summaries exist
+    const int n =
+        candidate_pages(seq_raw, summ_raw, a.summarized != nullptr, a.page_size, a.max_pages);
     const int k = a.k_req < n ? a.k_req : n;
     const float* row = a.page_logmass + (size_t)bg * a.max_pages;
     int32_t* out_sel = a.sel_pages + (size_t)bg * a.width;

@@ -1,33 +1,43 @@
-"""Summaries kept current inside the decode graph: a step whose new token
-completes a page refreshes that page's summary before the scan reads it
-(technical summary, section 2: a page's summary is made once the page is
-final).  The refreshed summaries must equal a full build of the new state,
-and the step's selection and attention the eager calls on them."""
+"""Summaries of pages that became final during decoding, built off the
+step's critical path (technical summary, section 2: a page's summary is made
+once the page is final, off the attention's critical path).  A step whose
+new token completes a page attends that page outside the budget (the page
+table's count of summarised pages has not reached it); the refresh, on a
+side stream, builds the page's summaries and then advances the count, and
+later steps see the page as a candidate.  Every stage is checked against the
+oracle on the same count, and the captured step against the eager calls."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_cases import DEV, Case, bf16_small, say
+from gpu_cases import DEV, Case, band_ok, bf16_small, masses_close, say, to_np
 
 pytestmark = pytest.mark.gpu
 
 
-def _build(lk, case, lens=None):
+def _build(lk, case):
     s = case.spec
     summ = lk.Summaries.empty(s.num_blocks, s.num_kv_heads, s.page_size, s.head_dim, s.rank)
     lk.locks_build_summaries(case.kv, case.pages, summ)
     return summ
 
 
-def _full_blocks(case):
-    lens = case.pages.seq_lens.cpu().numpy()
-    bt = case.layer.block_table
-    return np.concatenate([bt[b, :lens[b] // case.spec.page_size] for b in range(len(lens))])
+def _oracle_step(case, summ, counts, k, budget):
+    """The oracle's scan (of the library's summaries), selection and the
+    attention over a given page list, on the device's current lengths."""
+    s = case.spec
+    lens = case.pages.seq_lens.cpu().numpy().astype(np.int32)
+    lay = oracle.Layout(s.num_q_heads, s.num_kv_heads, s.head_dim, s.page_size,
+                        case.layer.block_table, lens, summarized=np.asarray(counts, np.int32))
+    mu, basis, coef = (t.cpu().numpy() for t in (summ.mu, summ.basis, summ.coef))
+    _, page = oracle.scan_pool(lay, s.rank, case.layer.q, mu, basis, coef)
+    sel, _ = oracle.select_pool(lay, budget, page.astype(np.float32), k)
+    return lay, page, sel
 
 
 @pytest.mark.parametrize("agg", [0, 1], ids=["lse", "mean-share"])
-def test_refresh_in_graph_tracks_page_crossing(agg):
+def test_refresh_off_the_step_path(agg):
     import kv_cache_page_rank_amd as lk
     P = 64
     # one token short of a page boundary in both sequences; the slots past the
@@ -37,47 +47,72 @@ def test_refresh_in_graph_tracks_page_crossing(agg):
     k = s.k_pages
     say("refresh: initial build", agg)
     summ = _build(lk, case)
+    counts = torch.tensor([40, 23], dtype=torch.int32, device=DEV)
+    pages = lk.PageTable(case.pages.block_table, case.pages.seq_lens, counts)
     torch.cuda.synchronize()
-    begin = torch.tensor([40, 23], dtype=torch.int32, device=DEV)  # full pages before the step
-    ws_b = lk.workspace_bytes(lk.OP_STEP, s.batch, s.max_pages, s.num_q_heads, s.num_kv_heads,
-                              P, s.head_dim, s.rank, k)
-    g = dict(sel=torch.empty((s.batch, s.num_kv_heads, k), dtype=torch.int32, device=DEV),
-             mass=torch.empty((s.batch, s.num_kv_heads, k), device=DEV),
-             out=torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.bfloat16, device=DEV),
-             lse=torch.empty((s.batch, s.num_q_heads), device=DEV), ws=lk.workspace(ws_b))
-    graph = lk.StepGraph(case.q, summ, case.kv, case.pages, s.budget_tokens, g["sel"], g["mass"],
-                         g["out"], g["lse"], ws=g["ws"], agg=agg, refresh_begin=begin,
-                         refresh_pages=1)
-    # the decode step appends one token: both sequences complete a page
+    args = (s.batch, s.max_pages, s.num_q_heads, s.num_kv_heads, P, s.head_dim, s.rank, k)
+    mk = lambda: dict(sel=torch.empty((s.batch, s.num_kv_heads, k), dtype=torch.int32, device=DEV),
+                      mass=torch.empty((s.batch, s.num_kv_heads, k), device=DEV),
+                      out=torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.bfloat16,
+                                      device=DEV),
+                      lse=torch.empty((s.batch, s.num_q_heads), device=DEV),
+                      pm=torch.empty((s.batch, s.num_kv_heads, s.max_pages), device=DEV),
+                      ws=lk.workspace(lk.workspace_bytes(lk.OP_STEP, *args)))
+    g, e = mk(), mk()
+    graph = lk.StepGraph(case.q, summ, case.kv, pages, s.budget_tokens, g["sel"], g["mass"],
+                         g["out"], g["lse"], page_logmass=g["pm"], ws=g["ws"], agg=agg)
+    sel_b = lk.workspace_bytes(lk.OP_SELECT, *args)
+
+    def step_and_check(stage, cnt):
+        say("refresh:", stage, cnt)
+        graph.launch()
+        lk.locks_select(case.q, summ, pages, s.budget_tokens, e["sel"], e["mass"],
+                        page_logmass=e["pm"], ws=e["ws"], agg=agg)
+        lk.locks_sparse_attend(case.q, case.kv, pages, e["sel"], e["out"], e["lse"],
+                               ws=e["ws"][sel_b:])
+        torch.cuda.synchronize()
+        for key in ("sel", "mass", "out", "lse", "pm"):
+            assert torch.equal(g[key], e[key]), (stage, key)
+        lay, page, sel_o = _oracle_step(case, summ, cnt, k, s.budget_tokens)
+        if agg == 1:
+            head, _ = oracle.scan_pool(lay, s.rank, case.layer.q,
+                                       *(t.cpu().numpy() for t in (summ.mu, summ.basis, summ.coef)))
+            page = oracle.share_pool(lay, head)
+            sel_o, _ = oracle.select_pool(lay, s.budget_tokens, page.astype(np.float32), k)
+        assert masses_close(to_np(g["pm"]), page) <= 1e-4
+        sel = to_np(g["sel"])
+        for b in range(s.batch):
+            for gg in range(s.num_kv_heads):
+                assert band_ok(sel[b, gg], sel_o[b, gg], page[b, gg, :cnt[b]], min(k, cnt[b]))
+        o_o, l_o = oracle.attend_pool(lay, case.layer.q, case.k_f32, case.layer.v_f32(), sel)
+        got = to_np(g["out"]).astype(np.float64)
+        assert np.all(np.abs(got - o_o) <= np.maximum(1e-2, 2.0 ** (np.floor(
+            np.log2(np.maximum(np.abs(o_o), 1e-30))) - 7)))
+        assert np.abs(to_np(g["lse"]) - l_o).max() <= 1e-4
+        return sel
+
+    # the decode step appends one token: both sequences complete a page, whose
+    # summary does not exist yet - the step attends it outside the budget
     case.pages.seq_lens += 1
-    say("refresh: graph replay across the page boundary")
-    graph.launch()
-    torch.cuda.synchronize()
-    ref = _build(lk, case)
-    torch.cuda.synchronize()
-    blocks = torch.from_numpy(_full_blocks(case).astype(np.int64)).to(DEV)
-    for got, want in ((summ.mu, ref.mu), (summ.basis, ref.basis), (summ.coef, ref.coef)):
-        assert torch.equal(got[blocks].view(torch.int32), want[blocks].view(torch.int32))
-    # the refreshed pages against the oracle's build of the new state
+    sel = step_and_check("step with the new pages pending", [40, 23])
+    assert np.all(sel[0][sel[0] >= 0] < 40) and np.all(sel[1][sel[1] >= 0] < 23)
+    # the refresh on a side stream builds the new pages and then moves the count
+    side = torch.cuda.Stream()
+    begin = counts.clone()
+    with torch.cuda.stream(side):
+        say("refresh: side-stream build of the new pages")
+        lk.locks_refresh_summaries(case.kv, pages, begin, 1, summ, stream=side)
+    side.synchronize()
+    assert counts.cpu().tolist() == [41, 24]
     _check_refreshed_against_oracle(case, summ, [(0, 40), (1, 23)])
-    # the step's outputs equal the eager calls on fully rebuilt summaries
-    e = {key: torch.empty_like(v) for key, v in g.items()}
-    lk.locks_select(case.q, ref, case.pages, s.budget_tokens, e["sel"], e["mass"], ws=e["ws"],
-                    agg=agg)
-    sel_b = lk.workspace_bytes(lk.OP_SELECT, s.batch, s.max_pages, s.num_q_heads, s.num_kv_heads,
-                               P, s.head_dim, s.rank, k)
-    lk.locks_sparse_attend(case.q, case.kv, case.pages, e["sel"], e["out"], e["lse"],
-                           ws=e["ws"][sel_b:])
-    torch.cuda.synchronize()
-    for key in ("sel", "mass", "out", "lse"):
-        assert torch.equal(g[key], e[key]), key
-    # a step that completes no page leaves every summary as it is
+    step_and_check("step after the refresh", [41, 24])
+    # a token inside a page: the refresh finds no new full page, nothing moves
     before = [t.clone() for t in (summ.mu, summ.basis, summ.coef)]
-    begin.copy_(torch.tensor([41, 24], dtype=torch.int32))
     case.pages.seq_lens += 1
-    say("refresh: graph replay inside a page")
-    graph.launch()
+    begin.copy_(counts)
+    lk.locks_refresh_summaries(case.kv, pages, begin, 1, summ)
     torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [41, 24]
     for a, b in zip(before, (summ.mu, summ.basis, summ.coef)):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     graph.close()
