@@ -17,6 +17,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short bf16x4 __attribute__((ext_vector_type(4)));  // 4 bf16 bit patterns
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -107,6 +108,14 @@ __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c)
 // l/16; it receives D[4*(l/16) + v][l%16] in element v.
 __device__ __forceinline__ f32x4 mfma_16x16x16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x64) * B(64x16), int8 inputs, int32 accumulate (exact).
+// Lane l supplies 16 int8 of row l%16 of A and of column l%16 of B, k-group
+// l/16 (A and B share the lane and byte order of k); it receives
+// D[4*(l/16) + v][l%16] in element v.
+__device__ __forceinline__ i32x4 mfma_16x16x64_i8(i32x4 a, i32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

@@ -43,7 +43,8 @@ namespace {
 // with PF basis tiles in flight ahead of the one computed; the launcher picks
 // them per workload.  The bf16 and integer-code paths use one run, one tile.
 constexpr int kBatch = kRunPages;  // pages per wave of the bf16 / code paths
-constexpr int kPrefetch = 1;       // their tiles in flight ahead
+constexpr int kPrefetch = 1;       // the bf16 path's tiles in flight ahead
+constexpr int kCodePrefetch = 2;   // the code path's (its tiles are small: more in flight)
 constexpr int kChains = 2;         // independent accumulator chains of an fp32 d contraction
 
 // State of one wave's batch, shared by the two specialisations below.
@@ -544,54 +545,106 @@ __device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveC
     }
 }
 
-// Integer codes widened to bf16: small integers are exact in bf16, so the
-// bf16 MFMA products of the codes with the split query stay exact; the
-// scales are applied in fp32 to the accumulated sums.  The codes are read
-// as unsigned fields with the sign bit flipped (excess-8 / excess-128) and
-// the bias subtracted in float, which is exact: a sign-extending field
-// extract followed by an int-to-float convert is folded by this compiler into
-// an unsigned convert of the sign-extended value, wrong for negative codes.
-// 8 int4 codes (element e in bits 4e..4e+3) -> 8 bf16, pairs packed low first.
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-}
-__device__ __forceinline__ u32x4 widen_i4x8(uint32_t w) {
-    const uint32_t u = w ^ 0x88888888u;  // two's complement -> excess-8
-    u32x4 o;
+// Per-page tail of batches whose logits arrive shifted: the coefficient
+// product starts from beta - shift, shift = the page's largest beta over the
+// group's heads (a wave-uniform value).  Lane (w, c) holds the shifted logits
+// of tokens 16 mt + 4w + v for head c (log2 units) in L[mt][v], every lane
+// the same page; padding heads carry values near -1e30 and drop out.
+// Log-sum-exp over the group is the log-sum-exp of all 64 x 16 (token, head)
+// logits of the page.  The coefficients of a page sum to zero over its tokens
+// (they are projections of keys less their mean), so the best head's largest
+// shifted logit is about 0 or more and the sum of 2^logit is at least about 1;
+// it exceeds 2^60 only for deviations from the centroid term of some 50 log2
+// units.  Pages whose sum leaves [2^-60, 2^60] take the exact form (the
+// page's max subtracted first).  With per-head output (kHeads) every head's
+// sum is taken with its own max.
+template <int MT, bool kHeads, bool kMasked, int D>
+__device__ __forceinline__ void page_mass_shifted(const ScanParams& a, const WaveCtx<D>& x,
+                                                  const f32x4* L, int pb, float shift,
+                                                  float& run_mx) {
+    const int j = x.j0 + pb;
+    auto local_max = [&]() {
+        float m = L[0][0];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float lo = (float)((u >> (8 * p)) & 15u) - 8.f;
-        const float hi = (float)((u >> (8 * p + 4)) & 15u) - 8.f;
-        o[p] = bf16_pair(lo, hi);
-    }
-    return o;
-}
-// 4 int8 codes (element e in byte e) -> 4 bf16.
-__device__ __forceinline__ u32x2 widen_i8x4(uint32_t w) {
-    const uint32_t u = w ^ 0x80808080u;  // two's complement -> excess-128
-    u32x2 o;
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const float lo = (float)((u >> (16 * p)) & 255u) - 128.f;
-        const float hi = (float)((u >> (16 * p + 8)) & 255u) - 128.f;
-        o[p] = bf16_pair(lo, hi);
+            for (int v = 0; v < 4; ++v) m = fmaxf(m, L[mt][v]);
+        return m;
+    };
+    auto local_sum = [&](float off) {
+        float s = fast_exp2(L[0][0] - off);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = (mt == 0 ? 1 : 0); v < 4; ++v) s += fast_exp2(L[mt][v] - off);
+        return s;
+    };
+    float a2, s2 = 0.0f;
+    if constexpr (!kHeads) {
+        const float sum = sum_in_row(sum_over_rows(local_sum(0.0f)));
+        if (sum >= 0x1p-60f && sum <= 0x1p60f) {
+            a2 = shift + fast_log2(sum);
+        } else {
+            const float mx = max_in_row(max_over_rows(local_max()));
+            a2 = shift + mx + fast_log2(sum_in_row(sum_over_rows(local_sum(mx))));
+        }
+    } else {
+        const float mx = max_over_rows(local_max());
+        s2 = shift + mx + fast_log2(sum_over_rows(local_sum(mx)));
+        const float xv = x.head_ok ? s2 : -INFINITY;
+        const float gm = max_in_row(xv);
+        a2 = gm + fast_log2(sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f));
     }
-    return o;
+    if (j < a.max_pages) {
+        const bool ok = !kMasked || __builtin_amdgcn_readlane(x.my_phys, pb) >= 0;
+        const float mass = ok ? a2 * kLn2 : -INFINITY;
+        run_mx = fmaxf(run_mx, mass);
+        if (x.lane == 0) x.out_page[j] = mass;
+        if constexpr (kHeads) {
+            if (x.w == 0 && x.head_ok)
+                a.head_logmass[((size_t)x.b * a.num_q_heads + x.g * x.G + x.c) * a.max_pages + j] =
+                    ok ? s2 * kLn2 : -INFINITY;
+        }
+    }
 }
 
-// One batch of kBatch pages with int8 / int4 summaries: the bf16 scan's
-// operand layout and MFMAs on the widened codes.  With codes m (centroid),
-// v (basis), c (coefficients) and scales s_mu, s_v[k], s_c[k]:
-//   beta = s_mu (m . q),   t_k = s_v[k] s_c[k] (v_k . q),   logit_i = beta + sum_k c_ik t_k,
-// the same estimator on the dequantised summary (scale * code).
-template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked>
+// The KS2 int8 codes in the low bytes of v as floats, one sign-extending
+// byte convert each (v a full word: nothing known about its upper bytes).
+template <int KS2>
+__device__ __forceinline__ void sbytes_f32(uint32_t v, float* out) {
+#pragma unroll
+    for (int k = 0; k < KS2; ++k) out[k] = (float)(int8_t)(v >> (8 * k));
+}
+
+// One batch of kBatch pages with integer-code summaries (int8 centroid and
+// coefficients, int4 basis, one fp32 scale per vector).  With codes m, v, c
+// and scales s_mu, s_v[k], s_c[k]:
+//   beta = s_mu (m . q),   T_k = s_v[k] s_c[k] (v_k . q),   logit_i = beta + sum_k c_ik T_k,
+// the estimator on the dequantised summary (scale * code).
+//
+// The query is held as four signed 8-bit digits per value: with E the
+// exponent of head h's largest |q| (|q| < 2^E), X = trunc(q 2^(30-E)) =
+// d0 + 2^8 d1 + 2^16 d2 + 2^24 d3, digits in [-128, 127], read off the bytes
+// of (X + 0x808080) ^ 0x808080.  Code-by-digit products run on the int8
+// matrix cores and are exact in int32; the four digit sums meet in fp32
+// (relative error ~2^-24, that of fp32 arithmetic).  int4 basis codes c are
+// widened to the bytes c + 8 (a few bit operations per 8 codes) and the +8
+// comes off through the accumulator's starting value, -8 times the digits'
+// sums over d (one int8 product with a ones matrix, once per wave).  The
+// coefficient product runs in fp32 (16x16x4 steps) on codes converted one
+// instruction each, from a starting value of beta, so the logits leave it
+// with the centroid term in.
+template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked, int PF>
 __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<D>& x) {
-    constexpr int PPT = 16 / RR;          // pages per tile
+    constexpr int PPT = 16 / RR;          // pages per basis tile
     constexpr int NTILE = kBatch / PPT;
     constexpr int MT = P / 16;            // token tiles per page
-    constexpr int NCH = D / 32;           // 32-wide d chunks
-    constexpr int WPP = RR / 4;           // lane groups per page in the coefficient operand
-    constexpr int PF = kPrefetch;
+    constexpr int KS2 = RR / 4;           // coefficient k-steps per page (codes per lane)
+    constexpr int NW = D / 32;            // basis words (8 int4 codes) per lane and row
+    constexpr int NCK = D / 64;           // 64-deep int8 products over d
+    constexpr int NQ = D / 4;             // query values per lane
+    static_assert(D % 64 == 0, "d a multiple of 64");
+    static_assert(PF >= 1, "at least one tile in flight");
     using Off = typename std::conditional<kOff32, uint32_t, size_t>::type;
     // the exact path's rank is the compile-time RR (address products become shifts)
     const int w = x.w, c = x.c, g = x.g, Hkv = x.Hkv, r = kExact ? RR : x.r;
@@ -600,164 +653,264 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
     const uint8_t* const mu_q = static_cast<const uint8_t*>(a.mu);
     const uint8_t* const basis_q = static_cast<const uint8_t*>(a.basis);
     const uint8_t* const coef_q = static_cast<const uint8_t*>(a.coef);
-
-    // q parts, in the order of the summary loads: chunk t holds d = 32t + 8w + e.
-    // Split after the first tile's and the centroids' loads are issued.
-    bf16x8 qp[3][NCH];
-    auto split_q = [&]() {
-        float qv[D / 4];
-        query_after_loads<D / 4>(x.qf, qv);
-#pragma unroll
-        for (int t = 0; t < NCH; ++t)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                __bf16 h, m, l;
-                split3(qv[8 * t + e] * x.qs, h, m, l);
-                qp[0][t][e] = h;
-                qp[1][t][e] = m;
-                qp[2][t][e] = l;
-            }
+    // scales of the unit (block, g): 32-bit byte offsets when the arrays allow
+    auto scales_of = [&](int blk) -> const float* {
+        const Off o = ((Off)blk * Hkv + g) * SC;
+        return reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.scales) +
+                                              (Off)(o * (Off)sizeof(float)));
     };
 
-    const int a_pin = c / RR, a_k = c % RR;   // basis row loaded by this lane
-    const int c_pin = w / WPP;                // page whose coefficients this lane supplies
-    const int c_k0 = 4 * (w % WPP);           // its first coefficient index
-    const int s_pin = (4 * w) / RR;           // page of the T rows 4w..4w+3 this lane holds
-    const int s_k0 = (4 * w) % RR;            // their first basis index
+    // Basis row loaded by the lane (tile row m = c): page (m%4)/KS2 of the
+    // tile, row KS2 (m/4) + (m%4)%KS2.  Row 4w + v of T is then page v / KS2,
+    // k = KS2 w + v % KS2: the lane's B operand of k-step v % KS2 of that page.
+    const int a_pin = (c & 3) / KS2;
+    const int a_kk = KS2 * (c >> 2) + ((c & 3) % KS2);
     struct Tile {
-        uint32_t v[NCH];   // 8 int4 codes per chunk
-        uint32_t cf[MT];   // 4 int8 codes per token tile
-        float sc[4];       // s_v[k] s_c[k] of the lane's four T rows
+        uint32_t v[NW];          // 8 int4 codes each, d = 32t + 8w + e
+        uint32_t cf[PPT][MT];    // the aligned word holding codes k = KS2 w .. KS2 w + KS2 - 1
     };
+    // the lane's codes start at bit cshift of its coefficient word (rank
+    // RR: a token's row of r codes is word-aligned)
+    const uint32_t cshift = kExact ? (uint32_t)(8 * ((KS2 * w) & 3)) : 0u;
+    // Loaded words stay as they are until the tile is computed (arithmetic on
+    // them here would wait for the next tile's loads right after issuing them).
     auto load_tile = [&](int tt, Tile& T) {
         const int pj = __shfl(my_phys, tt * PPT + a_pin, kWave);
-        const bool row_ok = !kMasked || (pj >= 0 && a_k < r);
+        const bool row_ok = !kMasked || (pj >= 0 && a_kk < r);
         const Off src = (((Off)(kMasked && pj < 0 ? 0 : pj) * Hkv + g) * r +
-                         (kMasked && a_k >= r ? r - 1 : a_k)) * (D / 2) + 4 * w;
+                         (kMasked && a_kk >= r ? r - 1 : a_kk)) * (D / 2) + 4 * w;
 #pragma unroll
-        for (int t = 0; t < NCH; ++t) {
+        for (int t = 0; t < NW; ++t) {
             const uint32_t v = *reinterpret_cast<const uint32_t*>(basis_q + src + 16 * t);
             T.v[t] = row_ok ? v : 0u;
         }
-        const int pp = __shfl(my_phys, tt * PPT + c_pin, kWave);
-        const bool ok = !kMasked || pp >= 0;
-        const Off csrc = ((Off)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const Off row = csrc + (Off)(16 * mt + c) * r;
-            if constexpr (kExact) {
-                const uint32_t v = *reinterpret_cast<const uint32_t*>(coef_q + row + c_k0);
-                T.cf[mt] = ok ? v : 0u;
-            } else {  // padded rank: byte by byte, clamped and zeroed past it
-                uint32_t hv = 0u;
+        for (int p = 0; p < PPT; ++p) {
+            const int pp = __builtin_amdgcn_readlane(my_phys, tt * PPT + p);
+            const bool ok = !kMasked || pp >= 0;
+            const Off csrc = ((Off)(kMasked && pp < 0 ? 0 : pp) * Hkv + g) * P * r;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int kk = c_k0 + e;
-                    const uint32_t b = coef_q[row + (kk < r ? kk : r - 1)];
-                    hv |= ((ok && kk < r) ? b : 0u) << (8 * e);
+            for (int mt = 0; mt < MT; ++mt) {
+                const Off row = csrc + (Off)(16 * mt + c) * r;
+                if constexpr (kExact) {
+                    const uint32_t v =
+                        *reinterpret_cast<const uint32_t*>(coef_q + row + ((KS2 * w) & ~3));
+                    T.cf[p][mt] = ok ? v : 0u;
+                } else {  // padded rank: byte by byte, clamped and zeroed past it
+                    uint32_t hv = 0u;
+#pragma unroll
+                    for (int ks = 0; ks < KS2; ++ks) {
+                        const int kk = KS2 * w + ks;
+                        const uint32_t b = coef_q[row + (kk < r ? kk : r - 1)];
+                        hv |= ((ok && kk < r) ? b : 0u) << (8 * ks);
+                    }
+                    T.cf[p][mt] = hv;
                 }
-                T.cf[mt] = hv;
             }
-        }
-        const int ps = __shfl(my_phys, tt * PPT + s_pin, kWave);
-        const float* sp = a.scales + ((size_t)(kMasked && ps < 0 ? 0 : ps) * Hkv + g) * SC;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int k = s_k0 + v;
-            const bool kok = (!kMasked || ps >= 0) && (kExact || k < r);
-            const int kc = kExact || k < r ? k : r - 1;
-            T.sc[v] = kok ? sp[1 + kc] * sp[1 + r + kc] : 0.f;
         }
     };
 
+    // s_v[k] s_c[k] of every page and row of the batch: lane l loads page
+    // l / 4, rows KS2 (l%4) .. + KS2 - 1 (0 past the rank or for an absent page)
+    float sl_v[KS2], sl_c[KS2];
+    {
+        const int ps = __shfl(my_phys, x.lane >> 2, kWave);
+        const float* sp = scales_of(ps < 0 ? 0 : ps);
+#pragma unroll
+        for (int e = 0; e < KS2; ++e) {
+            const int k = KS2 * (x.lane & 3) + e;
+            const int kc = kExact || k < r ? k : r - 1;
+            sl_v[e] = sp[1 + kc];
+            sl_c[e] = sp[1 + r + kc];
+            if (ps < 0 || (!kExact && k >= r)) sl_v[e] = 0.0f;
+        }
+    }
+    // centroid scales of pages j0 + 4w + v (the rows of the beta product this
+    // lane receives)
+    float smu[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int pv = __shfl(my_phys, 4 * w + v, kWave);
+        smu[v] = pv < 0 ? 0.0f : scales_of(pv)[0];
+    }
+    // centroid codes of page j0 + c (row c of the beta product), d = 32t + 8w + e
+    u32x2 m8[NW];
+    {
+        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + 8 * w;
+#pragma unroll
+        for (int t = 0; t < NW; ++t) m8[t] = *reinterpret_cast<const u32x2*>(mu_q + src + 32 * t);
+    }
+    // the first tiles' loads follow the ones the batch's set-up waits for
     Tile ring[PF + 1];
 #pragma unroll
     for (int i = 0; i < PF && i < NTILE; ++i) load_tile(i, ring[i]);
 
-    // beta tile: A row m = page j0 + m (lane column c supplies row c).
-    f32x4 beta;
+    // Query digits.  Word wd of product chunk j holds d = 32t + 8w + pi + 2k in
+    // byte k, t = 2j + wd/2, pi = wd%2: even d of a basis word's 8, then odd.
+    i32x4 qd[4][NCK];
+    float p2;  // 2^(E-30): the digits' unit
     {
-        const Off src = ((Off)(my_phys < 0 ? 0 : my_phys) * Hkv + g) * D + 8 * w;
-        f32x4 bacc[3];
+        float qv[NQ];
+        query_after_loads<NQ>(x.qf, qv);
+        float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 3; ++i) bacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        u32x2 m8[NCH];
-#pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-            m8[t] = *reinterpret_cast<const u32x2*>(mu_q + src + 32 * t);
+        for (int i = 0; i < NQ; ++i) {
+            qv[i] *= x.qs;
+            amax = fmaxf(amax, fabsf(qv[i]));
         }
+        amax = max_over_rows(amax);
+        int E = __builtin_amdgcn_frexp_expf(amax);  // amax < 2^E; 0 for amax 0
+        E = E < -90 ? -90 : (E > 120 ? 120 : E);
+        const float up = __builtin_ldexpf(1.0f, 30 - E);
+        p2 = __builtin_ldexpf(1.0f, E - 30);
 #pragma unroll
-        for (int t = 0; t < NCH; ++t) {
+        for (int t = 0; t < NW; ++t)
+#pragma unroll
+            for (int pi = 0; pi < 2; ++pi) {
+                uint32_t z[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int X = (int)(qv[8 * t + pi + 2 * k] * up);
+                    z[k] = ((uint32_t)X + 0x808080u) ^ 0x808080u;
+                }
+                // 4 x 4 byte transpose: digit i of the four values
+                const uint32_t lo_ab = __builtin_amdgcn_perm(z[1], z[0], 0x05010400u);
+                const uint32_t hi_ab = __builtin_amdgcn_perm(z[1], z[0], 0x07030602u);
+                const uint32_t lo_cd = __builtin_amdgcn_perm(z[3], z[2], 0x05010400u);
+                const uint32_t hi_cd = __builtin_amdgcn_perm(z[3], z[2], 0x07030602u);
+                const int j = t / 2, wd = 2 * (t % 2) + pi;
+                qd[0][j][wd] = (int)__builtin_amdgcn_perm(lo_cd, lo_ab, 0x05040100u);
+                qd[1][j][wd] = (int)__builtin_amdgcn_perm(lo_cd, lo_ab, 0x07060302u);
+                qd[2][j][wd] = (int)__builtin_amdgcn_perm(hi_cd, hi_ab, 0x05040100u);
+                qd[3][j][wd] = (int)__builtin_amdgcn_perm(hi_cd, hi_ab, 0x07060302u);
+            }
+    }
+    // starting values of the basis product: -8 times each digit's sum over d,
+    // digits 0 and 1 (and 2 and 3) in the accumulator the pair combines into
+    int bias_lo, bias_hi;
+    {
+        const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+        i32x4 S[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            S[i] = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < NCK; ++j) S[i] = mfma_16x16x64_i8(ones, qd[i][j], S[i]);
+        }
+        bias_lo = (int)(0u - 8u * ((uint32_t)S[0][0] + 256u * (uint32_t)S[1][0]));
+        bias_hi = (int)(0u - 8u * ((uint32_t)S[2][0] + 256u * (uint32_t)S[3][0]));
+    }
+    // digit sums -> fp32 in units of the digits (times p2 for q's units)
+    auto combine = [](const i32x4* acc, int v) -> float {
+        const int r10 = (int)(((uint32_t)acc[1][v] << 8) + (uint32_t)acc[0][v]);
+        const int r32 = (int)(((uint32_t)acc[3][v] << 8) + (uint32_t)acc[2][v]);
+        return fmaf((float)r32, 65536.0f, (float)r10);
+    };
+
+    // beta - shift of the batch's 16 pages for the lane's head, in every lane:
+    // the product gives lane (w, c) pages 4w..4w+3; a per-wave table in LDS
+    // hands each lane the other twelve.  shift of page 4w + v = the largest
+    // beta over the group's heads, in sv[v] of lane (w, c).
+    float betas[kBatch];
+    float sv[4];
+    __shared__ float stbl[4][kBatch][RR];     // [wave of the block][page][row]: s_v s_c
+    const int wv = threadIdx.x >> 6;
+    {
+        __shared__ float tbl[4][16][kBatch];  // [wave of the block][head][page]
+        i32x4 acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < NW; ++t) {
             after_loads(m8[t]);
             if (kMasked && my_phys < 0) m8[t] = u32x2{0u, 0u};
         }
-        split_q();
 #pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-            const u32x2 lo = widen_i8x4(m8[t][0]), hi = widen_i8x4(m8[t][1]);
-            const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+        for (int j = 0; j < NCK; ++j) {
+            const i32x4 mw = {(int)__builtin_amdgcn_perm(m8[2 * j][1], m8[2 * j][0], 0x06040200u),
+                              (int)__builtin_amdgcn_perm(m8[2 * j][1], m8[2 * j][0], 0x07050301u),
+                              (int)__builtin_amdgcn_perm(m8[2 * j + 1][1], m8[2 * j + 1][0], 0x06040200u),
+                              (int)__builtin_amdgcn_perm(m8[2 * j + 1][1], m8[2 * j + 1][0], 0x07050301u)};
 #pragma unroll
-            for (int i = 0; i < 3; ++i) bacc[i] = mfma_16x16x32_bf16(as_bf16x8(v), qp[i][t], bacc[i]);
+            for (int i = 0; i < 4; ++i) acc[i] = mfma_16x16x64_i8(mw, qd[i][j], acc[i]);
         }
-        beta = bacc[0] + bacc[1] + bacc[2];
-        // rows 4w + v are pages j0 + 4w + v: their centroid scales
+        f32x4 bt;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int pv = __shfl(my_phys, 4 * w + v, kWave);
-            const float sm = a.scales[((size_t)(pv < 0 ? 0 : pv) * Hkv + g) * SC];
-            beta[v] *= pv < 0 ? 0.f : sm;
+            bt[v] = !x.head_ok ? -1e30f : combine(acc, v) * p2 * smu[v];
+            sv[v] = max_in_row(bt[v]);
+            bt[v] -= sv[v];
+        }
+#pragma unroll
+        for (int e = 0; e < KS2; ++e) stbl[wv][x.lane >> 2][KS2 * (x.lane & 3) + e] = sl_v[e] * sl_c[e];
+        *reinterpret_cast<f32x4*>(&tbl[wv][c][4 * w]) = bt;
+        // the wave's LDS writes are done before its reads of other lanes' entries
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int n4 = 0; n4 < kBatch / 4; ++n4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&tbl[wv][c][4 * n4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) betas[4 * n4 + e] = v[e];
         }
     }
 
+    // Products of tile tt (matrix cores) are issued before the page masses of
+    // tile tt - 1 (VALU), so the two overlap.
+    auto products = [&](int tt, const Tile& cur, f32x4 (*L)[MT]) {
+        // T (16 rows x 16 heads) on the int8 matrix cores, one accumulator per digit
+        i32x4 acc[4] = {i32x4{bias_lo, bias_lo, bias_lo, bias_lo}, i32x4{0, 0, 0, 0},
+                        i32x4{bias_hi, bias_hi, bias_hi, bias_hi}, i32x4{0, 0, 0, 0}};
+#pragma unroll
+        for (int j = 0; j < NCK; ++j) {
+            const uint32_t u0 = cur.v[2 * j] ^ 0x88888888u, u1 = cur.v[2 * j + 1] ^ 0x88888888u;
+            const i32x4 bw = {(int)(u0 & 0x0F0F0F0Fu), (int)((u0 >> 4) & 0x0F0F0F0Fu),
+                              (int)(u1 & 0x0F0F0F0Fu), (int)((u1 >> 4) & 0x0F0F0F0Fu)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mfma_16x16x64_i8(bw, qd[i][j], acc[i]);
+        }
+        // row 4w + v of T: page tt PPT + v / KS2, k = KS2 w + v % KS2
+        float T[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            T[v] = combine(acc, v) * p2 * stbl[wv][tt * PPT + v / KS2][KS2 * w + v % KS2];
+        // coefficient product in fp32 from beta: page p, k-step ks takes the
+        // lane's code KS2 w + ks against T[KS2 p + ks]
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float b = betas[tt * PPT + p];
+                f32x4 l = {b, b, b, b};
+                float cv[4];
+                sbytes_f32<KS2>(cur.cf[p][mt] >> cshift, cv);
+#pragma unroll
+                for (int ks = 0; ks < KS2; ++ks) l = mfma_16x16x4_f32(cv[ks], T[KS2 * p + ks], l);
+                L[p][mt] = l;
+            }
+    };
     float run_mx = -INFINITY;
+    auto masses = [&](int tt, const f32x4 (*L)[MT]) {
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int pb = tt * PPT + p;
+            const float shift =
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv[pb & 3]), 16 * (pb >> 2)));
+            page_mass_shifted<MT, kHeads, kMasked>(a, x, L[p], pb, shift, run_mx);
+        }
+    };
+    f32x4 Lb[2][PPT][MT];
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
         if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
-        const Tile& cur = ring[tt % (PF + 1)];
-        f32x4 tacc[3];
-#pragma unroll
-        for (int i = 0; i < 3; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-            const bf16x8 vb = as_bf16x8(widen_i4x8(cur.v[t]));
-#pragma unroll
-            for (int i = 0; i < 3; ++i) tacc[i] = mfma_16x16x32_bf16(vb, qp[i][t], tacc[i]);
-        }
-        f32x4 T = tacc[0] + tacc[1] + tacc[2];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) T[v] *= cur.sc[v];
-        // lane (w, c) holds T[tile row 4w + v][head c]: its B operand rows of the
-        // coefficient product, split into three bf16 parts
-        bf16x4 tp[3];
-        {
-            __bf16 hv[4], mv[4], lv[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) split3(T[v], hv[v], mv[v], lv[v]);
-            typedef __bf16 bf16v4 __attribute__((ext_vector_type(4)));
-            tp[0] = __builtin_bit_cast(bf16x4, bf16v4{hv[0], hv[1], hv[2], hv[3]});
-            tp[1] = __builtin_bit_cast(bf16x4, bf16v4{mv[0], mv[1], mv[2], mv[3]});
-            tp[2] = __builtin_bit_cast(bf16x4, bf16v4{lv[0], lv[1], lv[2], lv[3]});
-        }
-        f32x4 L[PPT][MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const bf16x4 cw = as_bf16x4(widen_i8x4(cur.cf[mt]));
-#pragma unroll
-            for (int p = 0; p < PPT; ++p) {
-                const bf16x4 A = c_pin == p ? cw : bf16x4{0, 0, 0, 0};
-                f32x4 acc = mfma_16x16x16_bf16(A, tp[0], f32x4{0.f, 0.f, 0.f, 0.f});
-                acc = mfma_16x16x16_bf16(A, tp[1], acc);
-                L[p][mt] = mfma_16x16x16_bf16(A, tp[2], acc);
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < PPT; ++p)
-            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], tt * PPT + p, beta, run_mx);
+        // keep the next tile's loads ahead of this tile's waits
+        __builtin_amdgcn_sched_barrier(0);
+        products(tt, ring[tt % (PF + 1)], Lb[tt & 1]);
+        if (tt > 0) masses(tt - 1, Lb[(tt - 1) & 1]);
     }
-    if (a.run_max) {
-        run_mx = max_over_rows(run_mx);
+    masses(NTILE - 1, Lb[(NTILE - 1) & 1]);
+    if (a.run_max && x.lane == 0) {
         const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
-        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
+        a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
     }
 }
 
@@ -767,8 +920,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     static_assert(P % 16 == 0 && D % 32 == 0, "P a multiple of 16, d of 32");
     static_assert(RR == 4 || RR == 8 || RR == 16, "padded rank");
     static_assert(NP % kRunPages == 0 && NP <= kWave, "whole runs per wave");
-    static_assert(sizeof(TS) == 4 || (NP == kBatch && PF == kPrefetch),
-                  "the bf16 and code paths scan one run per wave");
+    static_assert(sizeof(TS) == 4 || NP == kBatch, "the bf16 and code paths scan one run per wave");
+    static_assert(sizeof(TS) != 2 || PF == kPrefetch, "the bf16 path keeps one tile in flight");
     constexpr int E = Summ<TS>::E;
     constexpr int NCH = D / (4 * E);
 
@@ -788,6 +941,26 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     x.head_ok = x.c < x.G;
     x.j0 = jb * NP;
     const int c = x.c, w = x.w;
+
+    // Query fragment, in the contraction order of the summary loads:
+    // qf[E t + e] = q[h][4E t + E w + e] for head h = c, as loaded; the batch
+    // functions scale it to log2 units (qs, 0 for padding heads) when they
+    // split it, after their first summary loads are issued.  Its loads go out
+    // first: they depend on nothing the block table gives.
+    x.qs = x.head_ok ? kLog2e / sqrtf((float)D) : 0.0f;
+    {
+        const float* qp =
+            a.q + ((size_t)x.b * a.num_q_heads + x.g * x.G + (x.head_ok ? c : 0)) * D;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t)
+#pragma unroll
+            for (int h4 = 0; h4 < E / 4; ++h4) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(qp + 4 * E * t + E * w + 4 * h4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x.qf[E * t + 4 * h4 + e] = v[e];
+            }
+    }
 
     // Lane l looks after page j0 + l % NP.  Its block-table entry is read
     // together with the sequence length (clamped index, kept only if the page
@@ -818,30 +991,12 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
     }
     x.my_phys = (jc < full && p_spec >= 0 && p_spec < a.num_blocks) ? p_spec : -1;
 
-    // Query fragment, in the contraction order of the summary loads:
-    // qf[E t + e] = q[h][4E t + E w + e] for head h = c, as loaded; the batch
-    // functions scale it to log2 units (qs, 0 for padding heads) when they
-    // split it, after their first summary loads are issued.
-    x.qs = x.head_ok ? kLog2e / sqrtf((float)D) : 0.0f;
-    {
-        const float* qp =
-            a.q + ((size_t)x.b * a.num_q_heads + x.g * x.G + (x.head_ok ? c : 0)) * D;
-#pragma unroll
-        for (int t = 0; t < NCH; ++t)
-#pragma unroll
-            for (int h4 = 0; h4 < E / 4; ++h4) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(qp + 4 * E * t + E * w + 4 * h4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    x.qf[E * t + 4 * h4 + e] = v[e];
-            }
-    }
 
     // every page of the batch present and the rank not padded: no masking
     if constexpr (kExact) {
         if (x.j0 + NP <= full && __ballot(x.lane < NP && x.my_phys < 0) == 0ull) {
             if constexpr (sizeof(TS) == 1)
-                scan_batch_q<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
+                scan_batch_q<P, D, RR, kExact, kHeads, kOff32, false, PF>(a, x);
             else if constexpr (sizeof(TS) == 2)
                 scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, false>(a, x);
             else
@@ -850,7 +1005,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
         }
     }
     if constexpr (sizeof(TS) == 1)
-        scan_batch_q<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
+        scan_batch_q<P, D, RR, kExact, kHeads, kOff32, true, PF>(a, x);
     else if constexpr (sizeof(TS) == 2)
         scan_batch_bf16<P, D, RR, kExact, kHeads, kOff32, true>(a, x);
     else
@@ -889,7 +1044,10 @@ hipError_t launch_ts(const ScanParams& p, hipStream_t s) {
 
 template <typename TS, int P, int D, int RR>
 hipError_t launch_typed(const ScanParams& p, hipStream_t s) {
-    return launch_ts<TS, P, D, RR>(p, s);
+    if constexpr (sizeof(TS) == 1)
+        return launch_ts<TS, P, D, RR, kBatch, kCodePrefetch>(p, s);
+    else
+        return launch_ts<TS, P, D, RR>(p, s);
 }
 
 template <typename TS, int P, int D>

@@ -146,3 +146,48 @@ def test_select_codes_band():
         f = s.seq_lens[b] // s.page_size
         for g in range(s.num_kv_heads):
             assert band_ok(sel_g[b, g], sel_o[b, g], page_o[b, g, :f], min(k, f)), (b, g)
+
+
+@pytest.mark.parametrize("scale", [16.0, 32.0])
+def test_scan_codes_large_logits(scale):
+    """Logits of tens to hundreds over codes (queries scaled up, page centroids
+    offset): masses within 1e-4 of the oracle's estimate on the dequantised
+    summary.  The scan sums each page's 2^logit shifted by the page's largest
+    centroid term and takes the exact form (the page's max first) where that
+    sum leaves [2^-60, 2^60]; at these scales both forms are taken, which the
+    oracle's own values confirm below."""
+    import kv_cache_page_rank_amd as lk
+    case = Case(bf16_small(num_kv_heads=8, page_offset_std=4.0))
+    s = case.spec
+    codes = oracle.quantize_pool(*case.oracle_summaries())
+    deq = oracle.dequantize_pool(*codes)
+    q_host = (case.layer.q.astype(np.float64) * scale).astype(np.float32)
+    head_o, page_o = oracle.scan_pool(case.lay, s.rank, q_host, *deq)
+    # log2 of each page's shifted sum, from the oracle: mass / ln 2 minus the
+    # largest centroid term over the group's heads
+    H, G, d, P = s.num_kv_heads, s.group, s.head_dim, s.page_size
+    mu = deq[0].reshape(s.num_blocks, H, d)
+    shifted = []
+    for b in range(s.batch):
+        for g in range(H):
+            for j in range(s.seq_lens[b] // P):
+                m = mu[case.layer.block_table[b, j], g].astype(np.float64)
+                beta = q_host[b, g * G:(g + 1) * G].astype(np.float64) @ m / np.sqrt(d)
+                shifted.append((page_o[b, g, j] - beta.max()) / np.log(2))
+    shifted = np.array(shifted)
+    assert (shifted < 56).any()
+    if scale >= 32:
+        assert (shifted > 64).sum() >= 10
+    say("scan codes large logits", scale, "shifted log2-sum range", shifted.min(), shifted.max())
+    summ = codes_to_device(*codes)
+    q = torch.from_numpy(q_host).to(DEV)
+    pm = torch.empty((s.batch, s.num_kv_heads, s.max_pages), device=DEV)
+    pm2 = torch.empty_like(pm)
+    hm = torch.empty((s.batch, s.num_q_heads, s.max_pages), device=DEV)
+    lk.locks_scan(q, summ, case.pages, pm, hm)
+    lk.locks_scan(q, summ, case.pages, pm2)
+    torch.cuda.synchronize()
+    err = (masses_close(to_np(pm), page_o), masses_close(to_np(pm2), page_o),
+           masses_close(to_np(hm), head_o))
+    say("max |log-mass error|", *err)
+    assert max(err) <= 1e-4
