@@ -148,6 +148,69 @@ __device__ __forceinline__ void page_mass(const ScanParams& a, const WaveCtx<D>&
     }
 }
 
+// Per-page tail of batches whose logits arrive shifted: the coefficient
+// product starts from beta - shift, shift = the page's largest beta over the
+// group's heads (a wave-uniform value).  Lane (w, c) holds the shifted logits
+// of tokens 16 mt + 4w + v for head c (log2 units) in L[mt][v], every lane
+// the same page; padding heads carry values near -1e30 and drop out.
+// Log-sum-exp over the group is the log-sum-exp of all 64 x 16 (token, head)
+// logits of the page.  The coefficients of a page sum to zero over its tokens
+// (they are projections of keys less their mean), so the best head's largest
+// shifted logit is about 0 or more and the sum of 2^logit is at least about 1;
+// it exceeds 2^60 only for deviations from the centroid term of some 50 log2
+// units.  Pages whose sum leaves [2^-60, 2^60] take the exact form (the
+// page's max subtracted first).  With per-head output (kHeads) every head's
+// sum is taken with its own max.
+template <int MT, bool kHeads, bool kMasked, int D>
+__device__ __forceinline__ void page_mass_shifted(const ScanParams& a, const WaveCtx<D>& x,
+                                                  const f32x4* L, int pb, float shift,
+                                                  float& run_mx) {
+    const int j = x.j0 + pb;
+    auto local_max = [&]() {
+        float m = L[0][0];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) m = fmaxf(m, L[mt][v]);
+        return m;
+    };
+    auto local_sum = [&](float off) {
+        float s = fast_exp2(L[0][0] - off);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = (mt == 0 ? 1 : 0); v < 4; ++v) s += fast_exp2(L[mt][v] - off);
+        return s;
+    };
+    float a2, s2 = 0.0f;
+    if constexpr (!kHeads) {
+        const float sum = sum_in_row(sum_over_rows(local_sum(0.0f)));
+        if (sum >= 0x1p-60f && sum <= 0x1p60f) {
+            a2 = shift + fast_log2(sum);
+        } else {
+            const float mx = max_in_row(max_over_rows(local_max()));
+            a2 = shift + mx + fast_log2(sum_in_row(sum_over_rows(local_sum(mx))));
+        }
+    } else {
+        const float mx = max_over_rows(local_max());
+        s2 = shift + mx + fast_log2(sum_over_rows(local_sum(mx)));
+        const float xv = x.head_ok ? s2 : -INFINITY;
+        const float gm = max_in_row(xv);
+        a2 = gm + fast_log2(sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f));
+    }
+    if (j < a.max_pages) {
+        const bool ok = !kMasked || __builtin_amdgcn_readlane(x.my_phys, pb) >= 0;
+        const float mass = ok ? a2 * kLn2 : -INFINITY;
+        run_mx = fmaxf(run_mx, mass);
+        if (x.lane == 0) x.out_page[j] = mass;
+        if constexpr (kHeads) {
+            if (x.w == 0 && x.head_ok)
+                a.head_logmass[((size_t)x.b * a.num_q_heads + x.g * x.G + x.c) * a.max_pages + j] =
+                    ok ? s2 * kLn2 : -INFINITY;
+        }
+    }
+}
+
 // The query words, passed through empty asm statements that clobber memory:
 // they stay after every load issued before them, and the query's arithmetic
 // stays after them, so a wave's first summary loads go out before it waits
@@ -329,7 +392,36 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
             beta[n] = dot_q(mv[n]);
         }
     }
-    // lane (w, c) now holds beta[page j0 + 16 n + 4w + v][head c] in element v of beta[n].
+    // lane (w, c) now holds beta[page j0 + 16 n + 4w + v][head c] in element v
+    // of beta[n].  The coefficient products start from beta - shift, shift =
+    // the page's largest beta over the group's heads (page_mass_shifted): the
+    // shifts stay in sv[n][v] of lane (w, c), and a per-wave table in LDS hands
+    // every lane beta - shift of all NP pages for its head.
+    float sv[NRUN][4];
+    float betas[NP];
+    {
+        __shared__ float tbl[4][16][NP];  // [wave of the block][head][page]
+        const int wv = threadIdx.x >> 6;
+#pragma unroll
+        for (int n = 0; n < NRUN; ++n) {
+            f32x4 bt = beta[n];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                bt[v] = x.head_ok ? bt[v] : -1e30f;
+                sv[n][v] = max_in_row(bt[v]);
+                bt[v] -= sv[n][v];
+            }
+            *reinterpret_cast<f32x4*>(&tbl[wv][c][16 * n + 4 * w]) = bt;
+        }
+        // the wave's LDS writes are done before its reads of other lanes' entries
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int n4 = 0; n4 < NP / 4; ++n4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&tbl[wv][c][4 * n4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) betas[4 * n4 + e] = v[e];
+        }
+    }
 
     float run_mx = -INFINITY;  // max of the written page masses of the current run
 #pragma unroll
@@ -348,7 +440,8 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
         for (int p = 0; p < PPT; ++p)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                L[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const float b = betas[tt * PPT + p];
+                L[p][mt] = f32x4{b, b, b, b};
 #pragma unroll
                 for (int ks = 0; ks < KS2; ++ks)
                     L[p][mt] = mfma_16x16x4_f32(coef_el(cur, p, mt, ks), Tcur[p * KS2 + ks], L[p][mt]);
@@ -357,7 +450,9 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int pb = tt * PPT + p;
-            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], pb, beta[pb / kRunPages], run_mx);
+            const float shift = __int_as_float(__builtin_amdgcn_readlane(
+                __float_as_int(sv[pb / kRunPages][pb & 3]), 16 * ((pb & 15) >> 2)));
+            page_mass_shifted<MT, kHeads, kMasked>(a, x, L[p], pb, shift, run_mx);
         }
         // a run ends with this tile: its maximum (row w holds pages 4w..4w+3)
         if ((tt + 1) * PPT % kRunPages == 0) {
@@ -542,69 +637,6 @@ __device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveC
         run_mx = max_over_rows(run_mx);
         const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
         if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
-    }
-}
-
-// Per-page tail of batches whose logits arrive shifted: the coefficient
-// product starts from beta - shift, shift = the page's largest beta over the
-// group's heads (a wave-uniform value).  Lane (w, c) holds the shifted logits
-// of tokens 16 mt + 4w + v for head c (log2 units) in L[mt][v], every lane
-// the same page; padding heads carry values near -1e30 and drop out.
-// Log-sum-exp over the group is the log-sum-exp of all 64 x 16 (token, head)
-// logits of the page.  The coefficients of a page sum to zero over its tokens
-// (they are projections of keys less their mean), so the best head's largest
-// shifted logit is about 0 or more and the sum of 2^logit is at least about 1;
-// it exceeds 2^60 only for deviations from the centroid term of some 50 log2
-// units.  Pages whose sum leaves [2^-60, 2^60] take the exact form (the
-// page's max subtracted first).  With per-head output (kHeads) every head's
-// sum is taken with its own max.
-template <int MT, bool kHeads, bool kMasked, int D>
-__device__ __forceinline__ void page_mass_shifted(const ScanParams& a, const WaveCtx<D>& x,
-                                                  const f32x4* L, int pb, float shift,
-                                                  float& run_mx) {
-    const int j = x.j0 + pb;
-    auto local_max = [&]() {
-        float m = L[0][0];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) m = fmaxf(m, L[mt][v]);
-        return m;
-    };
-    auto local_sum = [&](float off) {
-        float s = fast_exp2(L[0][0] - off);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int v = (mt == 0 ? 1 : 0); v < 4; ++v) s += fast_exp2(L[mt][v] - off);
-        return s;
-    };
-    float a2, s2 = 0.0f;
-    if constexpr (!kHeads) {
-        const float sum = sum_in_row(sum_over_rows(local_sum(0.0f)));
-        if (sum >= 0x1p-60f && sum <= 0x1p60f) {
-            a2 = shift + fast_log2(sum);
-        } else {
-            const float mx = max_in_row(max_over_rows(local_max()));
-            a2 = shift + mx + fast_log2(sum_in_row(sum_over_rows(local_sum(mx))));
-        }
-    } else {
-        const float mx = max_over_rows(local_max());
-        s2 = shift + mx + fast_log2(sum_over_rows(local_sum(mx)));
-        const float xv = x.head_ok ? s2 : -INFINITY;
-        const float gm = max_in_row(xv);
-        a2 = gm + fast_log2(sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f));
-    }
-    if (j < a.max_pages) {
-        const bool ok = !kMasked || __builtin_amdgcn_readlane(x.my_phys, pb) >= 0;
-        const float mass = ok ? a2 * kLn2 : -INFINITY;
-        run_mx = fmaxf(run_mx, mass);
-        if (x.lane == 0) x.out_page[j] = mass;
-        if constexpr (kHeads) {
-            if (x.w == 0 && x.head_ok)
-                a.head_logmass[((size_t)x.b * a.num_q_heads + x.g * x.G + x.c) * a.max_pages + j] =
-                    ok ? s2 * kLn2 : -INFINITY;
-        }
     }
 }
 
