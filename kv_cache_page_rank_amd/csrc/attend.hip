@@ -266,10 +266,10 @@ __device__ __forceinline__ void load_q_raw(const AttnParams& a, int b, int hq, i
     }
 }
 __device__ __forceinline__ void split3_bits(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
-    h = f32_to_bf16_bits(x);
+    h = bf16_rne(x);
     const float r = x - bf16_bits_to_f32(h);
-    m = f32_to_bf16_bits(r);
-    l = f32_to_bf16_bits(r - bf16_bits_to_f32(m));
+    m = bf16_rne(r);
+    l = bf16_rne(r - bf16_bits_to_f32(m));
 }
 template <int D>
 __device__ __forceinline__ void split_q(const f32x4* xa, const f32x4* xb, bool head_ok,
@@ -526,6 +526,10 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
     const bool head_ok = c < G;
     const int hq = g * G + (head_ok ? c : 0);
     const int tok0 = 16 * wv;
+    // the query's loads go out first (they depend on nothing); it is split
+    // once the page's loads are out, while they are in flight
+    f32x4 xa[KS], xb[KS];
+    load_q_raw<D>(a, b, hq, w, xa, xb);
 
     // The list entry of this split is read together with the sequence length
     // (it does not depend on it), and the block-table entry as soon as both
@@ -578,11 +582,7 @@ __global__ __launch_bounds__(256) void attend_sparse_kernel(const AttnParams a) 
             vraw[md] = *reinterpret_cast<const u32x2*>(vp + (size_t)(16 * md + c) * P);
     }
 
-    if (pi == 0) {
-        f32x4 xa[KS], xb[KS];
-        load_q_raw<D>(a, b, hq, w, xa, xb);
-        split_q<D>(xa, xb, head_ok, qp);
-    }
+    if (pi == 0) split_q<D>(xa, xb, head_ok, qp);
 
     if (page_ok) {
         const int nv = seq - jpg * P < P ? seq - jpg * P : P;

@@ -134,11 +134,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
            (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
 }
 
+// Round to nearest even on the conversion unit (the gfx950 bf16 convert):
+// the same bits as f32_to_bf16_bits for every finite value, in one
+// instruction per pair.
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
 // Split x into hi + lo, both bf16-representable, hi = rne(x), lo = rne(x - hi):
 // the pair carries ~16 significant bits.
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
-    hi = f32_to_bf16_bits(x);
-    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+    hi = bf16_rne(x);
+    lo = bf16_rne(x - bf16_bits_to_f32(hi));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
