@@ -99,55 +99,6 @@ __device__ __forceinline__ void load_f32(const void* base, size_t off, float* ou
     }
 }
 
-// Per-page tail shared by both summary types: lane (w, c) holds the logits of
-// tokens 16 mt + 4w + v for head c (log2 units, beta not yet added) in
-// L[mt][v].  Forms the head's LSE, adds beta, aggregates the group and
-// writes page pb of the batch.  beta is the centroid tile of pb's run of 16
-// pages: its row w = (pb % 16) / 4 holds the right beta.
-template <int D, int MT, bool kHeads, bool kMasked>
-__device__ __forceinline__ void page_mass(const ScanParams& a, const WaveCtx<D>& x,
-                                          const f32x4* L, int pb, const f32x4& beta,
-                                          float& run_mx) {
-    const int w = x.w, c = x.c, g = x.g;
-    const int j = x.j0 + pb;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, L[mt][v]);
-    mx = max_over_rows(mx);
-    float sum = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sum += fast_exp2(L[mt][v] - mx);
-    sum = sum_over_rows(sum);
-    // head h's mass is sum * 2^(mx + beta); beta of page pb sits in row
-    // pb/4, element pb%4, so only that row's values are right
-    const float top = mx + beta[pb & 3];
-    float a2, s2 = 0.0f;
-    if constexpr (kHeads) {
-        s2 = top + fast_log2(sum);
-        const float xv = x.head_ok ? s2 : -INFINITY;
-        const float gm = max_in_row(xv);
-        a2 = gm + fast_log2(sum_in_row(x.head_ok ? fast_exp2(xv - gm) : 0.0f));
-    } else {  // the group sum without each head's log: sum_h sum_h 2^(top_h - max top)
-        const float gm = max_in_row(x.head_ok ? top : -INFINITY);
-        a2 = gm + fast_log2(sum_in_row(x.head_ok ? sum * fast_exp2(top - gm) : 0.0f));
-    }
-    if (w == ((pb & 15) >> 2) && j < a.max_pages) {
-        const bool ok = !kMasked || __builtin_amdgcn_readlane(x.my_phys, pb) >= 0;
-        const float mass = ok ? a2 * kLn2 : -INFINITY;
-        run_mx = fmaxf(run_mx, mass);
-        if (c == 0) x.out_page[j] = mass;
-        if constexpr (kHeads) {
-            if (x.head_ok)
-                a.head_logmass[((size_t)x.b * a.num_q_heads + g * x.G + c) * a.max_pages + j] =
-                    ok ? s2 * kLn2 : -INFINITY;
-        }
-    }
-}
-
 // Per-page tail of batches whose logits arrive shifted: the coefficient
 // product starts from beta - shift, shift = the page's largest beta over the
 // group's heads (a wave-uniform value).  Lane (w, c) holds the shifted logits
@@ -209,6 +160,40 @@ __device__ __forceinline__ void page_mass_shifted(const ScanParams& a, const Wav
                     ok ? s2 * kLn2 : -INFINITY;
         }
     }
+}
+
+// Shifted centroid terms for page_mass_shifted, from the beta tiles of NR
+// runs (lane (w, c) element v of beta[n]: page 16n + 4w + v, head c; padding
+// heads are given -1e30): each lane receives beta - shift of all 16 NR pages
+// for its head in betas[], through a per-wave LDS table tbl[16][16 NR], and
+// lane (w, c) keeps the shifts of pages 16n + 4w + v in sv[n][v].
+template <int NR>
+__device__ __forceinline__ void shift_betas(const f32x4* beta, bool head_ok, int w, int c,
+                                            float (*tbl)[16 * NR], float* betas, float (*sv)[4]) {
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+        f32x4 bt = beta[n];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            bt[v] = head_ok ? bt[v] : -1e30f;
+            sv[n][v] = max_in_row(bt[v]);
+            bt[v] -= sv[n][v];
+        }
+        *reinterpret_cast<f32x4*>(&tbl[c][16 * n + 4 * w]) = bt;
+    }
+    // the wave's LDS writes are done before its reads of other lanes' entries
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int n4 = 0; n4 < 4 * NR; ++n4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&tbl[c][4 * n4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) betas[4 * n4 + e] = v[e];
+    }
+}
+// The shift of page pb of the batch, wave-uniform (held by lane 16 ((pb%16)/4)).
+__device__ __forceinline__ float page_shift(const float (*sv)[4], int pb) {
+    return __int_as_float(
+        __builtin_amdgcn_readlane(__float_as_int(sv[pb / 16][pb & 3]), 16 * ((pb & 15) >> 2)));
 }
 
 // The query words, passed through empty asm statements that clobber memory:
@@ -401,26 +386,7 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
     float betas[NP];
     {
         __shared__ float tbl[4][16][NP];  // [wave of the block][head][page]
-        const int wv = threadIdx.x >> 6;
-#pragma unroll
-        for (int n = 0; n < NRUN; ++n) {
-            f32x4 bt = beta[n];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                bt[v] = x.head_ok ? bt[v] : -1e30f;
-                sv[n][v] = max_in_row(bt[v]);
-                bt[v] -= sv[n][v];
-            }
-            *reinterpret_cast<f32x4*>(&tbl[wv][c][16 * n + 4 * w]) = bt;
-        }
-        // the wave's LDS writes are done before its reads of other lanes' entries
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int n4 = 0; n4 < NP / 4; ++n4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(&tbl[wv][c][4 * n4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) betas[4 * n4 + e] = v[e];
-        }
+        shift_betas<NRUN>(beta, x.head_ok, w, c, tbl[threadIdx.x >> 6], betas, sv);
     }
 
     float run_mx = -INFINITY;  // max of the written page masses of the current run
@@ -450,9 +416,7 @@ __device__ __forceinline__ void scan_batch_f32(const ScanParams& a, const WaveCt
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int pb = tt * PPT + p;
-            const float shift = __int_as_float(__builtin_amdgcn_readlane(
-                __float_as_int(sv[pb / kRunPages][pb & 3]), 16 * ((pb & 15) >> 2)));
-            page_mass_shifted<MT, kHeads, kMasked>(a, x, L[p], pb, shift, run_mx);
+            page_mass_shifted<MT, kHeads, kMasked>(a, x, L[p], pb, page_shift(sv, pb), run_mx);
         }
         // a run ends with this tile: its maximum (row w holds pages 4w..4w+3)
         if ((tt + 1) * PPT % kRunPages == 0) {
@@ -588,6 +552,13 @@ __device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveC
             for (int i = 0; i < 3; ++i) bacc[i] = mfma_16x16x32_bf16(as_bf16x8(mv[t]), qp[i][t], bacc[i]);
         beta = bacc[0] + bacc[1] + bacc[2];
     }
+    // the coefficient products start from beta - shift (page_mass_shifted)
+    float sv[1][4];
+    float betas[kBatch];
+    {
+        __shared__ float tbl[4][16][kBatch];  // [wave of the block][head][page]
+        shift_betas<1>(&beta, x.head_ok, w, c, tbl[threadIdx.x >> 6], betas, sv);
+    }
 
     float run_mx = -INFINITY;
 #pragma unroll
@@ -625,18 +596,20 @@ __device__ __forceinline__ void scan_batch_bf16(const ScanParams& a, const WaveC
                 const bool mine = c_pin == p;
                 const u32x2 av = {mine ? cur.cf[mt][0] : 0u, mine ? cur.cf[mt][1] : 0u};
                 const bf16x4 A = as_bf16x4(av);
-                f32x4 acc = mfma_16x16x16_bf16(A, tp[0], f32x4{0.f, 0.f, 0.f, 0.f});
+                const float b = betas[tt * PPT + p];
+                f32x4 acc = mfma_16x16x16_bf16(A, tp[0], f32x4{b, b, b, b});
                 acc = mfma_16x16x16_bf16(A, tp[1], acc);
                 L[p][mt] = mfma_16x16x16_bf16(A, tp[2], acc);
             }
 #pragma unroll
-        for (int p = 0; p < PPT; ++p)
-            page_mass<D, MT, kHeads, kMasked>(a, x, L[p], tt * PPT + p, beta, run_mx);
+        for (int p = 0; p < PPT; ++p) {
+            const int pb = tt * PPT + p;
+            page_mass_shifted<MT, kHeads, kMasked>(a, x, L[p], pb, page_shift(sv, pb), run_mx);
+        }
     }
-    if (a.run_max) {
-        run_mx = max_over_rows(run_mx);
+    if (a.run_max && x.lane == 0) {
         const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
-        if (x.lane == 0) a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
+        a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;
     }
 }
 
@@ -842,9 +815,9 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
     // beta - shift of the batch's 16 pages for the lane's head, in every lane:
     // the product gives lane (w, c) pages 4w..4w+3; a per-wave table in LDS
     // hands each lane the other twelve.  shift of page 4w + v = the largest
-    // beta over the group's heads, in sv[v] of lane (w, c).
+    // beta over the group's heads, in sv[0][v] of lane (w, c).
     float betas[kBatch];
-    float sv[4];
+    float sv[1][4];
     __shared__ float stbl[4][kBatch][RR];     // [wave of the block][page][row]: s_v s_c
     const int wv = threadIdx.x >> 6;
     {
@@ -868,22 +841,11 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
         }
         f32x4 bt;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            bt[v] = !x.head_ok ? -1e30f : combine(acc, v) * p2 * smu[v];
-            sv[v] = max_in_row(bt[v]);
-            bt[v] -= sv[v];
-        }
+        for (int v = 0; v < 4; ++v) bt[v] = combine(acc, v) * p2 * smu[v];
 #pragma unroll
         for (int e = 0; e < KS2; ++e) stbl[wv][x.lane >> 2][KS2 * (x.lane & 3) + e] = sl_v[e] * sl_c[e];
-        *reinterpret_cast<f32x4*>(&tbl[wv][c][4 * w]) = bt;
-        // the wave's LDS writes are done before its reads of other lanes' entries
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int n4 = 0; n4 < kBatch / 4; ++n4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(&tbl[wv][c][4 * n4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) betas[4 * n4 + e] = v[e];
-        }
+        // (the helper's wait for its LDS writes covers these too)
+        shift_betas<1>(&bt, x.head_ok, w, c, tbl[wv], betas, sv);
     }
 
     // Products of tile tt (matrix cores) are issued before the page masses of
@@ -925,9 +887,7 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int pb = tt * PPT + p;
-            const float shift =
-                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv[pb & 3]), 16 * (pb >> 2)));
-            page_mass_shifted<MT, kHeads, kMasked>(a, x, L[p], pb, shift, run_mx);
+            page_mass_shifted<MT, kHeads, kMasked>(a, x, L[p], pb, page_shift(sv, pb), run_mx);
         }
     };
     f32x4 Lb[2][PPT][MT];
