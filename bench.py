@@ -66,7 +66,10 @@ def cpu_threads():
 
 
 # Kernel sources whose HBM traffic the committed counter summary describes.
-SCAN_SOURCES = ["kv_cache_page_rank_amd/csrc/scan_kernel.hpp", "kv_cache_page_rank_amd/csrc/scan_f32.hip",
+SCAN_SOURCES = ["kv_cache_page_rank_amd/csrc/scan_kernel.hpp",
+                "kv_cache_page_rank_amd/csrc/scan_common.hpp",
+                "kv_cache_page_rank_amd/csrc/scan_batch_f32.hpp",
+                "kv_cache_page_rank_amd/csrc/scan_f32.hip",
                 "kv_cache_page_rank_amd/csrc/device_common.hpp",
                 "kv_cache_page_rank_amd/csrc/launchers.hpp"]
 SCAN_COUNTERS = "profiles/scan_kernel_glm4-9b-layer-1m_hbm_counters.txt"
