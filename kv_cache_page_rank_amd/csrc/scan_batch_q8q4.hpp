@@ -33,6 +33,21 @@ __device__ __forceinline__ void sbytes_f32(uint32_t v, float* out) {
 // coefficient product runs in fp32 (16x16x4 steps) on codes converted one
 // instruction each, from a starting value of beta, so the logits leave it
 // with the centroid term in.
+// Per-workgroup LDS tables of the code path (one set for the masked and the
+// unmasked batch of a kernel): per wave, s_v s_c of each page and row, beta -
+// shift of each head and page, and the query digits of each lane.
+template <int RR, int NCK>
+struct CodeLds {
+    float scale[4][kBatch][RR];
+    float beta[4][16][kBatch];
+    i32x4 qd[4][4][NCK][64];
+};
+template <int RR, int NCK>
+__device__ __forceinline__ CodeLds<RR, NCK>& code_lds() {
+    __shared__ CodeLds<RR, NCK> lds;
+    return lds;
+}
+
 template <int P, int D, int RR, bool kExact, bool kHeads, bool kOff32, bool kMasked, int PF>
 __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<D>& x) {
     constexpr int PPT = 16 / RR;          // pages per basis tile
@@ -206,16 +221,24 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
         return fmaf((float)r32, 65536.0f, (float)r10);
     };
 
-    // beta - shift of the batch's 16 pages for the lane's head, in every lane:
-    // the product gives lane (w, c) pages 4w..4w+3; a per-wave table in LDS
-    // hands each lane the other twelve.  shift of page 4w + v = the largest
-    // beta over the group's heads, in sv[0][v] of lane (w, c).
-    float betas[kBatch];
+    // beta - shift of the batch's 16 pages for each head: the product gives
+    // lane (w, c) pages 4w..4w+3; they go to the per-wave LDS table, where
+    // every lane reads its head's entry of each page as the page comes up.
+    // shift of page 4w + v = the largest beta over the group's heads, in
+    // sv[0][v] of lane (w, c).  The query digits move to LDS as well (the
+    // tiles read them back), which keeps the kernel within three waves'
+    // registers per SIMD.
     float sv[1][4];
-    __shared__ float stbl[4][kBatch][RR];     // [wave of the block][page][row]: s_v s_c
+    CodeLds<RR, NCK>& lds = code_lds<RR, NCK>();
+    auto& stbl = lds.scale;  // [wave of the block][page][row]: s_v s_c
+    auto& tbl = lds.beta;    // [wave of the block][head][page]: beta - shift
+    auto& qtbl = lds.qd;     // [wave][digit][chunk][lane]: the query digits
     const int wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NCK; ++j) qtbl[wv][i][j][x.lane] = qd[i][j];
     {
-        __shared__ float tbl[4][16][kBatch];  // [wave of the block][head][page]
         i32x4 acc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = i32x4{0, 0, 0, 0};
@@ -239,11 +262,9 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
 #pragma unroll
         for (int e = 0; e < KS2; ++e) stbl[wv][x.lane >> 2][KS2 * (x.lane & 3) + e] = sl_v[e] * sl_c[e];
         // (the helper's wait for its LDS writes covers these too)
-        shift_betas<1>(&bt, x.head_ok, w, c, tbl[wv], betas, sv);
+        shift_betas<1>(&bt, x.head_ok, w, c, tbl[wv], nullptr, sv);
     }
 
-    // Products of tile tt (matrix cores) are issued before the page masses of
-    // tile tt - 1 (VALU), so the two overlap.
     auto products = [&](int tt, const Tile& cur, f32x4 (*L)[MT]) {
         // T (16 rows x 16 heads) on the int8 matrix cores, one accumulator per digit
         i32x4 acc[4] = {i32x4{bias_lo, bias_lo, bias_lo, bias_lo}, i32x4{0, 0, 0, 0},
@@ -254,7 +275,7 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
             const i32x4 bw = {(int)(u0 & 0x0F0F0F0Fu), (int)((u0 >> 4) & 0x0F0F0F0Fu),
                               (int)(u1 & 0x0F0F0F0Fu), (int)((u1 >> 4) & 0x0F0F0F0Fu)};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mfma_16x16x64_i8(bw, qd[i][j], acc[i]);
+            for (int i = 0; i < 4; ++i) acc[i] = mfma_16x16x64_i8(bw, qtbl[wv][i][j][x.lane], acc[i]);
         }
         // row 4w + v of T: page tt PPT + v / KS2, k = KS2 w + v % KS2
         float T[4];
@@ -267,7 +288,7 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
         for (int p = 0; p < PPT; ++p)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const float b = betas[tt * PPT + p];
+                const float b = tbl[wv][c][tt * PPT + p];
                 f32x4 l = {b, b, b, b};
                 float cv[4];
                 sbytes_f32<KS2>(cur.cf[p][mt] >> cshift, cv);
@@ -284,16 +305,15 @@ __device__ __forceinline__ void scan_batch_q(const ScanParams& a, const WaveCtx<
             page_mass_shifted<MT, kHeads, kMasked>(a, x, L[p], pb, page_shift(sv, pb), run_mx);
         }
     };
-    f32x4 Lb[2][PPT][MT];
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
         if (tt + PF < NTILE) load_tile(tt + PF, ring[(tt + PF) % (PF + 1)]);
         // keep the next tile's loads ahead of this tile's waits
         __builtin_amdgcn_sched_barrier(0);
-        products(tt, ring[tt % (PF + 1)], Lb[tt & 1]);
-        if (tt > 0) masses(tt - 1, Lb[(tt - 1) & 1]);
+        f32x4 Lc[PPT][MT];
+        products(tt, ring[tt % (PF + 1)], Lc);
+        masses(tt, Lc);
     }
-    masses(NTILE - 1, Lb[(NTILE - 1) & 1]);
     if (a.run_max && x.lane == 0) {
         const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
         a.run_max[((size_t)x.b * Hkv + g) * nruns + x.j0 / kBatch] = run_mx;

@@ -43,8 +43,7 @@ namespace {
 // with PF basis tiles in flight ahead of the one computed; the launcher picks
 // them per workload.  The bf16 and integer-code paths use one run, one tile.
 constexpr int kBatch = kRunPages;  // pages per wave of the bf16 / code paths
-constexpr int kPrefetch = 1;       // the bf16 path's tiles in flight ahead
-constexpr int kCodePrefetch = 2;   // the code path's (its tiles are small: more in flight)
+constexpr int kPrefetch = 1;       // their tiles in flight ahead
 constexpr int kChains = 2;         // independent accumulator chains of an fp32 d contraction
 
 // State of one wave's batch, shared by the two specialisations below.
@@ -165,8 +164,9 @@ __device__ __forceinline__ void page_mass_shifted(const ScanParams& a, const Wav
 // Shifted centroid terms for page_mass_shifted, from the beta tiles of NR
 // runs (lane (w, c) element v of beta[n]: page 16n + 4w + v, head c; padding
 // heads are given -1e30): each lane receives beta - shift of all 16 NR pages
-// for its head in betas[], through a per-wave LDS table tbl[16][16 NR], and
-// lane (w, c) keeps the shifts of pages 16n + 4w + v in sv[n][v].
+// for its head in betas[] (null: it reads them from the table later), through
+// a per-wave LDS table tbl[16][16 NR], and lane (w, c) keeps the shifts of
+// pages 16n + 4w + v in sv[n][v].
 template <int NR>
 __device__ __forceinline__ void shift_betas(const f32x4* beta, bool head_ok, int w, int c,
                                             float (*tbl)[16 * NR], float* betas, float (*sv)[4]) {
@@ -183,6 +183,7 @@ __device__ __forceinline__ void shift_betas(const f32x4* beta, bool head_ok, int
     }
     // the wave's LDS writes are done before its reads of other lanes' entries
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (betas == nullptr) return;  // the caller reads the table itself
 #pragma unroll
     for (int n4 = 0; n4 < 4 * NR; ++n4) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(&tbl[c][4 * n4]);

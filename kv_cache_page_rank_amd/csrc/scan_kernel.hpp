@@ -13,9 +13,13 @@ namespace locks {
 
 namespace {
 
+// Code summaries keep their per-wave tables in LDS and fit three waves per
+// SIMD (asked for here, so that batches of many waves overlap one wave's
+// set-up with another's tiles); the others take the registers they need.
 template <typename TS, int P, int D, int RR, bool kExact, bool kHeads, bool kOff32,
           int NP = kBatch, int PF = kPrefetch>
-__global__ __launch_bounds__(256) void scan_kernel(const ScanParams a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(TS) == 1 ? 3 : 1)))
+void scan_kernel(const ScanParams a) {
     static_assert(P % 16 == 0 && D % 32 == 0, "P a multiple of 16, d of 32");
     static_assert(RR == 4 || RR == 8 || RR == 16, "padded rank");
     static_assert(NP % kRunPages == 0 && NP <= kWave, "whole runs per wave");
@@ -143,10 +147,7 @@ hipError_t launch_ts(const ScanParams& p, hipStream_t s) {
 
 template <typename TS, int P, int D, int RR>
 hipError_t launch_typed(const ScanParams& p, hipStream_t s) {
-    if constexpr (sizeof(TS) == 1)
-        return launch_ts<TS, P, D, RR, kBatch, kCodePrefetch>(p, s);
-    else
-        return launch_ts<TS, P, D, RR>(p, s);
+    return launch_ts<TS, P, D, RR>(p, s);
 }
 
 template <typename TS, int P, int D>
