@@ -45,11 +45,26 @@ void scan_kernel(const ScanParams a) {
     x.j0 = jb * NP;
     const int c = x.c, w = x.w;
 
+    // Lane l looks after page j0 + l % NP.  Its block-table entry is read
+    // together with the sequence length (clamped index, kept only if the page
+    // is full), so the two loads overlap instead of following each other.
+    const int pl = x.lane % NP;
+    const int jc = x.j0 + pl;
+    const int p_spec =
+        a.block_table[(size_t)x.b * a.max_pages + (jc < a.max_pages ? jc : a.max_pages - 1)];
+    // the pages that compete: full pages whose summaries exist (the count is
+    // read beside the length; pages past it are not scanned and get -inf)
+    const int summ_raw = a.summarized ? a.summarized[x.b] : 0;
+    const int full =
+        candidate_pages(a.seq_lens[x.b], summ_raw, a.summarized != nullptr, P, a.max_pages);
     // Query fragment, in the contraction order of the summary loads:
     // qf[E t + e] = q[h][4E t + E w + e] for head h = c, as loaded; the batch
     // functions scale it to log2 units (qs, 0 for padding heads) when they
-    // split it, after their first summary loads are issued.  Its loads go out
-    // first: they depend on nothing the block table gives.
+    // split it, after their first summary loads are issued.  Its loads come
+    // after the block-table and length reads (the compiler places them past
+    // the early exit, beside the first tile's loads): vector loads complete in
+    // issue order, so a wave that waits for its block-table entry would
+    // otherwise wait for the query as well (measured: 0.2-0.9 us faster).
     x.qs = x.head_ok ? kLog2e / sqrtf((float)D) : 0.0f;
     {
         const float* qp =
@@ -65,18 +80,6 @@ void scan_kernel(const ScanParams a) {
             }
     }
 
-    // Lane l looks after page j0 + l % NP.  Its block-table entry is read
-    // together with the sequence length (clamped index, kept only if the page
-    // is full), so the two loads overlap instead of following each other.
-    const int pl = x.lane % NP;
-    const int jc = x.j0 + pl;
-    const int p_spec =
-        a.block_table[(size_t)x.b * a.max_pages + (jc < a.max_pages ? jc : a.max_pages - 1)];
-    // the pages that compete: full pages whose summaries exist (the count is
-    // read beside the length; pages past it are not scanned and get -inf)
-    const int summ_raw = a.summarized ? a.summarized[x.b] : 0;
-    const int full =
-        candidate_pages(a.seq_lens[x.b], summ_raw, a.summarized != nullptr, P, a.max_pages);
     x.out_page = a.page_logmass + ((size_t)x.b * x.Hkv + x.g) * a.max_pages;
     if (x.j0 >= full) {  // whole batch past the full pages
         const int nruns = (a.max_pages + kRunPages - 1) / kRunPages;
