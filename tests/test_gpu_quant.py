@@ -22,6 +22,10 @@ CASES = [
     ("bf16-G16-r2", lambda: bf16_small(rank=2)),
     ("bf16-G4-r16-offset", lambda: bf16_small(num_kv_heads=8, rank=16, page_offset_std=1.0)),
     ("bf16-G1-r5", lambda: bf16_small(num_q_heads=2, rank=5)),
+    # several runs per (b, g), workgroups spanning two (b, g), ragged last
+    # pages (d 128 and d 64)
+    ("bf16-G16-r8-long", lambda: bf16_small(seq_lens=[64 * 130 + 5, 64 * 64])),
+    ("tiny-long-ragged", lambda: tiny(seq_lens=[16 * 150 + 3])),
 ]
 
 
