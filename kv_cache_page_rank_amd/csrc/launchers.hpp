@@ -31,6 +31,7 @@ struct ScanParams {
     float* page_logmass;   // [B][Hkv][max_pages]
     float* head_logmass;   // [B][Hq][max_pages] or null
     float* run_max;        // [B][Hkv][ceil(max_pages / kRunPages)] or null
+    int32_t one_round;     // set by launch_scan: every wave of the launch is resident at once
 };
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 bool scan_supported(int page_size, int head_dim, int rank);

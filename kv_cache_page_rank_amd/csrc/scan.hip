@@ -16,10 +16,32 @@ bool scan_supported(int page_size, int head_dim, int rank) {
            rank >= 1 && rank <= 16 && rank <= page_size && rank <= head_dim;
 }
 
+// Compute units of the current device (0 if the query fails), cached per
+// device: a property query, no stream work, so it is safe under capture.
+static int device_compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n = -1;
+        cached[dev] = n;
+    }
+    return cached[dev] > 0 ? cached[dev] : 0;
+}
+
 hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
-    if (p.summ_dtype == kSummQ8Q4) return launch_scan_q8q4(p, s);
-    if (p.summ_dtype == kSummBF16) return launch_scan_bf16(p, s);
-    return launch_scan_f32(p, s);
+    ScanParams q = p;
+    q.one_round = 0;
+    if (p.summ_dtype == kSummQ8Q4) {
+        // the code kernel keeps three waves per SIMD, four SIMDs per CU
+        const long waves = (long)p.batch * p.num_kv_heads * ((p.max_pages + kRunPages - 1) / kRunPages);
+        q.one_round = waves <= 12L * device_compute_units() ? 1 : 0;
+        return launch_scan_q8q4(q, s);
+    }
+    if (p.summ_dtype == kSummBF16) return launch_scan_bf16(q, s);
+    return launch_scan_f32(q, s);
 }
 
 }  // namespace locks
