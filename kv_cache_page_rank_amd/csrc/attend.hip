@@ -743,16 +743,77 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const AttnParams a) {
     }
 }
 
+// DPP row rotation by 8 lanes (within each 16-lane row): lane l reads l ^ 8.
+constexpr int kDppRowRor8 = 0x128;
+
+// A running softmax state: max, sum and unnormalised output (4 dims).
+struct MergeState {
+    float m, l;
+    f32x4 o;
+};
+// The merge of two states, the same bits whichever argument comes first
+// (products formed separately, then added; no fused multiply-add), so the
+// two lanes of an exchanged pair end up holding one state.  An empty state
+// (m = -inf, l = 0) contributes nothing.
+__device__ __forceinline__ MergeState merge_states(const MergeState& x, const MergeState& y) {
+#pragma clang fp contract(off)
+    const float M = fmaxf(x.m, y.m);
+    const float wx = x.m == -INFINITY ? 0.f : fast_exp2(x.m - M);
+    const float wy = y.m == -INFINITY ? 0.f : fast_exp2(y.m - M);
+    MergeState r;
+    r.m = M;
+    r.l = x.l * wx + y.l * wy;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.o[e] = x.o[e] * wx + y.o[e] * wy;
+    return r;
+}
+// Lane l and lane l ^ 8 (DPP row rotation by 8 within each 16-lane row).
+__device__ __forceinline__ MergeState merge_xor8(const MergeState& x) {
+    MergeState y;
+    y.m = dpp<kDppRowRor8>(x.m);
+    y.l = dpp<kDppRowRor8>(x.l);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y.o[e] = dpp<kDppRowRor8>(x.o[e]);
+    return merge_states(x, y);
+}
+// Lane l with lane l ^ 16 (kRow16) or l ^ 32: the gfx950 row swaps of a
+// register with itself give each lane the pair (own, partner) in some order,
+// which the symmetric merge does not need to know.
+template <bool kRow16>
+__device__ __forceinline__ MergeState merge_swap(const MergeState& x) {
+    auto sw = [](float v) {
+        const auto p = kRow16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v),
+                                                                 __float_as_uint(v), false, false)
+                              : __builtin_amdgcn_permlane32_swap(__float_as_uint(v),
+                                                                 __float_as_uint(v), false, false);
+        return f32x2{__uint_as_float(p[0]), __uint_as_float(p[1])};
+    };
+    MergeState u, v;
+    const f32x2 mm = sw(x.m), ll = sw(x.l);
+    u.m = mm[0];
+    v.m = mm[1];
+    u.l = ll[0];
+    v.l = ll[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const f32x2 oo = sw(x.o[e]);
+        u.o[e] = oo[0];
+        v.o[e] = oo[1];
+    }
+    return merge_states(u, v);
+}
+
 // Merge of the partials of one (b, h).  Grid: (b, h) x 32-dim chunk;
 // thread t handles dims [32*chunk + 4*(t%8), +4) over the partials
 // p = t/8, t/8 + 32, ... with a running (max, sum, output) rescaled as each
-// partial arrives (one round of loads, no max pre-pass); the 32 running
-// states are then combined in order.  Deterministic: the combination order
-// depends only on the shapes.
+// partial arrives (one round of loads, no max pre-pass).  The 32 running
+// states of each 4 dims are then merged as a tree: the 8 of a wave by lane
+// exchanges (lanes l ^ 8, l ^ 16, l ^ 32), the 4 waves' results in order
+// through LDS.  Deterministic: the merge order depends only on the shapes.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnParams a) {
-    __shared__ f32x4 pacc[32][8];
-    __shared__ float pm[32], pl[32];
+    __shared__ f32x4 so[4][8];
+    __shared__ float sm[4][8], sl[4][8];
     const int bh = blockIdx.x;
     const int chunk = blockIdx.y;
     const int t = threadIdx.x;
@@ -780,26 +841,24 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnParams a) {
         l_run = ok ? l_n : l_run;
         m_run = ok ? mn : m_run;
     }
-    pacc[part][d4] = acc;
-    if (d4 == 0) {
-        pm[part] = m_run;  // -inf with l = 0 when the thread held nothing
-        pl[part] = l_run;
+    // -inf with l = 0 when the thread held nothing
+    MergeState st{m_run, l_run, acc};
+    st = merge_xor8(st);
+    st = merge_swap<true>(st);
+    st = merge_swap<false>(st);
+    const int wv = t >> 6;
+    if ((t & 63) < 8) {
+        so[wv][d4] = st.o;
+        sm[wv][d4] = st.m;
+        sl[wv][d4] = st.l;
     }
     __syncthreads();
     if (t < 8) {
-        float M = -INFINITY;
+        MergeState f{sm[0][t], sl[0][t], so[0][t]};
 #pragma unroll
-        for (int pp = 0; pp < 32; ++pp) M = fmaxf(M, pm[pp]);
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        float L = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int pp = 0; pp < 32; ++pp) {
-                const float wt = fast_exp2(pm[pp] - M);  // 0 for empty states (-inf)
-                o += pacc[pp][t] * wt;
-                L += pl[pp] * wt;
-            }
-        }
+        for (int w = 1; w < 4; ++w) f = merge_states(f, MergeState{sm[w][t], sl[w][t], so[w][t]});
+        const float M = f.m, L = f.l;
+        const f32x4 o = f.o;
         const size_t base = (size_t)bh * D + 32 * chunk + 4 * t;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
