@@ -26,6 +26,9 @@ CASES = [
     # pages (d 128 and d 64)
     ("bf16-G16-r8-long", lambda: bf16_small(seq_lens=[64 * 130 + 5, 64 * 64])),
     ("tiny-long-ragged", lambda: tiny(seq_lens=[16 * 150 + 3])),
+    # the other two (page size, head dim) instantiations
+    ("bf16-G16-r8-d64", lambda: bf16_small(head_dim=64)),
+    ("tiny-P16-d128-r8", lambda: tiny(head_dim=128, rank=8, seq_lens=[16 * 70 + 9])),
 ]
 
 

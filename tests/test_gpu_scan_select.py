@@ -35,6 +35,9 @@ SCAN_CASES = [
     ("bf16-G16-r2", lambda: bf16_small(rank=2)),
     ("bf16-G4-r16-offset", lambda: bf16_small(num_kv_heads=8, rank=16, page_offset_std=1.0)),
     ("bf16-G1-r5", lambda: bf16_small(num_q_heads=2, rank=5)),
+    # the other two (page size, head dim) instantiations
+    ("bf16-G16-r8-d64", lambda: bf16_small(head_dim=64)),
+    ("tiny-P16-d128-r8", lambda: tiny(head_dim=128, rank=8, seq_lens=[16 * 70 + 9])),
 ]
 
 
