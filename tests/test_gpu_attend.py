@@ -64,6 +64,10 @@ def _random_sel(case, k, seed):
 CASES = [
     ("tiny-f32", lambda: tiny(), False),
     ("tiny-f32-G4-ragged", lambda: tiny(num_q_heads=4, num_kv_heads=1, seq_lens=[1000]), False),
+    # fp32 caches at the other (page size, head dim) instantiations
+    ("tiny-f32-d128", lambda: tiny(head_dim=128, rank=8, seq_lens=[16 * 70 + 9]), False),
+    ("f32-P64-G16", lambda: bf16_small(kv_bf16=False), False),
+    ("f32-P64-G4-d64", lambda: bf16_small(kv_bf16=False, head_dim=64, num_kv_heads=8), False),
     ("bf16-G16", lambda: bf16_small(), True),
     ("bf16-G4", lambda: bf16_small(num_kv_heads=8), True),
     ("bf16-G1", lambda: bf16_small(num_q_heads=2), True),

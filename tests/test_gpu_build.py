@@ -94,10 +94,11 @@ def _check_units(case, summ, units, r, gap_min=1e-3):
     ("bf16-r8", lambda: bf16_small()),
     ("bf16-r2-offset", lambda: bf16_small(rank=2, page_offset_std=1.0)),
     ("bf16-r16-d64", lambda: bf16_small(rank=16, head_dim=64)),
+    ("tiny-P16-d128-r4", lambda: tiny(head_dim=128, seq_lens=[16 * 70 + 9])),
     ("bf16-r8-low-noise", lambda: bf16_small(noise_std=1e-3)),
     ("bf16-r8-rank8-pages", lambda: bf16_small(noise_std=1e-3, subspace_rank=8)),
 ], ids=["tiny-r4", "tiny-r16-full-rank", "tiny-r4-offset-G2", "bf16-r8", "bf16-r2-offset",
-        "bf16-r16-d64", "bf16-r8-low-noise", "bf16-r8-rank8-pages"])
+        "bf16-r16-d64", "tiny-P16-d128-r4", "bf16-r8-low-noise", "bf16-r8-rank8-pages"])
 def test_build_matches_oracle(name, mk):
     case = Case(mk())
     s = case.spec
