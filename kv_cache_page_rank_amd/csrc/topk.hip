@@ -18,9 +18,11 @@
 //     a few dozen candidates.  T is found by ranking the 64 group maxima,
 //     16 threads per value and a DPP row sum.
 //     With the scan's run maxima (maxima of runs of 16 consecutive pages,
-//     each a real key) the threads hold run maxima instead of masses, and
-//     only the runs whose maximum reaches T are then read, one page per
-//     thread (more than 64 such runs: the masses are read instead).
+//     each a real key) the threads hold run maxima instead of masses, dealt
+//     so that each group is one row of 16 threads (its maximum a DPP row
+//     reduction, no LDS round), and only the runs whose maximum reaches T
+//     are then read, one page per thread (more than 256 such runs: the
+//     masses are read instead).
 //  2. Keys >= T are appended to an LDS list (wave ballot + one LDS atomic per
 //     wave; order irrelevant).  Each candidate's rank is counted against the
 //     whole list by 16 threads and a row sum; rank < k wins.
@@ -73,14 +75,22 @@ __device__ __forceinline__ void wave_append(bool hit, T item, T* list, uint32_t*
     }
 }
 
-// The k-th largest of 64 group maxima of the threads' maxima (group i =
-// threads i, i+64, ..., i+960).  Contains two barriers; every thread gets T.
+// The k-th largest of 64 group maxima of the threads' maxima.  kRows: group
+// i is the 16 threads of row i (t / 16 = i), whose maxima meet in DPP, and
+// the caller deals its items so that a row holds what a strided group would;
+// otherwise group i = threads i, i+64, ..., i+960, gathered through LDS.
+// Contains one (kRows) or two more barriers; every thread gets T.
+template <bool kRows>
 __device__ __forceinline__ uint32_t group_bound(uint32_t my_max, int k, uint32_t* s_tmax,
                                                 uint32_t* s_gmax, uint32_t* s_T) {
     const int t = threadIdx.x, i_row = t >> 4, q = t & 15;
-    s_tmax[t] = my_max;
-    __syncthreads();
-    const uint32_t gm = umax_in_row(s_tmax[i_row + 64 * q]);
+    uint32_t x = my_max;
+    if constexpr (!kRows) {
+        s_tmax[t] = my_max;
+        __syncthreads();
+        x = s_tmax[i_row + 64 * q];
+    }
+    const uint32_t gm = umax_in_row(x);
     if (q == 0) s_gmax[i_row] = gm;
     __syncthreads();
     // rank of group maximum i_row (larger first, then lower index): the ranks
@@ -104,13 +114,17 @@ __device__ __forceinline__ uint32_t group_bound(uint32_t my_max, int k, uint32_t
 // different threads, so they are keys of different pages, and at least k
 // keys are >= the result: a lower bound on the k-th largest key, tighter
 // than group_bound's once k approaches 64.  Key 0 marks an absent value.
-// Contains two barriers; every thread gets T.  s_gmax holds 128 entries.
+// Groups as in group_bound.  Every thread gets T.  s_gmax holds 128 entries.
+template <bool kRows>
 __device__ __forceinline__ uint32_t group_bound2(uint32_t my_max, int k, uint32_t* s_tmax,
                                                  uint32_t* s_gmax, uint32_t* s_T) {
     const int t = threadIdx.x, i_row = t >> 4, q = t & 15;
-    s_tmax[t] = my_max;
-    __syncthreads();
-    const uint32_t x = s_tmax[i_row + 64 * q];
+    uint32_t x = my_max;
+    if constexpr (!kRows) {
+        s_tmax[t] = my_max;
+        __syncthreads();
+        x = s_tmax[i_row + 64 * q];
+    }
     const uint32_t m1 = umax_in_row(x);
     // the second largest: the row's maximum without its first holder
     const unsigned long long eq = __ballot(x == m1);
@@ -224,9 +238,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
     const int wave = t >> 6;
     const int lane = t & 63;
 
-    // The run maxima this thread may need (runs t, t + 1024) are read
-    // together with the sequence length, clamped to the table's runs; which
-    // of them hold full pages is decided once the length is in.
+    // The run maxima this thread may need (runs 1024 i + run_of_thread, i =
+    // 0, 1) are read together with the sequence length, clamped to the
+    // table's runs; which of them hold full pages is decided once the length
+    // is in.  Runs are dealt so that row i of 16 threads holds runs i, i + 64,
+    // ..., i + 960 (and 1024 + those): the 64 strided groups of the bound,
+    // each in one DPP row, with every group populated once 64 runs exist.
+    const int run_of_thread = 64 * (t & 15) + (t >> 4);
     const int nruns_all = (a.max_pages + kRunPages - 1) / kRunPages;
     const int seq_raw = a.seq_lens[b];
     const int summ_raw = a.summarized ? a.summarized[b] : 0;
@@ -237,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
         const float* rm = a.run_max + (size_t)bg * nruns_all;
 #pragma unroll
         for (int i = 0; i < kRunPer; ++i) {
-            const int r = i * kThreads + t;
+            const int r = i * kThreads + run_of_thread;
             rmv[i] = rm[r < nruns_all ? r : nruns_all - 1];
         }
     }
@@ -273,22 +291,23 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
         }
         bool done = false;
         if (a.run_max) {
-            // ---- bound from the run maxima: thread t holds runs t, t + 1024
+            // ---- bound from the run maxima (dealt as above)
             const int nruns = (n + kRunPages - 1) / kRunPages;  // runs holding full pages
             uint32_t rkey[kRunPer];
             uint32_t my_max = 0;
 #pragma unroll
             for (int i = 0; i < kRunPer; ++i) {
-                const int r = i * kThreads + t;
+                const int r = i * kThreads + run_of_thread;
                 rkey[i] = r < nruns ? orderable_bits(rmv[i]) : 0u;
                 my_max = rkey[i] > my_max ? rkey[i] : my_max;
             }
-            const uint32_t T = k > 32 ? group_bound2(my_max, k, s_tmax, s_gmax, &s_T)
-                                      : group_bound(my_max, k, s_tmax, s_gmax, &s_T);
+            const uint32_t T = k > 32 ? group_bound2<true>(my_max, k, s_tmax, s_gmax, &s_T)
+                                      : group_bound<true>(my_max, k, s_tmax, s_gmax, &s_T);
 #pragma unroll
             for (int i = 0; i < kRunPer; ++i)
-                wave_append<uint32_t>(rkey[i] != 0u && rkey[i] >= T, (uint32_t)(i * kThreads + t),
-                                      s_list, &s_count[0], kListCap);
+                wave_append<uint32_t>(rkey[i] != 0u && rkey[i] >= T,
+                                      (uint32_t)(i * kThreads + run_of_thread), s_list,
+                                      &s_count[0], kListCap);
             __syncthreads();
             const int nlist = (int)s_count[0];
             if (nlist <= kListCap) {
@@ -351,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const TopkParams a) {
                     my_max = key[s] > my_max ? key[s] : my_max;
                 }
             }
-            const uint32_t T = group_bound(my_max, k, s_tmax, s_gmax, &s_T);
+            const uint32_t T = group_bound<false>(my_max, k, s_tmax, s_gmax, &s_T);
 #pragma unroll
             for (int s = 0; s < kMaxPer; ++s) {
                 const int j = vec ? 4 * ((s >> 2) * kThreads + t) + (s & 3) : s * kThreads + t;
