@@ -155,6 +155,10 @@ TOPK_CASES = [
     ("neg-inf", 1, 2, 2100, 64, [64 * 2100], 2048, 32, None, 0.5),
     ("all-equal", 1, 1, 4096, 64, [64 * 4096], 2048, 32, 1, 0.0),
     ("max-pages", 1, 2, 32768, 64, [64 * 32768], 4096, 64, 50, 0.0),
+    # more than 1024 runs of 16 pages with k <= 32 (both of a thread's runs in
+    # the bound), partial last runs
+    ("max-pages-k32", 1, 2, 32768, 64, [64 * 32760 - 5], 2048, 32, None, 0.0),
+    ("runs-1188-k20", 2, 1, 19000, 64, [64 * 19000 - 1, 64 * 18999 + 40], 64 * 20, 20, None, 0.1),
     ("empty-seq", 2, 1, 8, 64, [0, 63], 2048, 32, None, 0.0),
     ("wide-rows", 1, 1, 1500, 64, [64 * 1500], 2048, 40, None, 0.0),
     ("batch-varied", 4, 2, 4000, 64, [64 * 500, 64 * 3999 + 7, 64 * 40, 64 * 1100], 2048, 32,
