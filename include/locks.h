@@ -128,7 +128,10 @@ typedef struct {
  *               for int8, 7 for int4), its codes round-half-even(x / scale)
  *               clamped to [-Q, Q] (scale 0 and codes 0 for a zero vector);
  *               the value a code stands for is scale * code.  1220 bytes per
- *               unit at P 64, d 128, r 8 (fp32: 6656). */
+ *               unit at P 64, d 128, r 8 (fp32: 6656).
+ * Arrays of any size the device holds are accepted: the scan addresses
+ * them with 32-bit byte offsets while every array spans less than 4 GiB and
+ * with 64-bit offsets beyond. */
 typedef struct {
     int32_t dtype; /* locks_dtype of mu, basis and coef */
     int32_t num_blocks;
