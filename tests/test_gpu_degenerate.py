@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_cases import DEV, Case, band_ok, bf16_small, out_tol, say, tiny, to_np
-from workload.device import summaries_to_device
+from gpu_cases import DEV, Case, band_ok, bf16_small, masses_close, out_tol, say, tiny, to_np
+from workload.device import codes_to_device, summaries_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -101,3 +101,50 @@ def test_degenerate_batch_step(name, mk, bf16):
         for key, ref in (("sel", sel), ("mass", mass), ("out", out), ("lse", lse)):
             assert torch.equal(g[key], ref), (rep, key)
     graph.close()
+
+
+@pytest.mark.parametrize("sdt", ["bf16", "q8q4"])
+@pytest.mark.parametrize("name,mk,bf16", CASES, ids=[c[0] for c in CASES])
+def test_degenerate_batch_reduced_summaries(name, mk, bf16, sdt):
+    """The same batches with bf16 and integer-code summaries: scan masses
+    (per head and per group, -inf exactly where a page is not full) within
+    1e-4 of the oracle on the same rounded or dequantised values, and the
+    selection within the band of the oracle's selection from those masses."""
+    import kv_cache_page_rank_amd as lk
+    case = Case(mk())
+    s = case.spec
+    P, k = s.page_size, s.k_pages
+    mu, basis, coef = case.oracle_summaries()
+    if sdt == "q8q4":
+        codes = oracle.quantize_pool(mu, basis, coef)
+        vals = oracle.dequantize_pool(*codes)
+        summ = codes_to_device(*codes)
+    else:
+        t = [torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+             for x in (mu, basis, coef)]
+        vals = [x.float().numpy() for x in t]
+        summ = lk.Summaries(*(x.to(DEV) for x in t))
+    head_o, page_o = oracle.scan_pool(case.lay, s.rank, case.layer.q, *vals)
+    pm = torch.full((s.batch, s.num_kv_heads, s.max_pages), 7.0, device=DEV)
+    hm = torch.full((s.batch, s.num_q_heads, s.max_pages), 7.0, device=DEV)
+    say("degenerate scan", name, sdt, s.seq_lens)
+    lk.locks_scan(case.q, summ, case.pages, pm, hm)
+    args = (s.batch, s.max_pages, s.num_q_heads, s.num_kv_heads, P, s.head_dim, s.rank, k)
+    sel = torch.full((s.batch, s.num_kv_heads, k), -9, dtype=torch.int32, device=DEV)
+    mass = torch.zeros((s.batch, s.num_kv_heads, k), device=DEV)
+    ws = lk.workspace(lk.workspace_bytes(lk.OP_STEP, *args))
+    lk.locks_select(case.q, summ, case.pages, s.budget_tokens, sel, mass, ws=ws)
+    torch.cuda.synchronize()
+    assert masses_close(to_np(pm), page_o) <= 1e-4
+    assert masses_close(to_np(hm), head_o) <= 1e-4
+    sel_o, _ = oracle.select_pool(case.lay, s.budget_tokens, page_o.astype(np.float32), k)
+    sel_g = sel.cpu().numpy()
+    for b in range(s.batch):
+        f = s.seq_lens[b] // P
+        kb = min(k, f)
+        for g in range(s.num_kv_heads):
+            if kb == 0:
+                assert np.all(sel_g[b, g] == -1), (b, g)
+                continue
+            assert np.all(sel_g[b, g, kb:] == -1), (b, g)
+            assert band_ok(sel_g[b, g], sel_o[b, g], page_o[b, g, :f], kb), (b, g)
