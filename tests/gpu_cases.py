@@ -58,6 +58,24 @@ class Case:
         return [n // self.spec.page_size for n in self.spec.seq_lens]
 
 
+def shifted_log2_sums(case, q_host, mu, page_o):
+    """log2 of each full page's sum of 2^logit after the shift by the page's
+    largest centroid term over the group's heads, from the oracle's masses
+    (mass / ln 2 minus that term): where the scan's shifted form holds
+    (inside [-60, 60]) and where it takes the exact form."""
+    s = case.spec
+    H, G, d, P = s.num_kv_heads, s.group, s.head_dim, s.page_size
+    mu = np.asarray(mu).reshape(s.num_blocks, H, d)
+    out = []
+    for b in range(s.batch):
+        for g in range(H):
+            for j in range(s.seq_lens[b] // P):
+                m = mu[case.layer.block_table[b, j], g].astype(np.float64)
+                beta = q_host[b, g * G:(g + 1) * G].astype(np.float64) @ m / np.sqrt(d)
+                out.append((page_o[b, g, j] - beta.max()) / np.log(2))
+    return np.array(out)
+
+
 def masses_close(gpu, orc, atol=1e-4):
     """|a_gpu - a_orc| <= atol in the log domain (relative 1e-4 on the mass),
     with identical -inf entries."""

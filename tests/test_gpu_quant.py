@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_cases import DEV, Case, band_ok, bf16_small, masses_close, say, tiny, to_np
+from gpu_cases import (DEV, Case, band_ok, bf16_small, masses_close, say, shifted_log2_sums, tiny,
+                       to_np)
 from workload.device import codes_to_device, summaries_to_device
 
 pytestmark = pytest.mark.gpu
@@ -170,18 +171,7 @@ def test_scan_codes_large_logits(scale):
     deq = oracle.dequantize_pool(*codes)
     q_host = (case.layer.q.astype(np.float64) * scale).astype(np.float32)
     head_o, page_o = oracle.scan_pool(case.lay, s.rank, q_host, *deq)
-    # log2 of each page's shifted sum, from the oracle: mass / ln 2 minus the
-    # largest centroid term over the group's heads
-    H, G, d, P = s.num_kv_heads, s.group, s.head_dim, s.page_size
-    mu = deq[0].reshape(s.num_blocks, H, d)
-    shifted = []
-    for b in range(s.batch):
-        for g in range(H):
-            for j in range(s.seq_lens[b] // P):
-                m = mu[case.layer.block_table[b, j], g].astype(np.float64)
-                beta = q_host[b, g * G:(g + 1) * G].astype(np.float64) @ m / np.sqrt(d)
-                shifted.append((page_o[b, g, j] - beta.max()) / np.log(2))
-    shifted = np.array(shifted)
+    shifted = shifted_log2_sums(case, q_host, deq[0], page_o)
     assert (shifted < 56).any()
     if scale >= 32:
         assert (shifted > 64).sum() >= 10

@@ -7,7 +7,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_cases import DEV, Case, band_ok, bf16_small, masses_close, say, tiny, to_np
+from gpu_cases import (DEV, Case, band_ok, bf16_small, masses_close, say, shifted_log2_sums, tiny,
+                       to_np)
 from workload.device import summaries_to_device
 
 pytestmark = pytest.mark.gpu
@@ -377,26 +378,44 @@ def test_select_deterministic():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("scale", [16.0])
-def test_scan_large_logits(scale):
-    """Logits of tens (queries scaled up, page centroids offset): the fp32
-    scan still matches the oracle's masses within 1e-4 (its products carry
-    an error relative to the logits' size, so this is the demanding case)."""
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [16.0, 32.0])
+def test_scan_large_logits(scale, sdt):
+    """Logits of tens to hundreds (queries scaled up, page centroids offset):
+    the fp32 and bf16 scans still match the oracle's masses within 1e-4 (the
+    products carry an error relative to the logits' size, so this is the
+    demanding case), with and without per-head output.  The group form sums
+    each page's 2^logit shifted by its largest centroid term and takes the
+    exact form (the page's max first) where that sum leaves [2^-60, 2^60];
+    at x32 both forms are taken, which the oracle's values confirm."""
     case = Case(bf16_small(num_kv_heads=8, page_offset_std=4.0))
     s = case.spec
-    mu, basis, coef = case.oracle_summaries()
+    vals = case.oracle_summaries()
+    if sdt == "bf16":
+        t = [torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16) for x in vals]
+        vals = [x.float().numpy() for x in t]
     q_host = (case.layer.q.astype(np.float64) * scale).astype(np.float32)
-    head_o, page_o = oracle.scan_pool(case.lay, s.rank, q_host, mu, basis, coef)
-    summ = summaries_to_device(mu, basis, coef)
+    head_o, page_o = oracle.scan_pool(case.lay, s.rank, q_host, *vals)
+    shifted = shifted_log2_sums(case, q_host, vals[0], page_o)
+    assert (shifted < 56).any()
+    if scale >= 32:
+        assert (shifted > 64).sum() >= 10
     import kv_cache_page_rank_amd as lk
+    if sdt == "bf16":
+        summ = lk.Summaries(*(x.to(DEV) for x in t))
+    else:
+        summ = summaries_to_device(*vals)
     q = torch.from_numpy(q_host).to(DEV)
     pm = torch.empty((s.batch, s.num_kv_heads, s.max_pages), device=DEV)
+    pm2 = torch.empty_like(pm)
     hm = torch.empty((s.batch, s.num_q_heads, s.max_pages), device=DEV)
-    say("scan large logits", scale, s)
+    say("scan large logits", scale, sdt, "shifted log2-sum range", shifted.min(), shifted.max())
     lk.locks_scan(q, summ, case.pages, pm, hm)
+    lk.locks_scan(q, summ, case.pages, pm2)
     torch.cuda.synchronize()
     fin = np.isfinite(page_o)
     assert float(np.abs(page_o[fin]).max()) > 8.0  # the regime this case is for
-    err_page, err_head = masses_close(to_np(pm), page_o), masses_close(to_np(hm), head_o)
-    say("max |log-mass error|", err_page, err_head)
-    assert err_page <= 1e-4 and err_head <= 1e-4
+    err = (masses_close(to_np(pm), page_o), masses_close(to_np(pm2), page_o),
+           masses_close(to_np(hm), head_o))
+    say("max |log-mass error|", *err)
+    assert max(err) <= 1e-4
