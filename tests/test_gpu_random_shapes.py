@@ -1,14 +1,17 @@
 """GPU parity over seeded random shapes: page size, head dim, rank, GQA
-group, batch, ragged lengths and page offsets drawn at random; for each, the
-scan of fp32, bf16 and integer-code summaries (per head and per group, -inf
-where a page is not full) within 1e-4 of the oracle on the same values, and
-the selection within the band of the oracle's selection, through the C ABI."""
+group, batch, budget, ragged lengths and page offsets drawn at random; for
+each, the scan of fp32, bf16 and integer-code summaries (per head and per
+group, -inf where a page is not full) within 1e-4 of the oracle on the same
+values, the selection within the band of the oracle's selection, and sparse
+(over the library's selection) and dense attention at the attention bars,
+through the C ABI."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from gpu_cases import DEV, Case, band_ok, bf16_small, masses_close, say, tiny, to_np
+from test_gpu_attend import _check as check_attention, _run_dense, _run_sparse
 from workload.device import codes_to_device, summaries_to_device
 
 pytestmark = pytest.mark.gpu
@@ -26,7 +29,7 @@ def _shape(i):
     lens = [int(rng.integers(1, 64 * 60)) for _ in range(int(rng.integers(1, 4)))]
     return bf16_small(seed=seed, num_kv_heads=hkv, num_q_heads=hkv * g,
                       rank=int(rng.choice([2, 5, 8, 16])), head_dim=int(rng.choice([64, 128])),
-                      batch=len(lens), seq_lens=lens, carriers=min(4, min(n // 64 for n in lens)),
+                      budget_tokens=int(rng.choice([512, 2048, 4096])), batch=len(lens), seq_lens=lens, carriers=min(4, min(n // 64 for n in lens)),
                       page_offset_std=float(rng.choice([0.0, 1.0, 4.0])))
 
 
@@ -73,3 +76,29 @@ def test_random_shape_scan_and_select(i):
                 assert np.all(sg[b, g, kb:] == -1), (sdt, b, g)
                 if kb:
                     assert band_ok(sg[b, g], sel_o[b, g], page_o[b, g, :f], kb), (sdt, b, g)
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_random_shape_attention(i):
+    """Sparse attention over the library's own selection (fp32 summaries) and
+    dense attention, against the oracle's attention over the same pages."""
+    import kv_cache_page_rank_amd as lk
+    case = Case(_shape(i))
+    s = case.spec
+    k = s.k_pages
+    summ = summaries_to_device(*case.oracle_summaries())
+    args = (s.batch, s.max_pages, s.num_q_heads, s.num_kv_heads, s.page_size, s.head_dim, s.rank, k)
+    sel = torch.full((s.batch, s.num_kv_heads, k), -9, dtype=torch.int32, device=DEV)
+    mass = torch.zeros((s.batch, s.num_kv_heads, k), device=DEV)
+    say("random shape attention", i, s)
+    lk.locks_select(case.q, summ, case.pages, s.budget_tokens, sel, mass,
+                    ws=lk.workspace(lk.workspace_bytes(lk.OP_STEP, *args)))
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    v = case.layer.v_f32()
+    out_o, lse_o = oracle.attend_pool(case.lay, case.layer.q, case.k_f32, v, sel_np)
+    out_g, lse_g = _run_sparse(case, sel_np)
+    check_attention(out_g, lse_g, out_o, lse_o, s.kv_bf16)
+    out_o, lse_o = oracle.attend_pool(case.lay, case.layer.q, case.k_f32, v, None)
+    out_g, lse_g = _run_dense(case)
+    check_attention(out_g, lse_g, out_o, lse_o, s.kv_bf16)
