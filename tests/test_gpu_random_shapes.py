@@ -2,9 +2,9 @@
 group, batch, budget, ragged lengths and page offsets drawn at random; for
 each, the scan of fp32, bf16 and integer-code summaries (per head and per
 group, -inf where a page is not full) within 1e-4 of the oracle on the same
-values, the selection within the band of the oracle's selection, and sparse
+values, the selection within the band of the oracle's selection, sparse
 (over the library's selection) and dense attention at the attention bars,
-through the C ABI."""
+and the builder against the oracle's build, through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -12,6 +12,7 @@ import torch
 import oracle
 from gpu_cases import DEV, Case, band_ok, bf16_small, masses_close, say, tiny, to_np
 from test_gpu_attend import _check as check_attention, _run_dense, _run_sparse
+from test_gpu_build import _build_gpu, _check_units
 from workload.device import codes_to_device, summaries_to_device
 
 pytestmark = pytest.mark.gpu
@@ -102,3 +103,19 @@ def test_random_shape_attention(i):
     out_o, lse_o = oracle.attend_pool(case.lay, case.layer.q, case.k_f32, v, None)
     out_g, lse_g = _run_dense(case)
     check_attention(out_g, lse_g, out_o, lse_o, s.kv_bf16)
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_random_shape_build(i):
+    """The builder on every full page against the oracle's build: centroid,
+    orthonormal basis, coordinate residual, captured energy, and the
+    reconstructed logits on every page whose spectral gap passes the gate
+    (random ranks may leave none above it here)."""
+    case = Case(_shape(i))
+    s = case.spec
+    say("random shape build", i, s)
+    summ = _build_gpu(case)
+    units = np.array([[b, g, j] for b in range(s.batch) for g in range(s.num_kv_heads)
+                      for j in range(s.seq_lens[b] // s.page_size)], np.int32)
+    if len(units):
+        _check_units(case, summ, units, s.rank)
