@@ -4,7 +4,8 @@ each, the scan of fp32, bf16 and integer-code summaries (per head and per
 group, -inf where a page is not full) within 1e-4 of the oracle on the same
 values, the selection within the band of the oracle's selection, sparse
 (over the library's selection) and dense attention at the attention bars,
-and the builder against the oracle's build, through the C ABI."""
+the builder against the oracle's build and the quantiser bit for bit
+against the oracle's, through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -119,3 +120,23 @@ def test_random_shape_build(i):
                       for j in range(s.seq_lens[b] // s.page_size)], np.int32)
     if len(units):
         _check_units(case, summ, units, s.rank)
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_random_shape_quantise(i):
+    """The oracle's fp32 summaries quantised on the device and by the oracle:
+    identical codes and scales."""
+    import kv_cache_page_rank_amd as lk
+    case = Case(_shape(i))
+    s = case.spec
+    mu, basis, coef = case.oracle_summaries()
+    ref = oracle.quantize_pool(mu, basis, coef)
+    src = summaries_to_device(mu, basis, coef)
+    dst = lk.Summaries.empty(s.num_blocks, s.num_kv_heads, s.page_size, s.head_dim, s.rank,
+                             dtype=lk.Q8Q4)
+    say("random shape quantise", i, s)
+    lk.locks_quantize_summaries(src, dst)
+    torch.cuda.synchronize()
+    for got, want, what in zip((dst.mu, dst.basis, dst.coef, dst.scales), ref,
+                               ("mu", "basis", "coef", "scales")):
+        np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=what)
