@@ -383,8 +383,10 @@ typedef struct locks_step_graph locks_step_graph;
  * it, see locks_refresh_summaries) into an instantiated HIP graph (technical
  * summary, section 2, Implementatie: scoring, selection and sparse attention
  * run inside full graphs).  The pointers are baked in: replay reads the
- * current contents of the same buffers.  *graph receives a handle owned by
- * the caller.
+ * current contents of the same buffers.  The executable graph is uploaded to
+ * the device before the call returns (the call synchronises with its own
+ * capture stream), so its first launch costs what later ones do.  *graph
+ * receives a handle owned by the caller.
  */
 locks_status locks_step_graph_create(const locks_step_args* args, locks_step_graph** graph);
 locks_status locks_step_graph_launch(locks_step_graph* graph, void* stream);

@@ -551,15 +551,22 @@ locks_status locks_step_graph_create(const locks_step_args* a, locks_step_graph*
     }
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(s, &g);
-    (void)hipStreamDestroy(s);
-    if (st != LOCKS_OK) {
+    if (st != LOCKS_OK || e != hipSuccess) {
+        (void)hipStreamDestroy(s);
         if (g) (void)hipGraphDestroy(g);
-        return st;
+        return st != LOCKS_OK ? st : hip_fail(e);
     }
-    if (e != hipSuccess) return hip_fail(e);
     hipGraphExec_t exec;
     e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
     (void)hipGraphDestroy(g);
+    // Upload the executable graph now, so that its first launch costs what
+    // every later one does.
+    if (e == hipSuccess) {
+        e = hipGraphUpload(exec, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) (void)hipGraphExecDestroy(exec);
+    }
+    (void)hipStreamDestroy(s);
     if (e != hipSuccess) return hip_fail(e);
     locks_step_graph* h = new (std::nothrow) locks_step_graph{exec};
     if (!h) {
