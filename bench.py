@@ -553,7 +553,8 @@ def cpu_baseline(spec, layer, target_s, threads):
 
     The summary build (the oracle's one-sided Jacobi SVD of every page), on a
     prefix of the pages (all KV heads), with all cores and with one thread,
-    extrapolated per unit to every full page of the layer.  Returns the JSON
+    extrapolated per unit to every full page of the layer; dense attention
+    over a prefix of every sequence, scaled per token.  Returns the JSON
     record."""
     import numpy as np
 
@@ -631,6 +632,30 @@ def cpu_baseline(spec, layer, target_s, threads):
     log(f"cpu oracle build: {ball_u} units in {ball_s:.2f} s on {threads} threads, {b1_u} units "
         f"in {b1_s:.2f} s on one thread -> {all_units} units: {build_all_ms / 1e3:.1f} s / "
         f"{build_one_ms / 1e3:.1f} s (extrapolated per unit)")
+    # dense attention (every token of every sequence) on a prefix of each
+    # sequence sized to about a second, scaled per token to the whole layer
+    def dense_sample(nthreads, ntok):
+        seq = np.array([min(n, ntok) for n in spec.seq_lens], np.int32)
+        lay = oracle.Layout(spec.num_q_heads, Hkv, d, P, layer.block_table, seq)
+        t0 = time.perf_counter()
+        oracle.attend_pool(lay, layer.q, kf, vf, None, threads=nthreads)
+        return time.perf_counter() - t0, int(seq.sum())
+
+    all_tokens = int(sum(spec.seq_lens))
+
+    def dense_timed(nthreads, budget_s):
+        ntok = 16 * P
+        s_, done = dense_sample(nthreads, ntok)
+        while s_ < 0.25 * budget_s and done < all_tokens:
+            ntok = ntok * max(2, min(64, int(0.5 * budget_s / max(s_, 1e-4))))
+            s_, done = dense_sample(nthreads, ntok)
+        return s_ / done * all_tokens * 1e3, done
+
+    dense_all_ms, dense_all_tok = dense_timed(threads, 0.1 * target_s)
+    dense_one_ms, dense_one_tok = dense_timed(1, 0.1 * target_s)
+    log(f"cpu oracle dense attention: {dense_all_ms:.1f} ms on {threads} threads "
+        f"({dense_all_tok} tokens timed), {dense_one_ms:.1f} ms on one thread ({dense_one_tok} "
+        f"tokens timed), per step over {all_tokens} tokens")
     return {"value": round(step_s * 1e6, 1), "unit": "µs/step", "cores": threads,
             "kind": "oracle", "sample": sample, "cpu_model": cpu_model(),
             "one_thread": {"value": round(step1_s * 1e6, 1), "unit": "µs/step", "cores": 1,
@@ -640,7 +665,13 @@ def cpu_baseline(spec, layer, target_s, threads):
                       "units": all_units,
                       "sample": f"oracle build of {ball_u} units on {threads} threads and "
                                 f"{b1_u} units on one thread (the first pages of each "
-                                f"sequence, every KV head), scaled per unit"}}
+                                f"sequence, every KV head), scaled per unit"},
+            "dense_attend": {"all_cores_ms": round(dense_all_ms, 2),
+                             "one_thread_ms": round(dense_one_ms, 2),
+                             "sample": f"dense attention over the first {dense_all_tok} tokens "
+                                       f"({threads} threads) and {dense_one_tok} tokens (one "
+                                       f"thread) of the sequences, scaled per token to all "
+                                       f"{all_tokens}"}}
 
 
 if __name__ == "__main__":
