@@ -3,6 +3,8 @@
 // each GQA group; gist.science technical summary, section 2, Reconstructie
 // en Selectie and Group-Shared Selection) is in scan_kernel.hpp, compiled
 // once per type by scan_f32.hip, scan_bf16.hip and scan_q8q4.hip.
+#include <atomic>
+
 #include "launchers.hpp"
 
 namespace locks {
@@ -18,17 +20,19 @@ bool scan_supported(int page_size, int head_dim, int rank) {
 
 // Compute units of the current device (0 if the query fails), cached per
 // device: a property query, no stream work, so it is safe under capture.
+// Threads that race on the first query store the same value.
 static int device_compute_units() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];  // 0: not queried yet, -1: the query failed
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
             n = -1;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev] > 0 ? cached[dev] : 0;
+    return n > 0 ? n : 0;
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
